@@ -1,0 +1,32 @@
+"""Oracle for paged KV-cache attention: test infrastructure, not product code.
+
+A plain, slow, obviously correct CPU implementation in float64 of what the
+library computes, written from the ruDNN 0.1.7 ``paged_attention`` module page
+(``DevicePlan::attention`` / ``DevicePlan::mla`` doc comments and the
+``attention_into_split`` doc comment).  It shares no code with the HIP path:
+it does not import the ``paged_kv_cache_231_amd`` package and that package
+does not import it.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.
+
+Modules
+  reference  dense softmax attention over gathered pages, split + merge, MLA
+  plan       an independent encoder/decoder of the u32 plan words (spec v1)
+
+Pins: every function here is checked by the ``-m "not gpu"`` tests in
+``tests/test_oracle_pins.py`` and ``tests/test_oracle_plan.py`` against
+closed forms, brute force, a library routine (torch SDPA in float64) and
+hand-derived golden word lists; none is "parity unpinned".
+"""
+
+from .reference import (  # noqa: F401
+    visible_count,
+    paged_attention,
+    paged_attention_split,
+    merge_partials,
+    split_ranges,
+    paged_mla,
+    paged_mla_split,
+    attention_one,
+    mla_one,
+)
+from .plan import encode_plan, decode_plan, PlanError  # noqa: F401
