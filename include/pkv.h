@@ -1,0 +1,219 @@
+/*
+ * pkv — attention over a paged (block-table) KV cache on MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Every entry point takes plain pointers and sizes; no
+ * framework types cross it.  Device buffers are raw device addresses on the
+ * current HIP device; `stream` is a hipStream_t passed as `void *` (NULL is
+ * the null stream).
+ *
+ * The operation is the one the ruDNN 0.1.7 `paged_attention` module page
+ * states: an immutable, uploaded u32 plan (`DevicePlan::upload`, `HostPlan`),
+ * `attention` over packed queries and a paged cache (`DevicePlan::attention`
+ * doc), the MLA variant (`DevicePlan::mla` doc), and a reusable split
+ * workspace merged through FP32 statistics (`attention_into_split` doc,
+ * `SplitWorkspace`).  Kernels read lengths, positions and the block table
+ * from the plan's device words, so launches can be captured into a hipGraph
+ * and replayed after the words change (boostr 0.1.0 `decode_graph.rs` module
+ * doc, sections "Constraints", "Stable-address tensors", "Stream ordering").
+ *
+ * Errors: every call returns a pkv_status; on failure nothing is launched,
+ * no output is written and pkv_last_error() returns a static message for the
+ * calling thread (mirroring `PagedAttentionError(&'static str)`).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q/K/V/out (`check_tensor`: F32, F16 or BF16). */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,      /* invalid argument or schedule                        */
+  PKV_ESHAPE = 2,      /* shapes disagree (heads, dims, lengths vs table)     */
+  PKV_ERANGE = 3,      /* a dimension or element count exceeds u32 indexing  */
+  PKV_EDEVICE = 4,     /* plan used on another device or stream              */
+  PKV_EWORKSPACE = 5,  /* workspace shape/stream does not match the call     */
+  PKV_EHIP = 6         /* a HIP runtime call failed                          */
+} pkv_status;
+
+typedef struct pkv_plan pkv_plan;           /* opaque; device words + host copy */
+typedef struct pkv_workspace pkv_workspace; /* opaque; f32 split partials      */
+
+/* ------------------------------------------------------------------ plan
+ * Plan spec v1: little-endian u32 words (this library's own layout; the page
+ * shows a `HostPlan` of u32 words with queries, sequences, table_width,
+ * page_size and pages, not the layout).
+ *
+ *   0       PKV_PLAN_MAGIC
+ *   1       PKV_PLAN_VERSION
+ *   2..6    Q queries, S sequences, W table width, ps page size, N pages
+ *   7       R  row queries (attended one query at a time)
+ *   8       T  tiles (runs of consecutive queries of one sequence)
+ *   9..15   0
+ *   16      lens[S]      tokens in the cache of each sequence
+ *   +S      qseq[Q]      sequence of each query
+ *   +Q      qpos[Q]      absolute position of each query (< lens[qseq])
+ *   +Q      rows[R]      indices of the row queries, ascending
+ *   +R      tiles[T][2]  {first query, query count}
+ *   +2T     table[S*W]   row-major; entry j of sequence s is the physical
+ *                        page of logical token block j when
+ *                        j < ceil(lens[s]/ps), else PKV_UNUSED_PAGE
+ *
+ * Tiles: scanning queries in order, a run is a maximal range of queries of
+ * one sequence whose positions increase by one.  Runs of at least
+ * PKV_TILE_MIN queries are cut from their first query into tiles of at most
+ * PKV_TILE_MAX; queries of shorter runs are rows.
+ *
+ * Visible keys of query i: positions 0..qpos[i] when causal (absolute
+ * positions, prefill chunks included: `DevicePlan::attention` doc), all
+ * lens[qseq[i]] positions otherwise.  Token t of sequence s is slot t % ps of
+ * page table[s][t / ps].
+ */
+#define PKV_PLAN_MAGIC 0x564B5041u
+#define PKV_PLAN_VERSION 1u
+#define PKV_PLAN_HEADER_WORDS 16u
+#define PKV_UNUSED_PAGE 0xFFFFFFFFu
+#define PKV_TILE_MIN 8u
+#define PKV_TILE_MAX 128u
+
+/* Largest split count of a workspace and largest workspace allocation
+ * (`MAX_SPLITS`, `WORKSPACE_LIMIT_BYTES`: names on the page, values ours). */
+#define PKV_MAX_SPLITS 256u
+#define PKV_WORKSPACE_LIMIT_BYTES (512ull << 20)
+
+/* Validate a schedule and encode its words (host only, no HIP call).
+ *   seq_lens[sequences], query_seq[queries], query_pos[queries] (host);
+ *   block_table[sequences * table_width] (host, row-major; entries past a
+ *   sequence's last used page are ignored).
+ *   words: host output of *n_words entries, or NULL to ask for the size.
+ *   *n_words: in = capacity, out = words needed (set on success and on
+ *   PKV_EINVAL "word buffer too small").
+ * Errors: PKV_EINVAL (page_size 0, table_width 0 with sequences, query of a
+ * missing sequence, position outside its sequence, used table entry >= pages,
+ * small buffer), PKV_ESHAPE (a length above table_width * page_size),
+ * PKV_ERANGE (word count or sequences * table_width above u32). */
+pkv_status pkv_plan_encode(uint32_t sequences, const uint32_t *seq_lens,
+                           uint32_t queries, const uint32_t *query_seq,
+                           const uint32_t *query_pos, uint32_t table_width,
+                           const uint32_t *block_table, uint32_t page_size,
+                           uint32_t pages, uint32_t *words, size_t *n_words);
+
+/* Check that n_words host words are a valid spec-v1 plan (host only). */
+pkv_status pkv_plan_validate(const uint32_t *words, size_t n_words);
+
+/* Validate host words, copy them to a new device buffer on `stream` (one
+ * H2D copy, `DevicePlan::upload`) and return the plan.  The plan keeps its
+ * own host copy, is bound to the current device and to `stream`, and must be
+ * used on that stream.  Errors: as pkv_plan_validate, PKV_EHIP. */
+pkv_status pkv_plan_create(const uint32_t *words, size_t n_words, void *stream,
+                           pkv_plan **out);
+
+/* Replace the plan's words in place, stream-ordered (hipMemcpyAsync on the
+ * plan's stream; for a graph replay, call it before hipGraphLaunch on that
+ * stream).  The new words must validate and keep header words 2..8 (Q, S, W,
+ * ps, N, R, T) unchanged, so every launch grid and captured graph stays
+ * valid; lengths, positions, rows, tiles and table entries may change.
+ * `words` must stay unchanged until the copy has run (use pinned memory).
+ * Errors: PKV_EINVAL (invalid words), PKV_ESHAPE (header changed),
+ * PKV_EDEVICE (other stream/device), PKV_EHIP. */
+pkv_status pkv_plan_rebind_async(pkv_plan *plan, const uint32_t *words,
+                                 size_t n_words, void *stream);
+
+/* Set one word (index >= 16) with hipMemsetD32Async on the plan's stream:
+ * the value travels inside the call, so no host buffer must outlive it
+ * (boostr 0.1.0 `DeviceScalars::update` doc).  The plan with the new word
+ * must validate (e.g. grow a length only after the table entry of a newly
+ * used page is set).  Errors: PKV_EINVAL, PKV_EDEVICE, PKV_EHIP. */
+pkv_status pkv_plan_set_word_async(pkv_plan *plan, size_t index, uint32_t value,
+                                   void *stream);
+
+/* Copy the plan's 16 header words to `header` (host). */
+pkv_status pkv_plan_header(const pkv_plan *plan, uint32_t *header);
+
+/* Device address of the plan words (for callers that rebind from device
+ * memory with their own stream-ordered copies). */
+const uint32_t *pkv_plan_device_words(const pkv_plan *plan);
+
+/* Free the plan (synchronises the device through hipFree). */
+void pkv_plan_destroy(pkv_plan *plan);
+
+/* ------------------------------------------------------------- workspace
+ * f32 partials for split-KV: o[queries][splits][heads][dv] followed by
+ * lse[queries][splits][heads] (log2-sum-exp2 of the scaled scores).  Split j
+ * covers logical pages [j*pp, (j+1)*pp), pp = ceil(W / splits), of each
+ * query's block-table row.  Reusable across plans with the same queries,
+ * heads, dv and splits on the same stream (`attention_with_workspace` doc);
+ * its lifetime is independent of any plan.
+ * Errors: PKV_EINVAL (splits outside 1..PKV_MAX_SPLITS, a zero dimension),
+ * PKV_ERANGE (above PKV_WORKSPACE_LIMIT_BYTES), PKV_EHIP. */
+pkv_status pkv_workspace_create(uint32_t queries, uint32_t heads, uint32_t dv,
+                                uint32_t splits, void *stream,
+                                pkv_workspace **out);
+uint32_t pkv_workspace_splits(const pkv_workspace *ws);
+void pkv_workspace_destroy(pkv_workspace *ws);
+
+/* Split count that fills the GPU for a call with these heads over a plan:
+ * enough non-empty (query, KV head, part) blocks for several per compute
+ * unit, at most PKV_MAX_SPLITS and W, and small enough that the workspace
+ * for (plan queries, q_heads, value_dim) stays within
+ * PKV_WORKSPACE_LIMIT_BYTES.  A heuristic; any count gives the same result up
+ * to rounding.  Returns 1 for a null or empty plan. */
+uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads,
+                            uint32_t kv_heads, uint32_t value_dim);
+
+/* ------------------------------------------------------------- attention
+ * out[i,h,:] = softmax_t(scale * <q[i,h,:], k_t>) . v_t over the visible
+ * keys t of query i, with k_t = k[table[s][t/ps], t%ps, g, :] and
+ * g = h / (q_heads / kv_heads) (contiguous GQA groups; no KV repeat).
+ *   q   [Q, q_heads, head_dim]               device, dtype
+ *   k   [N, ps, kv_heads, head_dim]          device, dtype
+ *   v   [N, ps, kv_heads, value_dim]         device, dtype
+ *   out [Q, q_heads, value_dim]              device, dtype; must not overlap
+ *                                            q, k or v
+ * Accumulation is f32.  ws == NULL: unsplit.  Otherwise each query's
+ * visible range is split over pkv_workspace_splits(ws) parts whose f32
+ * partials are merged on the device, with no host synchronisation.
+ * Q == 0 returns PKV_OK with no launch.
+ * Errors: PKV_EINVAL (null pointer, bad dtype, scale not finite and > 0,
+ * out overlapping an input), PKV_ESHAPE (q_heads % kv_heads, head_dim or
+ * value_dim outside 1..1024), PKV_ERANGE (a tensor above u32 elements),
+ * PKV_EDEVICE, PKV_EWORKSPACE (ws built for other queries/heads/dv/stream),
+ * PKV_EHIP (launch failure). */
+pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q,
+                         const void *k, const void *v, void *out,
+                         uint32_t q_heads, uint32_t kv_heads, uint32_t head_dim,
+                         uint32_t value_dim, float scale, int causal,
+                         pkv_workspace *ws, void *stream);
+
+/* MLA (`DevicePlan::mla` doc): one shared latent head is both key and value;
+ * a position part only adds to the score:
+ *   x_t = scale * (<q_abs[i,h,:], latent_t> + <q_pos[i,h,:], k_pos_t>)
+ *   out[i,h,:] = softmax_t(x) . latent_t                 -> [Q, heads, rank]
+ *   q_abs  [Q, heads, rank]      q_pos [Q, heads, pos_dim]
+ *   latent [N, ps, 1, rank]      k_pos [N, ps, 1, pos_dim]
+ * `scale` comes from the model's QK dimensions, not from rank.
+ * Errors: as pkv_attention; PKV_ESHAPE for rank outside 1..1024 or pos_dim
+ * outside 1..256. */
+pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs,
+                   const void *q_pos, const void *latent, const void *k_pos,
+                   void *out, uint32_t heads, uint32_t rank, uint32_t pos_dim,
+                   float scale, int causal, pkv_workspace *ws, void *stream);
+
+/* Static message of the calling thread's last error ("" if none). */
+const char *pkv_last_error(void);
+
+/* Library version string. */
+const char *pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

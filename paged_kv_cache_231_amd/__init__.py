@@ -1,0 +1,260 @@
+"""Attention over a paged (block-table) KV cache on MI355X — Python binding.
+
+A thin layer over the C ABI of libpkv.so (include/pkv.h): it turns torch
+tensors into device pointers, sizes and the current HIP stream, and status
+codes into ``PKVError``.  Every step of the computation runs in the
+library's HIP kernels; there is no Python or CPU fallback.
+
+    plan = Plan(lens, qseq, qpos, table, page_size, pages)   # one upload
+    out = attention(plan, q, k, v, scale, causal=True)        # unsplit
+    ws = Workspace(plan.queries, q_heads, value_dim, splits)
+    out = attention(plan, q, k, v, scale, workspace=ws)       # split-KV
+    out = mla(plan, q_abs, q_pos, latent, k_pos, scale)
+
+Shapes (ruDNN 0.1.7 ``paged_attention`` page, ``DevicePlan::attention`` and
+``DevicePlan::mla`` docs): q [Q,Hq,D], k [N,ps,Hkv,D], v [N,ps,Hkv,Dv],
+out [Q,Hq,Dv]; MLA q_abs [Q,H,R], q_pos [Q,H,P], latent [N,ps,1,R],
+k_pos [N,ps,1,P], out [Q,H,R].
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import LIB_PATH, PKVError, STATUS, check, lib  # noqa: F401
+
+__all__ = ["Plan", "Workspace", "attention", "mla", "encode_plan", "validate_plan",
+           "suggest_splits", "PKVError", "LIB_PATH", "lib", "HEADER_WORDS", "MAX_SPLITS"]
+
+HEADER_WORDS = 16
+MAX_SPLITS = 256
+_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+def _u32_array(x) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x).reshape(-1))
+    if a.size and (a.min() < 0 or a.max() > 0xFFFFFFFF):
+        raise PKVError("ERANGE", "value outside u32")
+    return np.ascontiguousarray(a.astype(np.uint32))
+
+
+def _ptr32(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))
+
+
+def encode_plan(lens, qseq, qpos, table, page_size: int, pages: int) -> np.ndarray:
+    """Spec-v1 plan words of a schedule (host only, C++ encoder)."""
+    lens_a, qs, qp = _u32_array(lens), _u32_array(qseq), _u32_array(qpos)
+    tab = np.asarray(table)
+    if tab.ndim != 2 or tab.shape[0] != lens_a.size:
+        raise PKVError("EINVAL", "block table must be [sequences, table_width]")
+    if qs.size != qp.size:
+        raise PKVError("EINVAL", "qseq and qpos differ in length")
+    width = int(tab.shape[1])
+    for x in (width, int(page_size), int(pages)):
+        if x < 0 or x > 0xFFFFFFFF:
+            raise PKVError("ERANGE", "plan dimension exceeds u32")
+    tab_a = _u32_array(np.where(tab < 0, 0, tab)) if tab.size else np.zeros(0, np.uint32)
+    n = ctypes.c_size_t(0)
+    args = (lens_a.size, _ptr32(lens_a), qs.size, _ptr32(qs), _ptr32(qp), width, _ptr32(tab_a),
+            int(page_size), int(pages))
+    check(lib().pkv_plan_encode(*args, None, ctypes.byref(n)))
+    words = np.zeros(n.value, dtype=np.uint32)
+    check(lib().pkv_plan_encode(*args, _ptr32(words), ctypes.byref(n)))
+    return words
+
+
+def validate_plan(words) -> None:
+    w = _u32_array(words)
+    check(lib().pkv_plan_validate(_ptr32(w), w.size))
+
+
+def _stream_handle(stream, device=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return int(stream.cuda_stream)
+    return int(stream)
+
+
+class Plan:
+    """Immutable uploaded schedule (block table, lengths, positions).
+
+    Bound to the device and stream current at creation; use it on that
+    stream.  ``rebind`` / ``set_word`` change the device words in place,
+    stream-ordered, keeping the grid-defining header (graph replays stay
+    valid).
+    """
+
+    def __init__(self, lens, qseq, qpos, table, page_size: int, pages: int, stream=None,
+                 words=None):
+        self.words = encode_plan(lens, qseq, qpos, table, page_size, pages) if words is None \
+            else _u32_array(words)
+        self.device = torch.cuda.current_device()
+        self.stream = _stream_handle(stream)
+        h = ctypes.c_void_p()
+        check(lib().pkv_plan_create(_ptr32(self.words), self.words.size,
+                                    ctypes.c_void_p(self.stream), ctypes.byref(h)))
+        self._h = h
+        self._pinned = None
+        self._event = None
+
+    @classmethod
+    def from_words(cls, words, stream=None) -> "Plan":
+        return cls(None, None, None, None, 0, 0, stream=stream, words=words)
+
+    # header fields
+    @property
+    def queries(self) -> int: return int(self.words[2])
+    @property
+    def sequences(self) -> int: return int(self.words[3])
+    @property
+    def table_width(self) -> int: return int(self.words[4])
+    @property
+    def page_size(self) -> int: return int(self.words[5])
+    @property
+    def pages(self) -> int: return int(self.words[6])
+    @property
+    def n_rows(self) -> int: return int(self.words[7])
+    @property
+    def n_tiles(self) -> int: return int(self.words[8])
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise PKVError("EINVAL", "plan is closed")
+        return self._h
+
+    def rebind(self, lens, qseq, qpos, table) -> None:
+        """New schedule of the same shape, copied stream-ordered from pinned memory."""
+        self.rebind_words(encode_plan(lens, qseq, qpos, table, self.page_size, self.pages))
+
+    def rebind_words(self, words) -> None:
+        w = _u32_array(words)
+        if self._pinned is None or self._pinned.numel() != w.size:
+            self._pinned = torch.empty(w.size, dtype=torch.int32, pin_memory=True)
+            self._event = torch.cuda.Event()
+        else:
+            self._event.synchronize()  # the previous copy has read the buffer
+        self._pinned.numpy().view(np.uint32)[:] = w
+        check(lib().pkv_plan_rebind_async(self.handle, ctypes.c_void_p(self._pinned.data_ptr()),
+                                          w.size, ctypes.c_void_p(self.stream)))
+        self._event.record(torch.cuda.ExternalStream(self.stream) if self.stream else
+                           torch.cuda.default_stream())
+        self.words = w.copy()
+
+    def set_word(self, index: int, value: int) -> None:
+        """One word, set with hipMemsetD32Async (value passed by copy)."""
+        check(lib().pkv_plan_set_word_async(self.handle, int(index), int(value),
+                                            ctypes.c_void_p(self.stream)))
+        self.words[int(index)] = int(value)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            lib().pkv_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Workspace:
+    """f32 split partials for ``splits`` parts; reusable across plans with the
+    same queries, heads and value dim on the same stream."""
+
+    def __init__(self, queries: int, heads: int, dv: int, splits: int, stream=None):
+        self.stream = _stream_handle(stream)
+        self.queries, self.heads, self.dv, self.splits = int(queries), int(heads), int(dv), int(splits)
+        h = ctypes.c_void_p()
+        check(lib().pkv_workspace_create(self.queries, self.heads, self.dv, self.splits,
+                                         ctypes.c_void_p(self.stream), ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise PKVError("EINVAL", "workspace is closed")
+        return self._h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            lib().pkv_workspace_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def suggest_splits(plan: Plan, q_heads: int, kv_heads: int, value_dim: int) -> int:
+    """Split count that fills the GPU for this plan (heuristic, capped by the
+    workspace limit)."""
+    return int(lib().pkv_suggest_splits(plan.handle, int(q_heads), int(kv_heads), int(value_dim)))
+
+
+def _dtype_code(*ts) -> int:
+    dt = ts[0].dtype
+    for t in ts:
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise PKVError("EINVAL", "paged operands require contiguous, same-device, same-dtype float tensors")
+        if t.device != ts[0].device:
+            raise PKVError("EINVAL", "paged operands require contiguous, same-device, same-dtype float tensors")
+    if dt not in _DTYPES:
+        raise PKVError("EINVAL", "paged operands must be F32, F16 or BF16")
+    return _DTYPES[dt]
+
+
+def attention(plan: Plan, q, k, v, scale: float, causal: bool = True, workspace=None, out=None):
+    """Paged MHA/GQA attention; returns ``out`` [Q, Hq, Dv]."""
+    if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise PKVError("EINVAL", "invalid paged tensor ranks")
+    qn, hq, d = q.shape
+    n, ps, hkv, dk = k.shape
+    dv = v.shape[3]
+    if qn != plan.queries or n != plan.pages or ps != plan.page_size or dk != d \
+            or tuple(v.shape[:3]) != (n, ps, hkv):
+        raise PKVError("ESHAPE", "incompatible paged head/cache/output shape")
+    if out is None:
+        out = torch.empty((qn, hq, dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (qn, hq, dv):
+        raise PKVError("ESHAPE", "incompatible paged head/cache/output shape")
+    code = _dtype_code(q, k, v, out)
+    check(lib().pkv_attention(plan.handle, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              out.data_ptr(), hq, hkv, d, dv, float(scale), int(bool(causal)),
+                              workspace.handle if workspace is not None else None,
+                              ctypes.c_void_p(plan.stream)))
+    return out
+
+
+def mla(plan: Plan, q_abs, q_pos, latent, k_pos, scale: float, causal: bool = True,
+        workspace=None, out=None):
+    """Absorbed MLA over one shared latent head; returns ``out`` [Q, H, R]."""
+    if latent.dim() != 4 or latent.shape[2] != 1:
+        raise PKVError("EINVAL", "MLA latent cache must have one shared head")
+    if q_abs.dim() != 3 or q_pos.dim() != 3 or k_pos.dim() != 4:
+        raise PKVError("EINVAL", "invalid paged tensor ranks")
+    qn, h, r = q_abs.shape
+    p = q_pos.shape[2]
+    n, ps = latent.shape[0], latent.shape[1]
+    if qn != plan.queries or n != plan.pages or ps != plan.page_size or latent.shape[3] != r \
+            or tuple(q_pos.shape[:2]) != (qn, h) or tuple(k_pos.shape[:3]) != (n, ps, 1) \
+            or k_pos.shape[3] != p:
+        raise PKVError("ESHAPE", "incompatible MLA positional dimensions")
+    if out is None:
+        out = torch.empty((qn, h, r), dtype=q_abs.dtype, device=q_abs.device)
+    elif tuple(out.shape) != (qn, h, r):
+        raise PKVError("ESHAPE", "incompatible paged head/cache/output shape")
+    code = _dtype_code(q_abs, q_pos, latent, k_pos, out)
+    check(lib().pkv_mla(plan.handle, code, q_abs.data_ptr(), q_pos.data_ptr(), latent.data_ptr(),
+                        k_pos.data_ptr(), out.data_ptr(), h, r, p, float(scale),
+                        int(bool(causal)), workspace.handle if workspace is not None else None,
+                        ctypes.c_void_p(plan.stream)))
+    return out

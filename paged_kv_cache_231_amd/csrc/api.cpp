@@ -1,0 +1,442 @@
+// C ABI of libpkv: plan and workspace objects, argument validation and
+// kernel dispatch.
+//
+// Validation mirrors the checks of the ruDNN 0.1.7 `paged_attention` page
+// (`check_tensor`, `bounded`, `execute_attention_into`): every check runs
+// before the first launch, so a failing call launches nothing and leaves
+// `out` untouched; Q == 0 returns after the checks with no launch.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+struct pkv_plan {
+  int device = -1;
+  hipStream_t stream = nullptr;
+  uint32_t *dev = nullptr;
+  std::vector<uint32_t> host;
+  pkv::PlanLayout L;
+};
+
+struct pkv_workspace {
+  int device = -1;
+  hipStream_t stream = nullptr;
+  uint32_t queries = 0, heads = 0, dv = 0, splits = 0;
+  float *buf = nullptr;
+  size_t bytes = 0;
+};
+
+namespace pkv {
+namespace {
+
+constexpr uint64_t kU32Max = 0xFFFFFFFFull;
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool u32_elems(std::initializer_list<uint64_t> dims) {
+  uint64_t n = 1;
+  for (uint64_t d : dims) {
+    if (d > kU32Max) return false;
+    if (d != 0 && n > kU32Max / d) return false;
+    n *= d;
+  }
+  return n <= kU32Max;
+}
+
+bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) {
+  if (!a || !b || a_bytes == 0 || b_bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
+}
+
+size_t elem_size(pkv_dtype dt) { return dt == PKV_F32 ? 4 : 2; }
+
+pkv_status check_binding(const pkv_plan *plan, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PKV_EHIP, "hipGetDevice failed");
+  if (dev != plan->device || stream != plan->stream)
+    return fail(PKV_EDEVICE, "metadata belongs to another device/stream");
+  return PKV_OK;
+}
+
+PlanView view_of(const pkv_plan *p) {
+  PlanView v;
+  v.words = p->dev;
+  v.lens = uint32_t(p->L.lens);
+  v.qseq = uint32_t(p->L.qseq);
+  v.qpos = uint32_t(p->L.qpos);
+  v.table = uint32_t(p->L.table);
+  v.W = p->L.W;
+  v.ps = p->L.ps;
+  v.N = p->L.N;
+  return v;
+}
+
+pkv_status check_workspace(const pkv_workspace *ws, const pkv_plan *plan, uint32_t heads,
+                           uint32_t dv, hipStream_t stream) {
+  if (!ws) return PKV_OK;
+  if (ws->queries != plan->L.Q || ws->heads != heads || ws->dv != dv || ws->stream != stream ||
+      ws->device != plan->device)
+    return fail(PKV_EWORKSPACE, "split workspace shape/device/stream mismatch");
+  return PKV_OK;
+}
+
+pkv_status hip_fail(hipError_t e) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_EHIP, "kernel launch failed");
+}
+
+// Launches the row kernel (and the merge when split) over `qlist`.
+pkv_status run_rows(RowArgs ra, pkv_dtype dt, const pkv_workspace *ws, hipStream_t st) {
+  const bool fast = rows_fast_supported(ra, dt);
+  const uint64_t threads = uint64_t(ra.n_queries) * ra.hq * ra.splits * (fast ? 256u : 64u);
+  if (threads > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+  hipError_t e = fast ? launch_rows_fast(ra, dt, st) : launch_rows_generic(ra, dt, st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ws && ra.splits > 1) {
+    MergeArgs ma;
+    ma.plan = ra.plan;
+    ma.qlist = ra.qlist;
+    ma.n_queries = ra.n_queries;
+    ma.hq = ra.hq;
+    ma.dv = ra.dv;
+    ma.splits = ra.splits;
+    ma.pages_per_split = ra.pages_per_split;
+    ma.causal = ra.causal;
+    ma.ws_o = ra.ws_o;
+    ma.ws_lse = ra.ws_lse;
+    ma.out = ra.out;
+    e = launch_merge(ma, dt, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return PKV_OK;
+}
+
+void fill_split(RowArgs *ra, const pkv_plan *plan, pkv_workspace *ws) {
+  const uint32_t splits = ws ? ws->splits : 1u;
+  ra->splits = splits;
+  const uint32_t W = plan->L.W ? plan->L.W : 1u;
+  ra->pages_per_split = W / splits + (W % splits != 0);
+  if (ws && splits > 1) {
+    ra->ws_o = ws->buf;
+    ra->ws_lse = ws->buf + uint64_t(ws->queries) * splits * ws->heads * ws->dv;
+  } else {
+    ra->ws_o = nullptr;
+    ra->ws_lse = nullptr;
+  }
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char *pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+
+pkv_status pkv_plan_create(const uint32_t *words, size_t n_words, void *stream, pkv_plan **out) {
+  clear_error();
+  if (!out) return fail(PKV_EINVAL, "out must not be null");
+  *out = nullptr;
+  PlanLayout L;
+  pkv_status st = validate_plan(words, n_words, &L);
+  if (st != PKV_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PKV_EHIP, "hipGetDevice failed");
+  auto *p = new pkv_plan;
+  p->device = dev;
+  p->stream = static_cast<hipStream_t>(stream);
+  p->host.assign(words, words + n_words);
+  p->L = L;
+  if (hipMalloc(&p->dev, n_words * sizeof(uint32_t)) != hipSuccess) {
+    delete p;
+    return fail(PKV_EHIP, "hipMalloc of plan words failed");
+  }
+  if (hipMemcpyAsync(p->dev, p->host.data(), n_words * sizeof(uint32_t), hipMemcpyHostToDevice,
+                     p->stream) != hipSuccess) {
+    (void)hipFree(p->dev);
+    delete p;
+    return fail(PKV_EHIP, "plan upload failed");
+  }
+  *out = p;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_rebind_async(pkv_plan *plan, const uint32_t *words, size_t n_words,
+                                 void *stream) {
+  clear_error();
+  if (!plan) return fail(PKV_EINVAL, "null plan");
+  pkv_status st = check_binding(plan, static_cast<hipStream_t>(stream));
+  if (st != PKV_OK) return st;
+  PlanLayout L;
+  st = validate_plan(words, n_words, &L);
+  if (st != PKV_OK) return st;
+  if (n_words != plan->host.size() || std::memcmp(words + 2, plan->host.data() + 2, 7 * 4) != 0)
+    return fail(PKV_ESHAPE, "rebind must keep Q, S, W, ps, N, R and T");
+  if (hipMemcpyAsync(plan->dev, words, n_words * sizeof(uint32_t), hipMemcpyHostToDevice,
+                     plan->stream) != hipSuccess)
+    return fail(PKV_EHIP, "plan rebind copy failed");
+  std::memcpy(plan->host.data(), words, n_words * sizeof(uint32_t));
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_set_word_async(pkv_plan *plan, size_t index, uint32_t value, void *stream) {
+  clear_error();
+  if (!plan) return fail(PKV_EINVAL, "null plan");
+  pkv_status st = check_binding(plan, static_cast<hipStream_t>(stream));
+  if (st != PKV_OK) return st;
+  if (index < PKV_PLAN_HEADER_WORDS || index >= plan->host.size())
+    return fail(PKV_EINVAL, "word index outside the plan body");
+  const uint32_t old = plan->host[index];
+  plan->host[index] = value;
+  st = validate_plan(plan->host.data(), plan->host.size(), nullptr);
+  if (st != PKV_OK) {
+    plan->host[index] = old;
+    return st;
+  }
+  if (hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(plan->dev + index), int(value), 1,
+                        plan->stream) != hipSuccess) {
+    plan->host[index] = old;
+    return fail(PKV_EHIP, "hipMemsetD32Async failed");
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_header(const pkv_plan *plan, uint32_t *header) {
+  clear_error();
+  if (!plan || !header) return fail(PKV_EINVAL, "null argument");
+  std::memcpy(header, plan->host.data(), PKV_PLAN_HEADER_WORDS * sizeof(uint32_t));
+  return PKV_OK;
+}
+
+const uint32_t *pkv_plan_device_words(const pkv_plan *plan) { return plan ? plan->dev : nullptr; }
+
+void pkv_plan_destroy(pkv_plan *plan) {
+  if (!plan) return;
+  if (plan->dev) (void)hipFree(plan->dev);
+  delete plan;
+}
+
+pkv_status pkv_workspace_create(uint32_t queries, uint32_t heads, uint32_t dv, uint32_t splits,
+                                void *stream, pkv_workspace **out) {
+  clear_error();
+  if (!out) return fail(PKV_EINVAL, "out must not be null");
+  *out = nullptr;
+  if (splits < 1 || splits > PKV_MAX_SPLITS) return fail(PKV_EINVAL, "split count outside 1..PKV_MAX_SPLITS");
+  if (queries == 0 || heads == 0 || dv == 0) return fail(PKV_EINVAL, "workspace dimensions must be positive");
+  const uint64_t rows = uint64_t(queries) * splits * heads;
+  const uint64_t bytes = rows * (uint64_t(dv) + 1) * sizeof(float);
+  if (bytes > PKV_WORKSPACE_LIMIT_BYTES) return fail(PKV_ERANGE, "workspace above PKV_WORKSPACE_LIMIT_BYTES");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PKV_EHIP, "hipGetDevice failed");
+  auto *w = new pkv_workspace;
+  w->device = dev;
+  w->stream = static_cast<hipStream_t>(stream);
+  w->queries = queries;
+  w->heads = heads;
+  w->dv = dv;
+  w->splits = splits;
+  w->bytes = size_t(bytes);
+  if (hipMalloc(&w->buf, w->bytes) != hipSuccess) {
+    delete w;
+    return fail(PKV_EHIP, "hipMalloc of workspace failed");
+  }
+  *out = w;
+  return PKV_OK;
+}
+
+uint32_t pkv_workspace_splits(const pkv_workspace *ws) { return ws ? ws->splits : 0u; }
+
+void pkv_workspace_destroy(pkv_workspace *ws) {
+  if (!ws) return;
+  if (ws->buf) (void)hipFree(ws->buf);
+  delete ws;
+}
+
+uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads, uint32_t kv_heads,
+                            uint32_t value_dim) {
+  if (!plan || plan->L.Q == 0 || plan->L.W == 0) return 1;
+  int cus = 256;
+  int dev = plan->device;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const PlanLayout &L = plan->L;
+  const uint32_t *w = plan->host.data();
+  // pages of every query attended one at a time (non-causal upper bound)
+  std::vector<uint32_t> pages;
+  const bool tiles = L.T > 0;
+  const uint32_t nq = tiles ? L.R : L.Q;
+  pages.reserve(nq);
+  for (uint32_t r = 0; r < nq; ++r) {
+    const uint32_t i = tiles ? w[L.rows + r] : r;
+    const uint32_t len = w[L.lens + w[L.qseq + i]];
+    pages.push_back(len / L.ps + (len % L.ps != 0));
+  }
+  const uint64_t target = uint64_t(cus) * 8;              // blocks in flight to aim for
+  const uint32_t min_pages = std::max(1u, 256u / L.ps);    // >= 256 tokens per part
+  uint32_t smax = std::min<uint32_t>(PKV_MAX_SPLITS, L.W);
+  const uint64_t per_split = uint64_t(L.Q) * std::max(1u, q_heads) * (uint64_t(value_dim) + 1) * 4;
+  smax = uint32_t(std::min<uint64_t>(smax, std::max<uint64_t>(1, PKV_WORKSPACE_LIMIT_BYTES / per_split)));
+  uint32_t best = 1;
+  for (uint32_t s = 1; s <= smax; ++s) {
+    const uint32_t pp = L.W / s + (L.W % s != 0);
+    if (pp < min_pages) break;
+    uint64_t blocks = 0;
+    for (uint32_t pg : pages) blocks += std::min<uint32_t>(s, pg / pp + (pg % pp != 0));
+    blocks *= std::max(1u, kv_heads);
+    best = s;
+    if (blocks >= target) break;
+  }
+  return best;
+}
+
+pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, const void *k,
+                         const void *v, void *out, uint32_t hq, uint32_t hkv, uint32_t d,
+                         uint32_t dv, float scale, int causal, pkv_workspace *ws, void *stream_) {
+  clear_error();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!plan) return fail(PKV_EINVAL, "null plan");
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "paged operands must be F32, F16 or BF16");
+  if (hq == 0 || hkv == 0 || hq % hkv != 0 || d == 0 || dv == 0 || d > 1024 || dv > 1024)
+    return fail(PKV_ESHAPE, "incompatible paged head/cache/output shape");
+  if (!std::isfinite(scale) || scale <= 0.f) return fail(PKV_EINVAL, "scale must be finite and positive");
+  const PlanLayout &L = plan->L;
+  if (!u32_elems({L.Q, hq, d}) || !u32_elems({L.N, L.ps, hkv, d}) || !u32_elems({L.N, L.ps, hkv, dv}) ||
+      !u32_elems({L.Q, hq, dv}))
+    return fail(PKV_ERANGE, "paged tensor exceeds U32 indexing");
+  pkv_status st = check_binding(plan, stream);
+  if (st != PKV_OK) return st;
+  st = check_workspace(ws, plan, hq, dv, stream);
+  if (st != PKV_OK) return st;
+  if (L.Q == 0) return PKV_OK;
+  const bool have_cache = uint64_t(L.N) * L.ps > 0;
+  if (!q || !out || (have_cache && (!k || !v))) return fail(PKV_EINVAL, "null tensor pointer");
+  const uint64_t es = elem_size(dtype);
+  const uint64_t out_b = uint64_t(L.Q) * hq * dv * es;
+  if (overlaps(out, out_b, q, uint64_t(L.Q) * hq * d * es) ||
+      overlaps(out, out_b, k, uint64_t(L.N) * L.ps * hkv * d * es) ||
+      overlaps(out, out_b, v, uint64_t(L.N) * L.ps * hkv * dv * es))
+    return fail(PKV_EINVAL, "output overlaps an input");
+
+  RowArgs ra{};
+  ra.plan = view_of(plan);
+  ra.hq = hq;
+  ra.hkv = hkv;
+  ra.d = d;
+  ra.dv = dv;
+  ra.pdim = 0;
+  ra.causal = causal ? 1 : 0;
+  ra.scale_log2 = scale * kLog2e;
+  ra.q = q;
+  ra.k = k;
+  ra.v = v;
+  ra.qp = nullptr;
+  ra.kp = nullptr;
+  ra.k_tok = uint64_t(hkv) * d;
+  ra.k_page = ra.k_tok * L.ps;
+  ra.v_tok = uint64_t(hkv) * dv;
+  ra.v_page = ra.v_tok * L.ps;
+  ra.kp_tok = ra.kp_page = 0;
+  ra.out = out;
+  fill_split(&ra, plan, ws);
+
+  TileArgs ta{};
+  ta.plan = ra.plan;
+  ta.tiles = plan->dev + L.tiles;
+  ta.n_tiles = L.T;
+  ta.hq = hq;
+  ta.hkv = hkv;
+  ta.d = d;
+  ta.dv = dv;
+  ta.causal = ra.causal;
+  ta.scale_log2 = ra.scale_log2;
+  ta.q = q;
+  ta.k = k;
+  ta.v = v;
+  ta.k_page = ra.k_page;
+  ta.k_tok = ra.k_tok;
+  ta.v_page = ra.v_page;
+  ta.v_tok = ra.v_tok;
+  ta.out = out;
+  const bool use_tiles = L.T > 0 && tiles_supported(ta, dtype);
+  ra.qlist = use_tiles ? plan->dev + L.rows : nullptr;
+  ra.n_queries = use_tiles ? L.R : L.Q;
+
+  if (ra.n_queries) {
+    st = run_rows(ra, dtype, ws, stream);
+    if (st != PKV_OK) return st;
+  }
+  if (use_tiles) {
+    hipError_t e = launch_tiles(ta, dtype, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs, const void *q_pos,
+                   const void *latent, const void *k_pos, void *out, uint32_t heads, uint32_t rank,
+                   uint32_t pos_dim, float scale, int causal, pkv_workspace *ws, void *stream_) {
+  clear_error();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!plan) return fail(PKV_EINVAL, "null plan");
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "paged operands must be F32, F16 or BF16");
+  if (heads == 0 || rank == 0 || rank > 1024)
+    return fail(PKV_ESHAPE, "incompatible paged head/cache/output shape");
+  if (pos_dim == 0 || pos_dim > 256) return fail(PKV_ESHAPE, "incompatible MLA positional dimensions");
+  if (!std::isfinite(scale) || scale <= 0.f) return fail(PKV_EINVAL, "scale must be finite and positive");
+  const PlanLayout &L = plan->L;
+  if (!u32_elems({L.Q, heads, rank}) || !u32_elems({L.Q, heads, pos_dim}) ||
+      !u32_elems({L.N, L.ps, 1, rank}) || !u32_elems({L.N, L.ps, 1, pos_dim}))
+    return fail(PKV_ERANGE, "paged tensor exceeds U32 indexing");
+  pkv_status st = check_binding(plan, stream);
+  if (st != PKV_OK) return st;
+  st = check_workspace(ws, plan, heads, rank, stream);
+  if (st != PKV_OK) return st;
+  if (L.Q == 0) return PKV_OK;
+  const bool have_cache = uint64_t(L.N) * L.ps > 0;
+  if (!q_abs || !q_pos || !out || (have_cache && (!latent || !k_pos)))
+    return fail(PKV_EINVAL, "null tensor pointer");
+  const uint64_t es = elem_size(dtype);
+  const uint64_t out_b = uint64_t(L.Q) * heads * rank * es;
+  if (overlaps(out, out_b, q_abs, uint64_t(L.Q) * heads * rank * es) ||
+      overlaps(out, out_b, q_pos, uint64_t(L.Q) * heads * pos_dim * es) ||
+      overlaps(out, out_b, latent, uint64_t(L.N) * L.ps * rank * es) ||
+      overlaps(out, out_b, k_pos, uint64_t(L.N) * L.ps * pos_dim * es))
+    return fail(PKV_EINVAL, "output overlaps an input");
+
+  RowArgs ra{};
+  ra.plan = view_of(plan);
+  ra.hq = heads;
+  ra.hkv = 1;
+  ra.d = rank;
+  ra.dv = rank;
+  ra.pdim = pos_dim;
+  ra.causal = causal ? 1 : 0;
+  ra.scale_log2 = scale * kLog2e;
+  ra.q = q_abs;
+  ra.k = latent;
+  ra.v = latent;
+  ra.qp = q_pos;
+  ra.kp = k_pos;
+  ra.k_tok = rank;
+  ra.k_page = uint64_t(rank) * L.ps;
+  ra.v_tok = rank;
+  ra.v_page = ra.k_page;
+  ra.kp_tok = pos_dim;
+  ra.kp_page = uint64_t(pos_dim) * L.ps;
+  ra.out = out;
+  ra.qlist = nullptr;
+  ra.n_queries = L.Q;
+  fill_split(&ra, plan, ws);
+  return run_rows(ra, dtype, ws, stream);
+}
+
+}  // extern "C"

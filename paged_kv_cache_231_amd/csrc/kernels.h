@@ -1,0 +1,70 @@
+// Kernel argument blocks and launchers shared by the host dispatcher
+// (api.cpp) and the HIP sources.  All strides are in elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Where a kernel finds the schedule inside the device plan words.
+struct PlanView {
+  const uint32_t *words;  // device copy of the spec-v1 plan
+  uint32_t lens, qseq, qpos, table;  // word offsets of the sections
+  uint32_t W, ps, N;                 // table width, page size, pool pages
+};
+
+// One launch of a per-query ("row") kernel over a list of queries.
+struct RowArgs {
+  PlanView plan;
+  const uint32_t *qlist;  // device list of query indices, or null = 0..n-1
+  uint32_t n_queries;     // queries in the list (grid)
+  uint32_t hq, hkv, d, dv, pdim;  // pdim: MLA position dim, 0 for attention
+  uint32_t splits, pages_per_split;
+  int causal;
+  float scale_log2;  // scale * log2(e): scores are kept in base 2
+  const void *q, *k, *v;     // MLA: k = v = latent
+  const void *qp, *kp;       // MLA position parts (null for attention)
+  uint64_t k_page, k_tok;    // k: page stride, token stride
+  uint64_t v_page, v_tok;
+  uint64_t kp_page, kp_tok;
+  void *out;                 // [Q, hq, dv] in the input dtype (splits == 1)
+  float *ws_o, *ws_lse;      // [Q, splits, hq, dv], [Q, splits, hq] (splits > 1)
+};
+
+struct MergeArgs {
+  PlanView plan;
+  const uint32_t *qlist;
+  uint32_t n_queries;
+  uint32_t hq, dv, splits, pages_per_split;
+  int causal;
+  const float *ws_o, *ws_lse;
+  void *out;
+};
+
+// Query tiles of the chunked-prefill kernel.
+struct TileArgs {
+  PlanView plan;
+  const uint32_t *tiles;  // device {first, count} pairs
+  uint32_t n_tiles;
+  uint32_t hq, hkv, d, dv;
+  int causal;
+  float scale_log2;
+  const void *q, *k, *v;
+  uint64_t k_page, k_tok, v_page, v_tok;
+  void *out;
+};
+
+hipError_t launch_rows_generic(const RowArgs &a, pkv_dtype dt, hipStream_t st);
+// Fast VALU decode; returns hipErrorNotSupported when the shape is not one
+// of its specialisations (the caller then uses the generic kernel).
+bool rows_fast_supported(const RowArgs &a, pkv_dtype dt);
+hipError_t launch_rows_fast(const RowArgs &a, pkv_dtype dt, hipStream_t st);
+hipError_t launch_merge(const MergeArgs &a, pkv_dtype dt, hipStream_t st);
+bool tiles_supported(const TileArgs &a, pkv_dtype dt);
+hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st);
+
+}  // namespace pkv
