@@ -93,10 +93,19 @@ pkv_status hip_fail(hipError_t e) {
 
 // Launches the row kernel (and the merge when split) over `qlist`.
 pkv_status run_rows(RowArgs ra, pkv_dtype dt, const pkv_workspace *ws, hipStream_t st) {
-  const bool fast = rows_fast_supported(ra, dt);
-  const uint64_t threads = uint64_t(ra.n_queries) * ra.hq * ra.splits * (fast ? 256u : 64u);
-  if (threads > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
-  hipError_t e = fast ? launch_rows_fast(ra, dt, st) : launch_rows_generic(ra, dt, st);
+  hipError_t e;
+  if (rows_mfma_supported(ra, dt)) {
+    if (rows_mfma_blocks(ra) * 256u > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+    e = launch_rows_mfma(ra, dt, st);
+  } else if (rows_fast_supported(ra, dt)) {
+    if (uint64_t(ra.n_queries) * ra.hq * ra.splits * 256u > kU32Max)
+      return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+    e = launch_rows_fast(ra, dt, st);
+  } else {
+    if (uint64_t(ra.n_queries) * ra.hq * ra.splits * 64u > kU32Max)
+      return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+    e = launch_rows_generic(ra, dt, st);
+  }
   if (e != hipSuccess) return hip_fail(e);
   if (ws && ra.splits > 1) {
     MergeArgs ma;

@@ -1,0 +1,432 @@
+// Decode kernel on MFMA for F16/BF16, head_dim == value_dim in {64, 128, 256}.
+//
+// Computes the attention of the ruDNN 0.1.7 `paged_attention` page
+// (`DevicePlan::attention` doc) for queries attended one at a time.  For one
+// query and one KV head, the G q heads of its group (no per-head KV repeat,
+// module doc) form a dense contraction: S^T[tokens x heads] = K . Q^T over
+// the head dimension, then O^T[d x heads] += V^T . P^T over the tokens.  Both
+// run on 16x16 MFMA tiles with the tokens on the M side, so the paged K rows
+// feed the A operand with plain 16-byte loads and the softmax probabilities
+// come out of the first product already in the B-operand layout of the
+// second.  Only V needs a transpose, done through LDS.
+//
+// A block of four waves owns one (query, KV head, group of up to 16 q heads,
+// split part); its waves take 16-token tiles of the part in turn, each with
+// its own online softmax (base 2), merged through LDS at the end.  Max and
+// sum reductions across lanes use shuffles; no cross-wave traffic happens
+// inside the token loop.
+//
+// MFMA lane layouts used (16x16 tiles, lane l, j = l / 16):
+//   A [16 x K]: lane l holds row l % 16, K-slots (j, 0..e-1)
+//   B [K x 16]: lane l holds column l % 16, K-slots (j, 0..e-1)
+//   C [16 x 16] f32: lane l holds rows 4j + 0..3 of column l % 16
+// Only the C layout fixes meaning; the K-slot order just has to agree
+// between A and B, and it does because both are filled with one mapping.
+
+#include "device_common.h"
+
+namespace pkv {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <class DT>
+struct Mfma;
+
+template <>
+struct Mfma<BF16> {
+  // S^T += K(16 tokens x 32 d) . Q^T(32 d x 16 heads)
+  static __device__ __forceinline__ f32x4_t qk(const uint4 &a, const uint4 &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // O^T += V^T(16 d x 16 tokens) . P^T(16 tokens x 16 heads)
+  static __device__ __forceinline__ f32x4_t pv(const uint2 &a, const uint2 &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return BF16::pack2(lo, hi); }
+  static __device__ __forceinline__ float to_f(uint16_t x) { return BF16::to_f(x); }
+  static __device__ __forceinline__ uint16_t from_f(float x) { return BF16::from_f(x); }
+};
+
+template <>
+struct Mfma<F16> {
+  static __device__ __forceinline__ f32x4_t qk(const uint4 &a, const uint4 &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(const uint2 &a, const uint2 &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const _Float16 a = _Float16(lo), b = _Float16(hi);
+    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+  }
+  static __device__ __forceinline__ float to_f(uint16_t x) { return float(__builtin_bit_cast(_Float16, x)); }
+  static __device__ __forceinline__ uint16_t from_f(float x) {
+    return __builtin_bit_cast(uint16_t, _Float16(x));
+  }
+};
+
+constexpr int kWaves = 4;
+constexpr int kTile = 16;   // tokens per wave iteration
+constexpr int kHeads = 16;  // q heads per block (MFMA N)
+
+template <int D>
+struct Lds {
+  static constexpr int kRow = D * 2 + 16;  // bytes per staged row (padding spreads banks)
+  static constexpr int kTileBytes = 2 * kTile * kRow;  // K tile, then V tile
+  static constexpr int kOStride = D + 4;   // floats per head row in the merge area
+  static constexpr int kVBytes = kWaves * kTileBytes;
+  static constexpr int kOBytes = kWaves * kHeads * kOStride * 4;
+  static constexpr int kBytes = kVBytes > kOBytes ? kVBytes : kOBytes;
+};
+
+// K/V rows of one 16-token tile as loaded from the cache: each load
+// instruction covers RPI whole rows (CPR 16-byte chunks each, lane l taking
+// row RPI*n + l/CPR, chunk l%CPR), read with the streaming hint.  Whole-row
+// instructions keep HBM busy; the MFMA layouts are produced from LDS.
+template <int D>
+struct TileRegs {
+  static constexpr int KS = D / 32;    // loads per lane per tensor
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR; // rows per load instruction
+  uint4 k[KS], v[KS];
+  uint32_t valid16;  // bit r: token r of the tile exists
+};
+
+// Where the tokens of the wave's tiles live.  With PAGE_UNIFORM (page size a
+// power of two >= 16) every tile lies inside one page; the page numbers of
+// up to 64 consecutive tiles of the wave are held one per lane and read with
+// readlane, so the token loop issues no table loads.
+template <bool PAGE_UNIFORM>
+struct TileMap {
+  const uint32_t *table;
+  uint32_t t_lo, t_hi, wv, ps, ps_shift, n_pages_pool;
+  uint32_t lane_page;  // page of tile (base + lane)
+  uint32_t base;       // first tile held in lane_page
+
+  __device__ __forceinline__ uint32_t tile_start(uint32_t k) const {
+    return t_lo + (wv + 4u * k) * 16u;
+  }
+  __device__ __forceinline__ void fill(uint32_t k0, uint32_t lane) {
+    base = k0;
+    const uint32_t t0 = tile_start(k0 + lane);
+    lane_page = (PAGE_UNIFORM && t0 < t_hi) ? table[t0 >> ps_shift] : 0u;
+  }
+};
+
+template <class DT, int D, bool PU>
+__device__ __forceinline__ void load_tile(TileRegs<D> &t, const RowArgs &a, TileMap<PU> &map,
+                                          const typename DT::T *kbase,
+                                          const typename DT::T *vbase, uint32_t k,
+                                          uint32_t lane) {
+  using TR = TileRegs<D>;
+  const uint32_t t0 = map.tile_start(k);
+  const uint32_t chunk = lane % TR::CPR;
+  // A row past the end reads row 0 of page 0 (inside the pool whenever any
+  // token exists).  Its K feeds only scores masked to -inf and its V is
+  // replaced by zeros when staged (a select, so NaN never leaks).  The loads
+  // are unconditional, which keeps them in flight across the attention of
+  // the previous tile.  Element offsets fit in 32 bits: every cache tensor
+  // has < 2^32 elements.
+  if constexpr (PU) {
+    const uint32_t page = __builtin_amdgcn_readlane(map.lane_page, k - map.base);
+    const uint32_t rows = map.t_hi - t0 < 16u ? map.t_hi - t0 : 16u;
+    const bool page_ok = page < map.n_pages_pool;  // never read outside the pool
+    t.valid16 = page_ok ? (1u << rows) - 1u : 0u;
+    const uint32_t slot0 = t0 & (map.ps - 1);
+#pragma unroll
+    for (int n = 0; n < TR::KS; ++n) {
+      const uint32_t r = TR::RPI * n + lane / TR::CPR;
+      const bool ok = page_ok && r < rows;
+      const uint32_t ko = ok ? page * uint32_t(a.k_page) + (slot0 + r) * uint32_t(a.k_tok) : 0u;
+      const uint32_t vo = ok ? page * uint32_t(a.v_page) + (slot0 + r) * uint32_t(a.v_tok) : 0u;
+      t.k[n] = load_stream16(kbase + ko + 8u * chunk);
+      t.v[n] = load_stream16(vbase + vo + 8u * chunk);
+    }
+  } else {
+    uint32_t valid = 0;
+#pragma unroll
+    for (int n = 0; n < TR::KS; ++n) {
+      const uint32_t r = TR::RPI * n + lane / TR::CPR;
+      const uint32_t tok = t0 + r;
+      bool ok = tok < map.t_hi;
+      const uint32_t lp = map.ps_shift != 32u ? tok >> map.ps_shift : tok / map.ps;
+      const uint32_t slot = tok - lp * map.ps;
+      const uint32_t page = ok ? map.table[lp] : 0u;
+      ok = ok && page < map.n_pages_pool;  // never read outside the pool
+      valid |= ok ? 1u << r : 0u;
+      const uint32_t ko = ok ? page * uint32_t(a.k_page) + slot * uint32_t(a.k_tok) : 0u;
+      const uint32_t vo = ok ? page * uint32_t(a.v_page) + slot * uint32_t(a.v_tok) : 0u;
+      t.k[n] = load_stream16(kbase + ko + 8u * chunk);
+      t.v[n] = load_stream16(vbase + vo + 8u * chunk);
+    }
+    // every lane knows the rows it loaded; OR them across the wave
+    uint32_t all = valid;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) all |= __shfl_xor(all, o, 64);
+    t.valid16 = all & 0xffffu;
+  }
+}
+
+// Online-softmax state of one wave: running max m (base 2, uniform across
+// the four lane groups of a head), this lane's partial sum and O^T tiles.
+template <int D>
+struct WaveState {
+  f32x4_t o[D / 16];
+  float m, lsum;
+};
+
+template <class DT, int D>
+__device__ __forceinline__ void attend_tile(WaveState<D> &st, const TileRegs<D> &t,
+                                            const uint4 *qb, unsigned char *vt, float sl2,
+                                            uint32_t lane) {
+  using M = Mfma<DT>;
+  using L = Lds<D>;
+  constexpr int KS = D / 32, DB = D / 16;
+  const uint32_t c16 = lane & 15u, j = lane >> 4;
+  // stage the K and V rows (same byte layout as the cache rows); rows past
+  // the end get zero V
+  using TR = TileRegs<D>;
+  unsigned char *kt = vt;
+  unsigned char *vtile = vt + kTile * L::kRow;
+#pragma unroll
+  for (int n = 0; n < KS; ++n) {
+    const uint32_t r = TR::RPI * n + lane / TR::CPR;
+    const uint32_t off = r * L::kRow + 16u * (lane % TR::CPR);
+    *reinterpret_cast<uint4 *>(kt + off) = t.k[n];
+    *reinterpret_cast<uint4 *>(vtile + off) =
+        ((t.valid16 >> r) & 1u) ? t.v[n] : make_uint4(0, 0, 0, 0);
+  }
+
+  // S^T = K . Q^T : A = K[token c16][chunk 4ks + j]; rows = tokens 4j+0..3,
+  // column = head c16
+  f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint4 ka = *reinterpret_cast<const uint4 *>(kt + c16 * L::kRow + 16 * (4 * ks + j));
+    s = M::qk(ka, qb[ks], s);
+  }
+
+  float x[4];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool v = (t.valid16 >> (4 * j + e)) & 1u;
+    x[e] = v ? s[e] * sl2 : -INFINITY;
+    mt = fmaxf(mt, x[e]);
+  }
+  mt = rows4_max(mt);
+  const float m_new = fmaxf(st.m, mt);
+  const float alpha = fast_exp2(st.m - m_new);
+  st.m = m_new;
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = fast_exp2(x[e] - m_new);
+  st.lsum = st.lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b) st.o[b] *= alpha;
+  }
+  uint2 pb;
+  pb.x = M::pack2(p[0], p[1]);
+  pb.y = M::pack2(p[2], p[3]);
+
+  // O^T += V^T . P^T : A = V^T[d = 16b + c16][tokens 4j+0..3] from LDS
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    const unsigned char *col = vtile + 2 * (16 * b + c16) + 4 * j * L::kRow;
+    const uint32_t v0 = *reinterpret_cast<const uint16_t *>(col);
+    const uint32_t v1 = *reinterpret_cast<const uint16_t *>(col + L::kRow);
+    const uint32_t v2 = *reinterpret_cast<const uint16_t *>(col + 2 * L::kRow);
+    const uint32_t v3 = *reinterpret_cast<const uint16_t *>(col + 3 * L::kRow);
+    uint2 va;
+    va.x = v0 | (v1 << 16);
+    va.y = v2 | (v3 << 16);
+    st.o[b] = M::pv(va, pb, st.o[b]);
+  }
+}
+
+template <class DT, int D, bool PU>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
+  using M = Mfma<DT>;
+  constexpr int KS = D / 32;  // 32-wide K steps of q.k (also 16-byte chunks per lane per row)
+  constexpr int DB = D / 16;  // 16-wide value blocks
+  using L = Lds<D>;
+  __shared__ __align__(16) unsigned char lds[L::kBytes];
+  __shared__ float s_m[kWaves][kHeads], s_l[kWaves][kHeads];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t c16 = lane & 15u, j = lane >> 4;
+  const uint32_t grp = a.hq / a.hkv;
+  const uint32_t hgk = (grp + kHeads - 1) / kHeads;
+  const uint32_t part = blockIdx.x % a.splits;
+  const uint32_t rest = blockIdx.x / a.splits;
+  const uint32_t hsel = rest % (a.hkv * hgk);
+  const uint32_t qi = rest / (a.hkv * hgk);
+  const uint32_t kvh = hsel / hgk, sub = hsel % hgk;
+  const uint32_t i = a.qlist ? a.qlist[qi] : qi;
+  uint32_t seq;
+  const uint32_t n = visible_keys(a.plan, i, a.causal, &seq);
+  const uint32_t ps = a.plan.ps;
+  const uint64_t span = uint64_t(a.pages_per_split) * ps;
+  const uint64_t lo64 = uint64_t(part) * span;
+  if (a.splits > 1 && lo64 >= n) return;  // empty part: the merge skips it
+  const uint32_t t_lo = uint32_t(lo64 < n ? lo64 : n);
+  const uint32_t t_hi = uint32_t(lo64 + span < n ? lo64 + span : n);
+  const uint32_t h0 = kvh * grp + sub * kHeads;               // first q head of the block
+  const uint32_t nh = grp - sub * kHeads < kHeads ? grp - sub * kHeads : kHeads;
+
+  // Q^T as the B operand of q.k: column = head c16, K-slot chunk 4*ks + j.
+  uint4 qb[KS];
+  {
+    const typename DT::T *qrow =
+        static_cast<const typename DT::T *>(a.q) + (uint64_t(i) * a.hq + h0 + c16) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = c16 < nh ? *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j))
+                        : make_uint4(0, 0, 0, 0);
+  }
+
+  WaveState<D> st;
+#pragma unroll
+  for (int b = 0; b < DB; ++b) st.o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = kNoMax;
+  st.lsum = 0.f;
+
+  const typename DT::T *kbase = static_cast<const typename DT::T *>(a.k) + uint64_t(kvh) * D;
+  const typename DT::T *vbase = static_cast<const typename DT::T *>(a.v) + uint64_t(kvh) * D;
+  unsigned char *vt = lds + wv * L::kTileBytes;  // this wave's V tile
+  TileMap<PU> map;
+  map.table = a.plan.words + a.plan.table + uint64_t(seq) * a.plan.W;
+  map.t_lo = t_lo;
+  map.t_hi = t_hi;
+  map.wv = wv;
+  map.ps = ps;
+  const bool pow2 = (ps & (ps - 1)) == 0;
+  map.ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 32u;
+  map.n_pages_pool = a.plan.N;
+  const uint32_t first = t_lo + wv * 16u;
+  const uint32_t n_tiles = first < t_hi ? (t_hi - first + 63u) / 64u : 0u;
+  const float sl2 = a.scale_log2;
+
+  // Software pipeline, two tiles in flight: while one tile is attended the
+  // next one's loads run.  The steady-state loop issues its loads
+  // unconditionally, so the wait before each tile covers only that tile's
+  // loads; page numbers are refilled once per 64 tiles, outside the loop.
+  TileRegs<D> ta, tb;
+  for (uint32_t c0 = 0; c0 < n_tiles; c0 += 64) {
+    const uint32_t cn = n_tiles - c0 < 64u ? n_tiles - c0 : 64u;
+    map.fill(c0, lane);
+    uint32_t k = 0;
+    if (cn >= 4) {
+      load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0, lane);
+      load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + 1, lane);
+      for (; k + 3 < cn; k += 2) {
+        attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
+        load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
+        attend_tile<DT, D>(st, tb, qb, vt, sl2, lane);
+        load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + k + 3, lane);
+      }
+    } else {
+      load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0, lane);
+      if (cn > 1) load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + 1, lane);
+    }
+    // at most three tiles left: k in ta, k + 1 in tb
+    if (k < cn) {
+      attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
+      if (k + 2 < cn) load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
+    }
+    if (k + 1 < cn) attend_tile<DT, D>(st, tb, qb, vt, sl2, lane);
+    if (k + 2 < cn) attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
+  }
+
+  // per-head sum over the four lane groups (m is already uniform across them)
+  const float lsum = rows4_sum(st.lsum);
+  __syncthreads();  // every wave is done with its V tile: reuse LDS for the merge
+  float *so = reinterpret_cast<float *>(lds);
+  {
+    float *mine = so + wv * kHeads * L::kOStride + c16 * L::kOStride;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+      *reinterpret_cast<f32x4_t *>(mine + 16 * b + 4 * j) = st.o[b];
+    if (j == 0) {
+      s_m[wv][c16] = st.m;
+      s_l[wv][c16] = lsum;
+    }
+  }
+  __syncthreads();
+
+  for (uint32_t idx = tid; idx < nh * uint32_t(D); idx += 256) {
+    const uint32_t h = idx / D, d = idx % D;
+    float mx = s_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = fast_exp2(s_m[w][h] - mx);
+      num = fmaf(so[(w * kHeads + h) * L::kOStride + d], sc, num);
+      den = fmaf(s_l[w][h], sc, den);
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    if (a.splits == 1) {
+      auto *out = static_cast<uint16_t *>(a.out) + (uint64_t(i) * a.hq + h0 + h) * D;
+      out[d] = M::from_f(num * inv);
+    } else {
+      const uint64_t r = (uint64_t(i) * a.splits + part) * a.hq + h0 + h;
+      a.ws_o[r * D + d] = num * inv;
+      if (d == 0) a.ws_lse[r] = mx + fast_log2(den);
+    }
+  }
+}
+
+template <class DT, bool PU>
+hipError_t launch_d(const RowArgs &a, dim3 grid, hipStream_t st) {
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<DT, 64, PU>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<DT, 128, PU>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((decode_mfma_kernel<DT, 256, PU>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+bool rows_mfma_supported(const RowArgs &a, pkv_dtype dt) {
+  if (dt != PKV_F16 && dt != PKV_BF16) return false;
+  if (a.pdim != 0 || a.d != a.dv || (a.d != 64 && a.d != 128 && a.d != 256)) return false;
+  if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v)) return false;
+  return true;
+}
+
+uint64_t rows_mfma_blocks(const RowArgs &a) {
+  const uint32_t grp = a.hq / a.hkv;
+  const uint32_t hgk = (grp + kHeads - 1) / kHeads;
+  return uint64_t(a.n_queries) * a.hkv * hgk * a.splits;
+}
+
+hipError_t launch_rows_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
+  const uint64_t blocks = rows_mfma_blocks(a);
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  // page size a power of two >= 16: every 16-token tile lies in one page
+  const uint32_t ps = a.plan.ps;
+  const bool pu = (ps & (ps - 1)) == 0 && ps >= 16u;
+  if (dt == PKV_BF16) return pu ? launch_d<BF16, true>(a, grid, st) : launch_d<BF16, false>(a, grid, st);
+  return pu ? launch_d<F16, true>(a, grid, st) : launch_d<F16, false>(a, grid, st);
+}
+
+}  // namespace pkv

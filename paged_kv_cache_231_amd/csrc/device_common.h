@@ -23,18 +23,27 @@ struct F16 {
 struct BF16 {
   using T = uint16_t;
   static __device__ __forceinline__ float to_f(T x) { return __uint_as_float(uint32_t(x) << 16); }
-  // Round to nearest even; NaN stays NaN (quiet).
-  static __device__ __forceinline__ T from_f(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return T((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return T(u >> 16);
+  // Hardware conversion (v_cvt_pk_bf16_f32): round to nearest even, NaN
+  // stays NaN.
+  static __device__ __forceinline__ T from_f(float f) { return __builtin_bit_cast(T, (__bf16)f); }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    const bf16x2_v v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
   }
 };
 
 // Sentinel for "no key seen yet": finite, so exp2(m - m_new) stays defined
 // when a part of the history is empty; masked scores are -inf.
 constexpr float kNoMax = -1e30f;
+
+// 16-byte load marked nontemporal: K/V cache rows are streamed once per
+// (query, KV head), and the streaming hint lifts HBM read throughput.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -43,6 +52,21 @@ __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
+}
+
+// Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), with
+// the gfx950 row-swap instructions instead of an LDS round trip.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int CTRL>

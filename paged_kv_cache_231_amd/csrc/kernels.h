@@ -63,6 +63,10 @@ hipError_t launch_rows_generic(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 // of its specialisations (the caller then uses the generic kernel).
 bool rows_fast_supported(const RowArgs &a, pkv_dtype dt);
 hipError_t launch_rows_fast(const RowArgs &a, pkv_dtype dt, hipStream_t st);
+// MFMA decode (F16/BF16, head_dim == value_dim in {64, 128, 256}).
+bool rows_mfma_supported(const RowArgs &a, pkv_dtype dt);
+uint64_t rows_mfma_blocks(const RowArgs &a);
+hipError_t launch_rows_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, pkv_dtype dt, hipStream_t st);
 bool tiles_supported(const TileArgs &a, pkv_dtype dt);
 hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st);

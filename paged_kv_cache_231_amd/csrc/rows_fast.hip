@@ -159,8 +159,8 @@ __global__ __launch_bounds__(256) void rows_fast_kernel(RowArgs a) {
         kk[c] = make_uint4(0, 0, 0, 0);
         vv[c] = make_uint4(0, 0, 0, 0);
         if (ok[c]) {
-          kk[c] = *reinterpret_cast<const uint4 *>(kp + uint64_t(slot) * a.k_tok);
-          vv[c] = *reinterpret_cast<const uint4 *>(vp + uint64_t(slot) * a.v_tok);
+          kk[c] = load_stream16(kp + uint64_t(slot) * a.k_tok);
+          vv[c] = load_stream16(vp + uint64_t(slot) * a.v_tok);
         }
       }
 #pragma unroll
