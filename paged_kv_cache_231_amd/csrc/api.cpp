@@ -271,38 +271,96 @@ void pkv_workspace_destroy(pkv_workspace *ws) {
 uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads, uint32_t kv_heads,
                             uint32_t value_dim) {
   if (!plan || plan->L.Q == 0 || plan->L.W == 0) return 1;
-  int cus = 256;
-  int dev = plan->device;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
   const PlanLayout &L = plan->L;
+  int cus = 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  // concurrent blocks of the decode kernel for this head size
+  RowArgs probe{};
+  probe.plan = view_of(plan);
+  probe.d = probe.dv = value_dim;
+  probe.hq = std::max(1u, q_heads);
+  probe.hkv = std::max(1u, kv_heads);
+  int per_cu = 2;
+  if (value_dim == 64 || value_dim == 128 || value_dim == 256)
+    per_cu = rows_mfma_blocks_per_cu(probe, PKV_BF16);
+  const double slots = double(cus) * std::max(1, per_cu);
+  const uint32_t groups = std::max(1u, kv_heads) *
+                          ((std::max(1u, q_heads) / std::max(1u, kv_heads) + 15u) / 16u);
+
+  // visible keys of every query attended one at a time (non-causal bound)
   const uint32_t *w = plan->host.data();
-  // pages of every query attended one at a time (non-causal upper bound)
-  std::vector<uint32_t> pages;
   const bool tiles = L.T > 0;
   const uint32_t nq = tiles ? L.R : L.Q;
-  pages.reserve(nq);
+  std::vector<uint32_t> len(nq);
   for (uint32_t r = 0; r < nq; ++r) {
     const uint32_t i = tiles ? w[L.rows + r] : r;
-    const uint32_t len = w[L.lens + w[L.qseq + i]];
-    pages.push_back(len / L.ps + (len % L.ps != 0));
+    len[r] = w[L.lens + w[L.qseq + i]];
   }
-  const uint64_t target = uint64_t(cus) * 8;              // blocks in flight to aim for
-  const uint32_t min_pages = std::max(1u, 256u / L.ps);    // >= 256 tokens per part
-  uint32_t smax = std::min<uint32_t>(PKV_MAX_SPLITS, L.W);
-  const uint64_t per_split = uint64_t(L.Q) * std::max(1u, q_heads) * (uint64_t(value_dim) + 1) * 4;
-  smax = uint32_t(std::min<uint64_t>(smax, std::max<uint64_t>(1, PKV_WORKSPACE_LIMIT_BYTES / per_split)));
-  uint32_t best = 1;
-  for (uint32_t s = 1; s <= smax; ++s) {
-    const uint32_t pp = L.W / s + (L.W % s != 0);
-    if (pp < min_pages) break;
-    uint64_t blocks = 0;
-    for (uint32_t pg : pages) blocks += std::min<uint32_t>(s, pg / pp + (pg % pp != 0));
-    blocks *= std::max(1u, kv_heads);
-    best = s;
-    if (blocks >= target) break;
+
+  // Makespan model, in units of "one token row of one KV head": blocks are
+  // dispatched in part-major order onto `slots` places and progress at the
+  // fair share of the machine's bandwidth, each at most kBoost times that
+  // share when the machine is not full; every block costs kOverhead extra;
+  // a split adds the merge (its reads and a launch).
+  // (one token row = 2 * value_dim half-precision elements; the machine
+  // streams ~1.2e4 rows per microsecond, a block's fixed cost is ~2 us at a
+  // full machine's fair share and a merge launch ~4 us)
+  const double kBoost = 2.0, kOverhead = 64.0, kMergeLaunch = 48000.0;
+  const double rate_full = 1.0;  // machine bandwidth, rows per unit time
+  const uint32_t cand[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 48, 64, 96, 128, 192, 256};
+  uint32_t best_s = 1;
+  double best_t = 0.0;
+  for (uint32_t s : cand) {
+    if (s > L.W || s > PKV_MAX_SPLITS) break;
+    const uint64_t per_split = uint64_t(L.Q) * std::max(1u, q_heads) * (uint64_t(value_dim) + 1) * 4;
+    if (s > 1 && uint64_t(s) * per_split > PKV_WORKSPACE_LIMIT_BYTES) break;
+    const uint64_t pp = L.W / s + (L.W % s != 0);
+    const uint64_t span = pp * L.ps;
+    // processor sharing with virtual time: every active block advances by
+    // the same amount of work per unit of virtual time
+    std::vector<double> heap;  // finish points in virtual time (min-heap)
+    double now = 0.0, vnow = 0.0;
+    uint64_t parts_total = 0;
+    auto rate = [&](size_t active) {
+      return std::min(kBoost / slots, rate_full / double(active));
+    };
+    auto advance_one = [&]() {  // finish the earliest block
+      std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+      const double v = heap.back();
+      now += (v - vnow) / rate(heap.size());
+      vnow = v;
+      heap.pop_back();
+    };
+    for (uint32_t part = 0; part < s; ++part) {
+      for (uint32_t r = 0; r < nq; ++r) {
+        const uint64_t lo = uint64_t(part) * span;
+        if (lo >= len[r]) continue;
+        const double work = double(std::min<uint64_t>(span, len[r] - lo)) + kOverhead;
+        ++parts_total;
+        for (uint32_t g = 0; g < groups; ++g) {
+          if (heap.size() >= size_t(slots)) advance_one();
+          heap.push_back(vnow + work);
+          std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+        }
+      }
+    }
+    while (!heap.empty()) advance_one();
+    double t = now;
+    if (s > 1) {
+      // merge: read and write every part's rows of every q head (f32, Dv+1
+      // words), in units of KV rows of (D + Dv) half-precision elements
+      const double merge_rows = double(parts_total) * std::max(1u, q_heads) *
+                                (double(value_dim) + 1.0) * 4.0 / (4.0 * value_dim);
+      t += merge_rows / rate_full + kMergeLaunch;
+    }
+    if (best_t == 0.0 || t < best_t * 0.98) {  // prefer fewer parts unless clearly faster
+      best_t = t;
+      best_s = s;
+    }
   }
-  return best;
+  return best_s;
 }
 
 pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, const void *k,

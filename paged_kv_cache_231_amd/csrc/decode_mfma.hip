@@ -269,8 +269,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
   const uint32_t c16 = lane & 15u, j = lane >> 4;
   const uint32_t grp = a.hq / a.hkv;
   const uint32_t hgk = (grp + kHeads - 1) / kHeads;
-  const uint32_t part = blockIdx.x % a.splits;
-  const uint32_t rest = blockIdx.x / a.splits;
+  // Part-major block order: the first parts of every query (full length)
+  // are dispatched before the later, partly filled ones.
+  const uint32_t per_part = a.n_queries * a.hkv * hgk;
+  const uint32_t part = blockIdx.x / per_part;
+  const uint32_t rest = blockIdx.x % per_part;
   const uint32_t hsel = rest % (a.hkv * hgk);
   const uint32_t qi = rest / (a.hkv * hgk);
   const uint32_t kvh = hsel / hgk, sub = hsel % hgk;
@@ -410,6 +413,27 @@ bool rows_mfma_supported(const RowArgs &a, pkv_dtype dt) {
   if (a.pdim != 0 || a.d != a.dv || (a.d != 64 && a.d != 128 && a.d != 256)) return false;
   if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v)) return false;
   return true;
+}
+
+int rows_mfma_blocks_per_cu(const RowArgs &a, pkv_dtype dt) {
+  const uint32_t ps = a.plan.ps;
+  const bool pu = (ps & (ps - 1)) == 0 && ps >= 16u;
+  int blocks = 0;
+  hipError_t e = hipErrorNotSupported;
+#define PKV_OCC(DT, D, PU)                                                                  \
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma_kernel<DT, D, PU>, \
+                                                   256, 0)
+  if (dt == PKV_BF16) {
+    if (a.d == 64) { if (pu) PKV_OCC(BF16, 64, true); else PKV_OCC(BF16, 64, false); }
+    if (a.d == 128) { if (pu) PKV_OCC(BF16, 128, true); else PKV_OCC(BF16, 128, false); }
+    if (a.d == 256) { if (pu) PKV_OCC(BF16, 256, true); else PKV_OCC(BF16, 256, false); }
+  } else {
+    if (a.d == 64) { if (pu) PKV_OCC(F16, 64, true); else PKV_OCC(F16, 64, false); }
+    if (a.d == 128) { if (pu) PKV_OCC(F16, 128, true); else PKV_OCC(F16, 128, false); }
+    if (a.d == 256) { if (pu) PKV_OCC(F16, 256, true); else PKV_OCC(F16, 256, false); }
+  }
+#undef PKV_OCC
+  return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 uint64_t rows_mfma_blocks(const RowArgs &a) {

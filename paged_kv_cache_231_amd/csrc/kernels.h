@@ -31,7 +31,7 @@ struct RowArgs {
   uint64_t k_page, k_tok;    // k: page stride, token stride
   uint64_t v_page, v_tok;
   uint64_t kp_page, kp_tok;
-  void *out;                 // [Q, hq, dv] in the input dtype (splits == 1)
+  void *out;                 // [Q, hq, dv] in the input dtype
   float *ws_o, *ws_lse;      // [Q, splits, hq, dv], [Q, splits, hq] (splits > 1)
 };
 
@@ -66,6 +66,7 @@ hipError_t launch_rows_fast(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 // MFMA decode (F16/BF16, head_dim == value_dim in {64, 128, 256}).
 bool rows_mfma_supported(const RowArgs &a, pkv_dtype dt);
 uint64_t rows_mfma_blocks(const RowArgs &a);
+int rows_mfma_blocks_per_cu(const RowArgs &a, pkv_dtype dt);
 hipError_t launch_rows_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, pkv_dtype dt, hipStream_t st);
 bool tiles_supported(const TileArgs &a, pkv_dtype dt);

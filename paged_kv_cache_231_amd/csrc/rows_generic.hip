@@ -117,13 +117,15 @@ __global__ __launch_bounds__(64) void rows_generic_kernel(RowArgs a) {
 
 // Merge of the non-empty parts of one (query, head):
 //   M = max_j lse_j,  w_j = 2^(lse_j - M),  out = sum_j w_j o_j / sum_j w_j.
-// Four waves share the parts of one (query, head); each lane owns value
-// elements lane, lane + 64, ...
+// One block per (query, head).  The part statistics are read in parallel
+// (one part per thread) and reduced through LDS; each thread then owns value
+// elements d = tid, tid + 256, ... and sums over the parts with independent,
+// unrolled loads so that many are in flight at once.
 template <class DT>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   using T = typename DT::T;
-  __shared__ float part_sum[4][1024];
-  __shared__ float wsum_w[4];
+  __shared__ float s_w[256];  // splits <= 256
+  __shared__ float s_red[8];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
   const uint32_t h = blockIdx.x % a.hq;
   const uint32_t qi = blockIdx.x / a.hq;
@@ -133,37 +135,38 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const uint32_t used_pages = ceil_div_u(n, a.plan.ps);
   uint32_t parts = ceil_div_u(used_pages, a.pages_per_split);
   if (parts > a.splits) parts = a.splits;
-
   const uint64_t base = uint64_t(i) * a.splits;
-  float M = kNoMax;
-  for (uint32_t j = 0; j < parts; ++j) M = fmaxf(M, a.ws_lse[(base + j) * a.hq + h]);
-  float wsum = 0.f;
-  float acc[kMaxPerLane];
-#pragma unroll
-  for (int e = 0; e < kMaxPerLane; ++e) acc[e] = 0.f;
-  for (uint32_t j = wv; j < parts; j += 4) {
-    const uint64_t row = (base + j) * a.hq + h;
-    const float w = fast_exp2(a.ws_lse[row] - M);
-    wsum += w;
-    const float *o = a.ws_o + row * a.dv;
-#pragma unroll
-    for (int e = 0; e < kMaxPerLane; ++e) {
-      const uint32_t d = lane + 64u * e;
-      if (d < a.dv) acc[e] += w * o[d];
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < kMaxPerLane; ++e) {
-    const uint32_t d = lane + 64u * e;
-    if (d < a.dv) part_sum[wv][d] = acc[e];
-  }
-  if (lane == 0) wsum_w[wv] = wsum;
+
+  const float lse = tid < parts ? a.ws_lse[(base + tid) * a.hq + h] : -INFINITY;
+  float mx = wave_max(fmaxf(lse, kNoMax));
+  if (lane == 0) s_red[wv] = mx;
   __syncthreads();
-  const float total = wsum_w[0] + wsum_w[1] + wsum_w[2] + wsum_w[3];
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float w = tid < parts ? fast_exp2(lse - mx) : 0.f;
+  s_w[tid] = w;
+  const float ws = wave_sum(w);
+  if (lane == 0) s_red[4 + wv] = ws;
+  __syncthreads();
+  const float total = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
   const float inv = total > 0.f ? 1.f / total : 0.f;
+
   T *out = static_cast<T *>(a.out) + (uint64_t(i) * a.hq + h) * a.dv;
-  for (uint32_t d = tid; d < a.dv; d += 256)
-    out[d] = DT::from_f((part_sum[0][d] + part_sum[1][d] + part_sum[2][d] + part_sum[3][d]) * inv);
+  const uint64_t stride = uint64_t(a.hq) * a.dv;  // between parts
+  const float *o = a.ws_o + (base * a.hq + h) * a.dv;
+  for (uint32_t d = tid; d < a.dv; d += 256) {
+    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+    uint32_t p = 0;
+    for (; p + 4 <= parts; p += 4) {
+      const float o0 = o[(p + 0) * stride + d], o1 = o[(p + 1) * stride + d];
+      const float o2 = o[(p + 2) * stride + d], o3 = o[(p + 3) * stride + d];
+      acc0 = fmaf(s_w[p + 0], o0, acc0);
+      acc1 = fmaf(s_w[p + 1], o1, acc1);
+      acc2 = fmaf(s_w[p + 2], o2, acc2);
+      acc3 = fmaf(s_w[p + 3], o3, acc3);
+    }
+    for (; p < parts; ++p) acc0 = fmaf(s_w[p], o[p * stride + d], acc0);
+    out[d] = DT::from_f(((acc0 + acc1) + (acc2 + acc3)) * inv);
+  }
 }
 
 }  // namespace
