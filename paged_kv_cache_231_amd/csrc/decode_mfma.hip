@@ -23,57 +23,11 @@
 // Only the C layout fixes meaning; the K-slot order just has to agree
 // between A and B, and it does because both are filled with one mapping.
 
-#include "device_common.h"
+#include "mfma_common.h"
 
 namespace pkv {
 
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <class DT>
-struct Mfma;
-
-template <>
-struct Mfma<BF16> {
-  // S^T += K(16 tokens x 32 d) . Q^T(32 d x 16 heads)
-  static __device__ __forceinline__ f32x4_t qk(const uint4 &a, const uint4 &b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  }
-  // O^T += V^T(16 d x 16 tokens) . P^T(16 tokens x 16 heads)
-  static __device__ __forceinline__ f32x4_t pv(const uint2 &a, const uint2 &b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return BF16::pack2(lo, hi); }
-  static __device__ __forceinline__ float to_f(uint16_t x) { return BF16::to_f(x); }
-  static __device__ __forceinline__ uint16_t from_f(float x) { return BF16::from_f(x); }
-};
-
-template <>
-struct Mfma<F16> {
-  static __device__ __forceinline__ f32x4_t qk(const uint4 &a, const uint4 &b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4_t pv(const uint2 &a, const uint2 &b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
-                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    const _Float16 a = _Float16(lo), b = _Float16(hi);
-    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
-  }
-  static __device__ __forceinline__ float to_f(uint16_t x) { return float(__builtin_bit_cast(_Float16, x)); }
-  static __device__ __forceinline__ uint16_t from_f(float x) {
-    return __builtin_bit_cast(uint16_t, _Float16(x));
-  }
-};
 
 constexpr int kWaves = 4;
 constexpr int kTile = 16;   // tokens per wave iteration
@@ -240,19 +194,11 @@ __device__ __forceinline__ void attend_tile(WaveState<D> &st, const TileRegs<D> 
   pb.x = M::pack2(p[0], p[1]);
   pb.y = M::pack2(p[2], p[3]);
 
-  // O^T += V^T . P^T : A = V^T[d = 16b + c16][tokens 4j+0..3] from LDS
+  // O^T += V^T . P^T : A = V^T[d = 16b + c16][tokens 4j+0..3], one
+  // transposed LDS read per block of 16 value dims
+  const unsigned char *vrow = vtile + (4 * j + (c16 >> 2)) * L::kRow + 8 * (c16 & 3);
 #pragma unroll
-  for (int b = 0; b < DB; ++b) {
-    const unsigned char *col = vtile + 2 * (16 * b + c16) + 4 * j * L::kRow;
-    const uint32_t v0 = *reinterpret_cast<const uint16_t *>(col);
-    const uint32_t v1 = *reinterpret_cast<const uint16_t *>(col + L::kRow);
-    const uint32_t v2 = *reinterpret_cast<const uint16_t *>(col + 2 * L::kRow);
-    const uint32_t v3 = *reinterpret_cast<const uint16_t *>(col + 3 * L::kRow);
-    uint2 va;
-    va.x = v0 | (v1 << 16);
-    va.y = v2 | (v3 << 16);
-    st.o[b] = M::pv(va, pb, st.o[b]);
-  }
+  for (int b = 0; b < DB; ++b) st.o[b] = M::pv(lds_read_tr16(vrow + 32 * b), pb, st.o[b]);
 }
 
 template <class DT, int D, bool PU>
