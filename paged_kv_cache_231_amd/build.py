@@ -39,6 +39,9 @@ def _flags():
         # packed fp32 instructions stay off (they are emitted from plain
         # float code otherwise)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in ordinary VGPRs: the online softmax rescales
+        # them with VALU ops, which would otherwise copy through AGPRs
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function",
     ]
 

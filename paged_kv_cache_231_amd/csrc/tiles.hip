@@ -1,12 +1,354 @@
-// Chunked-prefill tile kernel (MFMA).  Not built yet: every query is served
-// by the per-query kernels until this kernel lands.
+// Chunked-prefill kernel on MFMA: causal attention at absolute positions for
+// runs of consecutive queries of one sequence ("tiles" of the plan).
+//
+// Computes the attention of the ruDNN 0.1.7 `paged_attention` page
+// (`DevicePlan::attention` doc: packed queries, paged K/V, `causal` by the
+// absolute positions of the plan, prefill chunks included).  A tile's queries
+// are consecutive positions p0, p0+1, ... of one sequence, so they share the
+// key rows 0..p_last, and every (query, q head) of one KV head forms a dense
+// contraction with those rows.
+//
+// A block owns 128 q-rows (a q-row is one (query, q head) pair; with G q
+// heads per KV head that is 128/G queries x G heads) of one tile and one KV
+// head; each of its four waves owns 32 q-rows as two MFMA N-tiles.  Keys are
+// walked in tiles of 32 rows.  K and V rows travel HBM -> LDS directly
+// (gfx950 global_load_lds, no registers on the way) into a ring of four
+// stages, three tiles ahead of the tile being computed, so the load latency
+// hides behind the MFMA work.  Each wave computes S^T = K . Q^T (tokens on
+// the M side), applies the absolute-position mask and an online softmax in
+// base 2, and accumulates O^T += V^T . P^T, with V^T read by transposed LDS
+// loads.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled by
+// row, which keeps both read patterns at most two-way banked.  The block
+// table of the sequence is cached in LDS.  Blocks that share a (tile, KV
+// head) are numbered so they land on one XCD and share its L2.
 
-#include "device_common.h"
+#include "mfma_common.h"
 
 namespace pkv {
 
-bool tiles_supported(const TileArgs &, pkv_dtype) { return false; }
+namespace {
 
-hipError_t launch_tiles(const TileArgs &, pkv_dtype, hipStream_t) { return hipErrorNotSupported; }
+constexpr int kPW = 4;             // waves per block
+constexpr int kRowsPerBlock = 128; // q-rows per block (32 per wave)
+constexpr int kTT = 32;            // key rows per tile
+constexpr int kStages = 4;         // LDS ring stages (3 tiles in flight)
+constexpr int kTableCache = 1024;  // block-table entries cached in LDS
+constexpr float kSlack = 8.0f;     // lazy-rescale threshold (log2 units)
+
+template <int D>
+struct PLds {
+  static constexpr int kRowB = D * 2;              // bytes per row (unpadded)
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int kTile = kTT * kRowB;        // one K or V tile
+  static constexpr int kStage = 2 * kTile;         // K then V
+  static constexpr int kBytes = kStages * kStage;
+  static constexpr int RPW = 1024 / kRowB;         // rows per wave load (64 lanes x 16 B)
+  static constexpr int NI = kTT / (RPW * kPW);     // loads per wave per tensor per tile
+  // chunk c of row r sits in slot c ^ swz(r): rows sharing a 256-byte bank
+  // line get different XOR keys
+  static __device__ __forceinline__ uint32_t swz(uint32_t r) {
+    return D == 64 ? (r >> 1) & 7u : r & 15u;
+  }
+};
+
+// Compiler-level memory barriers around the raw hardware barrier: LDS loads
+// and stores may not move across, and no wait for outstanding global loads
+// is implied (the ring waits for those explicitly).
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte-per-lane load from global memory straight into LDS: lane l's
+// 16 bytes land at LDS byte address lds_base + 16 * l.  Written as inline
+// assembly so the compiler's wait insertion does not treat every later LDS
+// read as dependent on it: the ring's explicit vmcnt waits and barriers order
+// these loads against the reads.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(src)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char *)(p)));
+}
+
+// Makes the compiler finish the loads of x here (it cannot see the DMA
+// loads, so a wait it placed later for x would drain them too).
+__device__ __forceinline__ void settle(const uint4 &x) {
+  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <class DT, int D>
+__global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub,
+                                                      uint32_t n_blocks, uint32_t per_xcd) {
+  using M = Mfma<DT>;
+  using L = PLds<D>;
+  using T = typename DT::T;
+  constexpr int KS = D / 32, DB = D / 16;
+  constexpr int kLoadsPerTile = 2 * L::NI;  // per thread: K and V
+  __shared__ __align__(1024) unsigned char lds[L::kBytes];
+  __shared__ uint32_t tcache[kTableCache];
+
+  // blocks sharing a (tile, KV head) get consecutive logical numbers on the
+  // XCD that blockIdx.x % 8 selects
+  const uint32_t logical = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
+  if (logical >= n_blocks) return;
+  const uint32_t sub = logical % n_sub;
+  const uint32_t kvh = (logical / n_sub) % a.hkv;
+  const uint32_t tile = logical / n_sub / a.hkv;
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t c16 = lane & 15u, j = lane >> 4;
+  const PlanView &pv = a.plan;
+  const uint32_t first = a.tiles[2 * tile], count = a.tiles[2 * tile + 1];
+  const uint32_t grp = a.hq / a.hkv;
+  const uint32_t qb_n = kRowsPerBlock / grp;  // queries per block
+  const uint32_t q_lo = sub * qb_n;
+  if (q_lo >= count) return;
+  const uint32_t q_hi = q_lo + qb_n < count ? q_lo + qb_n : count;
+  const uint32_t seq = pv.words[pv.qseq + first];
+  const uint32_t p0 = pv.words[pv.qpos + first];
+  const uint32_t len = pv.words[pv.lens + seq];
+  uint64_t k_end64 = a.causal ? uint64_t(p0) + q_hi : uint64_t(len);
+  const uint64_t reach = uint64_t(pv.W) * pv.ps;
+  if (k_end64 > reach) k_end64 = reach;
+  const uint32_t k_end = uint32_t(k_end64);
+  const uint32_t ps = pv.ps;
+  const bool pow2 = (ps & (ps - 1)) == 0;
+  const uint32_t ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 0u;
+
+  // block table of the sequence, first kTableCache entries, into LDS
+  const uint32_t *table = pv.words + pv.table + uint64_t(seq) * pv.W;
+  const uint32_t n_lp = (k_end + ps - 1) / ps;
+  for (uint32_t e = tid; e < n_lp && e < uint32_t(kTableCache); e += 256) {
+    const uint32_t pg = table[e];
+    tcache[e] = pg < pv.N ? pg : 0u;  // never read outside the pool
+  }
+
+  // this wave's q-rows: N-tile nt, column c16 -> q-row 32*wv + 16*nt + c16
+  uint4 qb[2][KS];
+  uint32_t pos[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint32_t r = 32u * wv + 16u * nt + c16;
+    const uint32_t qq = r / grp, h = r % grp;
+    row_ok[nt] = r < qb_n * grp && q_lo + qq < q_hi;
+    pos[nt] = p0 + q_lo + qq;
+    const T *qrow = static_cast<const T *>(a.q) +
+                    (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qb[nt][ks] = row_ok[nt] ? *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j))
+                              : make_uint4(0, 0, 0, 0);
+  }
+  // smallest position among the block's queries: key tiles wholly at or
+  // below it need no causal mask
+  const uint32_t pos_min = p0 + q_lo;
+
+  f32x4_t o[2][DB];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[nt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {kNoMax, kNoMax}, lsum[2] = {0.f, 0.f};
+  const float sl2 = a.scale_log2;
+  const T *kbase = static_cast<const T *>(a.k) + uint64_t(kvh) * D;
+  const T *vbase = static_cast<const T *>(a.v) + uint64_t(kvh) * D;
+  __syncthreads();  // table cache ready (Q loads may still be in flight: fine)
+
+  // DMA of key tile kt into its ring stage: wave wv, load n covers rows
+  // RPW*(NI*wv + n) .. +RPW-1; lane -> row r0 + lane / CPR, slot lane % CPR,
+  // which holds chunk slot ^ swz(row) of the cache row.  Rows past the end
+  // read row 0 of page 0 (inside the pool) and are zeroed before use.
+  auto issue = [&](uint32_t kt) {
+    unsigned char *stage = lds + (kt % kStages) * L::kStage;
+#pragma unroll
+    for (int n = 0; n < L::NI; ++n) {
+      const uint32_t r0 = L::RPW * (L::NI * wv + n);
+      const uint32_t r = r0 + lane / L::CPR;
+      const uint32_t tok = kt * kTT + r;
+      const bool ok = tok < k_end;
+      const uint32_t lp = ok ? (pow2 ? tok >> ps_shift : tok / ps) : 0u;
+      const uint32_t slot = ok ? tok - lp * ps : 0u;
+      const uint32_t page = ok ? (lp < uint32_t(kTableCache) ? tcache[lp]
+                                                             : (table[lp] < pv.N ? table[lp] : 0u))
+                               : 0u;
+      const uint32_t chunk = (lane % L::CPR) ^ L::swz(r);
+      const uint32_t ko = page * uint32_t(a.k_page) + slot * uint32_t(a.k_tok) + 8u * chunk;
+      const uint32_t vo = page * uint32_t(a.v_page) + slot * uint32_t(a.v_tok) + 8u * chunk;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + r0 * L::kRowB));
+      dma16(kbase + ko, dst);
+      dma16(vbase + vo, dst + uint32_t(L::kTile));
+    }
+  };
+
+  const uint32_t n_tiles = (k_end + kTT - 1) / kTT;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) settle(qb[nt][ks]);
+  for (uint32_t kt = 0; kt < n_tiles && kt < uint32_t(kStages - 1); ++kt) issue(kt);
+
+  for (uint32_t kt = 0; kt < n_tiles; ++kt) {
+    const uint32_t t0 = kt * kTT;
+    // this thread's loads of tile kt are done once at most the loads of the
+    // tiles issued after it are outstanding
+    const uint32_t ahead = n_tiles - 1 - kt;
+    if (ahead >= 2) wait_vm<2 * kLoadsPerTile>();
+    else if (ahead == 1) wait_vm<kLoadsPerTile>();
+    else wait_vm<0>();
+    unsigned char *kt_lds = lds + (kt % kStages) * L::kStage;
+    unsigned char *vt_lds = kt_lds + L::kTile;
+    if (t0 + kTT > k_end) {
+      // last tile: rows past the end hold whatever row 0 of page 0 holds;
+      // zero their V (a NaN there must not reach the product)
+      block_sync_lds();
+      for (uint32_t e = tid; e < uint32_t(kTT * L::CPR); e += 256) {
+        const uint32_t r = e / L::CPR;
+        if (t0 + r >= k_end)
+          *reinterpret_cast<uint4 *>(vt_lds + r * L::kRowB + 16u * (e % L::CPR)) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    block_sync_lds();  // tile kt visible to all waves; stage of kt-1 free
+
+    // scores for both 16-row halves and both N-tiles
+    f32x4_t s[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint32_t r = 16u * mb + c16;
+      uint4 ka[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[ks] = *reinterpret_cast<const uint4 *>(kt_lds + r * L::kRowB +
+                                                  16u * ((4u * ks + j) ^ L::swz(r)));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = M::qk(ka[ks], qb[nt][ks], acc);
+        s[mb][nt] = acc;
+      }
+    }
+    const bool full = a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
+                               : (t0 + kTT <= k_end);
+    uint2 pb[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float x[2][4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t tok = t0 + 16u * mb + 4u * j + e;
+          const bool vis = full || (tok < k_end && (!a.causal || tok <= pos[nt]));
+          x[mb][e] = vis ? s[mb][nt][e] * sl2 : -INFINITY;
+          mt = fmaxf(mt, x[mb][e]);
+        }
+      mt = rows4_max(mt);
+      // Lazy rescaling: the reference max only moves when a tile's max
+      // exceeds it by more than kSlack (base 2), so probabilities stay
+      // below 2^kSlack and most tiles skip rescaling O.  The result is the
+      // same softmax: numerator and denominator share the reference.
+      const float m_new = mt > m[nt] + kSlack ? mt : m[nt];
+      const float alpha = fast_exp2(m[nt] - m_new);
+      m[nt] = m_new;
+      float p_sum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = fast_exp2(x[mb][e] - m_new);
+          p_sum += p[e];
+        }
+        pb[mb][nt].x = M::pack2(p[0], p[1]);
+        pb[mb][nt].y = M::pack2(p[2], p[3]);
+      }
+      lsum[nt] = lsum[nt] * alpha + p_sum;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[nt][b] *= alpha;
+      }
+    }
+
+    // O^T += V^T . P^T over both halves: lane (j, c16) reads row
+    // 16mb + 4j + (c16 >> 2), value columns 16b + 4(c16 & 3) .. +3
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint32_t r = 16u * mb + 4u * j + (c16 >> 2);
+      const unsigned char *vrow = vt_lds + r * L::kRowB + 8u * (c16 & 1u);
+      const uint32_t key = L::swz(r);
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const uint32_t chunk = 2u * b + ((c16 & 3u) >> 1);
+        const uint2 va = lds_read_tr16(vrow + 16u * (chunk ^ key));
+        o[0][b] = M::pv(va, pb[mb][0], o[0][b]);
+        o[1][b] = M::pv(va, pb[mb][1], o[1][b]);
+      }
+    }
+    // refill the stage of tile kt-1 (every wave passed this iteration's
+    // barrier, so none still reads it)
+    if (kt + kStages - 1 < n_tiles) issue(kt + kStages - 1);
+  }
+
+  // normalise and write: lane holds O^T[d = 16b + 4j + e][q-row c16]
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float l_tot = rows4_sum(lsum[nt]);
+    if (!row_ok[nt]) continue;
+    const uint32_t r = 32u * wv + 16u * nt + c16;
+    const uint32_t qq = r / grp, h = r % grp;
+    T *out = static_cast<T *>(a.out) + (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + h) * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      uint2 w;
+      w.x = M::pack2(o[nt][b][0] * inv, o[nt][b][1] * inv);
+      w.y = M::pack2(o[nt][b][2] * inv, o[nt][b][3] * inv);
+      *reinterpret_cast<uint2 *>(out + 16 * b + 4 * j) = w;
+    }
+  }
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+bool tiles_supported(const TileArgs &a, pkv_dtype dt) {
+  if (dt != PKV_F16 && dt != PKV_BF16) return false;
+  if (a.d != a.dv || (a.d != 64 && a.d != 128)) return false;
+  if (a.hq / a.hkv > uint32_t(kRowsPerBlock)) return false;
+  return aligned16(a.q) && aligned16(a.k) && aligned16(a.v) && aligned16(a.out);
+}
+
+hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st) {
+  const uint32_t grp = a.hq / a.hkv;
+  const uint32_t qb_n = kRowsPerBlock / grp;
+  const uint32_t n_sub = (PKV_TILE_MAX + qb_n - 1) / qb_n;
+  const uint64_t n_blocks = uint64_t(a.n_tiles) * a.hkv * n_sub;
+  if (n_blocks == 0) return hipSuccess;
+  const uint32_t per_xcd = uint32_t((n_blocks + 7) / 8);
+  const dim3 grid(8u * per_xcd);
+  const uint32_t nb = uint32_t(n_blocks);
+  if (dt == PKV_BF16) {
+    if (a.d == 64) hipLaunchKernelGGL((prefill_kernel<BF16, 64>), grid, dim3(256), 0, st, a, n_sub, nb, per_xcd);
+    else hipLaunchKernelGGL((prefill_kernel<BF16, 128>), grid, dim3(256), 0, st, a, n_sub, nb, per_xcd);
+  } else {
+    if (a.d == 64) hipLaunchKernelGGL((prefill_kernel<F16, 64>), grid, dim3(256), 0, st, a, n_sub, nb, per_xcd);
+    else hipLaunchKernelGGL((prefill_kernel<F16, 128>), grid, dim3(256), 0, st, a, n_sub, nb, per_xcd);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace pkv

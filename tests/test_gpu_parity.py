@@ -229,3 +229,37 @@ def test_full_size_workloads_sampled(n):
     sel = np.stack([got[i, h] for i, h in pairs])
     assert_close(sel, want, wl.dtype, f"config {n} (splits={splits})")
     assert np.isfinite(got).all()
+
+
+def _prefill_wl(dtype, hq, hkv, d, ps, chunks, dec_lens, seed, causal=True):
+    """Chunks (prior, length) of consecutive queries plus decode rows."""
+    lens = [p + c for p, c in chunks] + list(dec_lens)
+    queries = []
+    for s, (p, c) in enumerate(chunks):
+        queries += [(s, p + j) for j in range(c)]
+    queries += [(len(chunks) + j, L - 1) for j, L in enumerate(dec_lens)]
+    return build_attention("t", seed, dtype, lens, queries, hq, hkv, d, d, ps, causal=causal,
+                           poison=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("g", [1, 3, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_tiles_gqa(dtype, g, d):
+    """Tiles of the chunked-prefill kernel: a 150-query chunk (tiles of 128
+    and 22 queries) after 77 cached tokens, a 20-query chunk from position 0,
+    and two decode rows."""
+    hkv = 2
+    wl = _prefill_wl(dtype, hkv * g, hkv, d, 16, [(77, 150), (0, 20)], [33, 300], seed=900 + g + d)
+    assert_close(run(wl), expected(wl), dtype, f"prefill g={g} d={d}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("ps", [1, 5, 64])
+def test_prefill_tiles_page_sizes(causal, ps):
+    """Odd page sizes; with ps=1 the 1200-token prior needs more block-table
+    entries than the kernel caches in LDS."""
+    wl = _prefill_wl(torch.bfloat16, 8, 2, 128, ps, [(1200, 40), (3, 129)], [7], seed=950 + ps,
+                     causal=causal)
+    assert_close(run(wl), expected(wl), torch.bfloat16, f"prefill ps={ps}")
+    assert_close(run(wl, splits=3), expected(wl), torch.bfloat16, f"prefill ps={ps} split")
