@@ -94,7 +94,10 @@ pkv_status hip_fail(hipError_t e) {
 // Launches the row kernel (and the merge when split) over `qlist`.
 pkv_status run_rows(RowArgs ra, pkv_dtype dt, const pkv_workspace *ws, hipStream_t st) {
   hipError_t e;
-  if (rows_mfma_supported(ra, dt)) {
+  if (ra.pdim != 0 && mla_mfma_supported(ra, dt)) {
+    if (mla_mfma_blocks(ra) > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+    e = launch_mla_mfma(ra, dt, st);
+  } else if (rows_mfma_supported(ra, dt)) {
     if (rows_mfma_blocks(ra) * 256u > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
     e = launch_rows_mfma(ra, dt, st);
   } else if (rows_fast_supported(ra, dt)) {

@@ -69,6 +69,11 @@ uint64_t rows_mfma_blocks(const RowArgs &a);
 int rows_mfma_blocks_per_cu(const RowArgs &a, pkv_dtype dt);
 hipError_t launch_rows_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, pkv_dtype dt, hipStream_t st);
+// MLA on MFMA (F16/BF16, rank 512, position dim 64): one block per
+// (query, 128-head group, split part).
+bool mla_mfma_supported(const RowArgs &a, pkv_dtype dt);
+uint64_t mla_mfma_blocks(const RowArgs &a);
+hipError_t launch_mla_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 bool tiles_supported(const TileArgs &a, pkv_dtype dt);
 hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st);
 

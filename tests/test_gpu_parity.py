@@ -85,6 +85,21 @@ def test_mla_small(dtype):
     assert_close(run(wl, splits=5), expected(wl), dtype, "mla split")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("h,ps", [(128, 64), (16, 16), (40, 5), (256, 1)])
+def test_mla_latent512(dtype, h, ps):
+    """The MFMA MLA kernel's shape (rank 512, position dim 64): ragged head
+    groups, page sizes 1/5/16/64, lengths that end inside a key tile, with
+    and without splits."""
+    lens = [1, 31, 32, 33, 300, 1000]
+    queries = decode_queries(lens) + [(4, 17), (5, 500)]
+    wl = build_mla("mla512", 29 + h + ps, dtype, lens, queries, h, 512, 64, ps, poison=True)
+    want = expected(wl)
+    assert_close(run(wl), want, dtype, "mla512")
+    assert_close(run(wl, splits=3), want, dtype, "mla512 split 3")
+    assert_close(run(wl, splits=16), want, dtype, "mla512 split 16")
+
+
 def test_page_permutation_is_bitwise_invariant():
     """Moving pages in the pool (same logical content) gives identical bits."""
     wl = _decode_wl(torch.bfloat16, 16, 2, 128, 128, 16, [300, 77, 1000], seed=41, pool_extra=0)
