@@ -46,28 +46,9 @@ def _flags():
     ]
 
 
-# Per-source changes to the common flags.  The MLA kernel keeps one wave
-# per SIMD with a 512 x 16 f32 output tile per wave: its accumulators live in
-# AGPRs (rescaled rarely), which leaves the VGPRs for operand prefetch.
-FLAG_DROP = {
-    "mla_mfma.hip": ["-amdgpu-mfma-vgpr-form"],
-}
-
-
-def _flags_for(src: str):
-    drop = FLAG_DROP.get(os.path.basename(src), [])
-    out = []
-    for f in _flags():
-        if f in drop:
-            out.pop()  # the preceding "-mllvm"
-            continue
-        out.append(f)
-    return out
-
-
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *_flags_for(src), "-c", src, "-o", obj]
+    cmd = [hipcc(), *_flags(), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -6,13 +6,13 @@
 // output are dense contractions over the latent:
 //   S^T[tokens x heads] = latent . q_abs^T + k_pos . q_pos^T   (576-deep)
 //   O^T[rank x heads]  += latent^T . P^T                        (token-deep)
-// A block owns one (query, split part) and up to 128 heads; each of its
-// eight waves owns 16 heads (one MFMA N-tile) with its 512 x 16 output tile
-// in registers, so every latent row read from HBM serves all heads.  Latent
-// and k_pos rows travel HBM -> LDS directly into a four-stage ring (three
-// 16-token tiles ahead), stored with XOR-swizzled 16-byte chunks; the
-// latent is read from LDS as the A operand of q.k and, transposed, of the
-// value product.  The online softmax is kept in base 2 with lazy
+// A block owns one (query, split part, 64-head group); its four waves (one
+// per SIMD) own 16 heads each, with the 512 x 16 f32 output tile in VGPRs
+// and the loop-invariant query operands in AGPRs (MFMA reads them there).
+// Latent and k_pos rows travel HBM -> LDS directly into a four-stage ring
+// (three 32-token tiles ahead); the latent is read from LDS as the A operand
+// of q.k and, transposed, as the A operand of the value product (16x16x32
+// with 32 tokens per step).  The online softmax is kept in base 2 with lazy
 // rescaling.  Split parts write f32 partials that the merge kernel combines.
 
 #include "mfma_common.h"
@@ -22,12 +22,20 @@ namespace pkv {
 namespace {
 
 constexpr int kWaves = 4;          // one wave per SIMD
-constexpr int kNT = 1;             // 16-head MFMA N-tiles per wave
-constexpr int kHeadsPerBlock = kWaves * kNT * 16;
+constexpr int kHeadsPerBlock = kWaves * 16;
 constexpr int kTT = 32;            // tokens per tile (two 16-row M-tiles)
 constexpr int kStages = 4;         // LDS ring stages
 constexpr int kTableCache = 1024;  // block-table entries cached in LDS
 constexpr float kSlack = 8.0f;     // lazy-rescale threshold (log2 units)
+
+// LDS layout of one ring stage: 32 latent rows of R bf16/f16 (row stride 2R
+// bytes), then 32 position rows of P.  Within each 256-byte segment of a
+// latent row, 16-byte chunk c of row r sits in slot c ^ (r & 15): the q.k
+// operand reads (one row per lane, eight lanes per LDS cycle) then fall into
+// distinct banks.  The transposed value reads (32 lanes per cycle, four
+// lanes per row) take their rows in an order that puts the eight rows of a
+// cycle into distinct 32-byte slot pairs (see pv_row below).  Position rows
+// (128 bytes) keep chunk c of row r in slot c ^ ((r >> 1) & 7).
 
 template <int R, int P>
 struct MLds {
@@ -40,8 +48,6 @@ struct MLds {
   static constexpr int kLatCPR = R / 8;            // 16-byte chunks per latent row
   static constexpr int kPosCPR = P / 8;            // per position row
   static constexpr int kLatPerWave = kTT / kWaves;  // latent rows each wave loads
-  // chunk c of latent row r sits in slot c ^ (r & 15) (same 256-byte line);
-  // chunk c of position row r in slot c ^ ((r >> 1) & 7)
   static __device__ __forceinline__ uint32_t lat_slot(uint32_t c, uint32_t r) { return c ^ (r & 15u); }
   static __device__ __forceinline__ uint32_t pos_slot(uint32_t c, uint32_t r) { return c ^ ((r >> 1) & 7u); }
 };
@@ -52,11 +58,19 @@ __device__ __forceinline__ void block_sync_lds() {
 
 // 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane
 // (inline assembly: the compiler's wait insertion would otherwise drain the
-// ring before every LDS read; the ring's explicit waits order it).
+// ring before every LDS read; the ring's explicit waits order it).  The first
+// form takes a per-lane address, the second a uniform base plus a per-lane
+// 32-bit byte offset.
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds_base), "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(base)
                : "memory", "m0");
 }
 
@@ -65,8 +79,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
       (__attribute__((address_space(3))) const char *)(p)));
 }
 
-__device__ __forceinline__ void settle(const uint4 &x) {
-  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+// Keep a loop-invariant MFMA operand in AGPRs (the MFMA reads it there).
+__device__ __forceinline__ void to_agpr(uint4 &x) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+a"(v));
+  x = __builtin_bit_cast(uint4, v);
 }
 
 template <int N>
@@ -129,47 +147,49 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
   };
   fill_window();
 
-  // this wave's heads: N-tile nt, column c16 -> head h0 + 16 nt + c16
-  const uint32_t h0 = hgi * kHeadsPerBlock + wv * (kNT * 16u);
-  uint4 qa[kNT][KS], qp[kNT][KP];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    // columns of heads past hq compute on head 0's query and are not stored
-    const uint32_t h = h0 + 16u * nt + c16;
+  // this wave's heads: column c16 -> head h0 + c16; columns of heads past hq
+  // compute on head 0's query and are not stored
+  const uint32_t h0 = hgi * kHeadsPerBlock + wv * 16u;
+  uint4 qa[KS], qp[KP];
+  {
+    const uint32_t h = h0 + c16;
     const uint64_t row = uint64_t(i) * a.hq + (h < a.hq ? h : 0u);
     const T *qrow = static_cast<const T *>(a.q) + row * R;
     const T *prow = static_cast<const T *>(a.qp) + row * P;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qa[nt][ks] = *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j));
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j));
 #pragma unroll
-    for (int ks = 0; ks < KP; ++ks) qp[nt][ks] = *reinterpret_cast<const uint4 *>(prow + 8 * (4 * ks + j));
+    for (int ks = 0; ks < KP; ++ks) qp[ks] = *reinterpret_cast<const uint4 *>(prow + 8 * (4 * ks + j));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) to_agpr(qa[ks]);
+#pragma unroll
+    for (int ks = 0; ks < KP; ++ks) to_agpr(qp[ks]);
   }
-  f32x4_t o[kNT][DB];
+  f32x4_t o[DB];
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-    for (int b = 0; b < DB; ++b) o[nt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[kNT], lsum[kNT];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    m[nt] = kNoMax;
-    lsum[nt] = 0.f;
-  }
+  for (int b = 0; b < DB; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNoMax, lsum = 0.f;
   const float sl2 = a.scale_log2;
   const T *lat = static_cast<const T *>(a.k);
   const T *kpos = static_cast<const T *>(a.kp);
   __syncthreads();  // table cache ready
 
   // DMA of tile kt: wave wv loads latent rows 8wv .. 8wv+7 (one whole row
-  // per instruction) and position rows 8wv .. 8wv+7 (one instruction, lane
-  // l row 8wv + l/8).  Lane l locates row 8wv + l/8; the latent loads take
-  // the page and slot of lanes 0, 8, .., 56.  Rows past the end read row 0
-  // of page 0; their latent is zeroed before use.
+  // per instruction: uniform row base, per-lane chunk offset) and position
+  // rows 8wv .. 8wv+7 (one instruction, lane l row 8wv + l/8).  Lane l
+  // locates row 8wv + l/8; the latent loads take the page and slot of lanes
+  // 0, 8, .., 56.  Rows past the end read row 0 of page 0; their latent is
+  // zeroed before use.
+  uint32_t lat_voff[L::kLatPerWave];  // byte offset of the chunk lane l fetches
+#pragma unroll
+  for (int n2 = 0; n2 < L::kLatPerWave; ++n2)
+    lat_voff[n2] = 16u * L::lat_slot(lane, wv * uint32_t(L::kLatPerWave) + n2);
+  const uint32_t pos_r = wv * uint32_t(L::kLatPerWave) + (lane >> 3);
+  const uint32_t pos_voff = 16u * L::pos_slot(lane % L::kPosCPR, pos_r);
   auto issue = [&](uint32_t kt) {
     unsigned char *stage = lds + (kt % kStages) * L::kStage;
     const uint32_t t0 = t_lo + kt * kTT;
-    const uint32_t r = wv * uint32_t(L::kLatPerWave) + (lane >> 3);
-    const uint32_t tok = t0 + r;
+    const uint32_t tok = t0 + pos_r;
     const bool ok = tok < t_hi;
     const uint32_t lp = ok ? page_of(tok) : wb;
     const uint32_t slot = ok ? tok - lp * ps : 0u;
@@ -179,13 +199,12 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
       const uint32_t rr = wv * uint32_t(L::kLatPerWave) + n2;
       const uint32_t pg = __builtin_amdgcn_readlane(page, 8 * n2);
       const uint32_t sl = __builtin_amdgcn_readlane(slot, 8 * n2);
-      const uint32_t base = pg * uint32_t(a.k_page) + sl * uint32_t(a.k_tok);
-      const uint32_t chunk = L::lat_slot(lane, rr);  // slot `lane` holds this chunk
-      dma16(lat + base + 8u * chunk, __builtin_amdgcn_readfirstlane(lds_addr(stage + rr * L::kLatRow)));
+      const T *row = lat + (pg * uint32_t(a.k_page) + sl * uint32_t(a.k_tok));
+      dma16_s(row, lat_voff[n2], __builtin_amdgcn_readfirstlane(lds_addr(stage + rr * L::kLatRow)));
     }
-    const uint32_t chunk = L::pos_slot(lane % L::kPosCPR, r);
-    const uint32_t off = page * uint32_t(a.kp_page) + slot * uint32_t(a.kp_tok) + 8u * chunk;
-    dma16(kpos + off, __builtin_amdgcn_readfirstlane(lds_addr(stage + L::kLat + 8u * wv * L::kPosRow)));
+    const uint32_t off = page * uint32_t(a.kp_page) + slot * uint32_t(a.kp_tok);
+    dma16(reinterpret_cast<const unsigned char *>(kpos + off) + pos_voff,
+          __builtin_amdgcn_readfirstlane(lds_addr(stage + L::kLat + 8u * wv * L::kPosRow)));
   };
   // before issuing tile kt: move the table window if the tile reaches past it
   auto window_for = [&](uint32_t kt) {
@@ -199,37 +218,33 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
     }
   };
 
-  // Per-lane LDS offsets.  The swizzle only permutes 16-byte chunks inside
-  // a 256-byte segment of a row, so each read is a per-lane base (a few
-  // registers) plus an immediate segment offset.
-  //   q.k:  lane (j, c16) reads chunk 4ks + j of row c16: segment ks >> 2,
-  //         in-segment chunk (4 (ks & 3) + j) ^ c16
-  //   pos:  chunk 4ks + j of position row c16, slot chunk ^ ((c16 >> 1) & 7)
-  //   V^T:  rows vr = 4j + (c16 >> 2) (+16), chunk 2b + ((c16 & 3) >> 1),
-  //         8-byte half c16 & 1: segment b >> 3, in-segment chunk
-  //         (2 (b & 7) + ((c16 & 3) >> 1)) ^ vr
-  const uint32_t qk_row = c16 * L::kLatRow;
+  // Per-lane LDS read offsets.  The swizzle only permutes 16-byte chunks
+  // inside a 256-byte segment of a row, so each read is a per-lane base plus
+  // an immediate segment offset.
+  //   q.k:  lane (j, c16) reads chunk 4ks + j of row c16 (+16 for M-tile 1):
+  //         segment ks >> 2, in-segment slot (4 (ks & 3) + j) ^ c16
+  //   pos:  chunk 4ks + j of position row c16 (+16)
+  //   V^T:  a transposed read gives lane (j, i) dim 16b + i of four rows,
+  //         supplied by the group's lanes: lane (j, c16) supplies row
+  //         pv_row(j, c16 >> 2) (+16 for the second read), dims 16b +
+  //         4 (c16 & 3) .. +3, i.e. chunk 2b + ((c16 & 3) >> 1), half c16 & 1.
+  //         pv_row(j, e) = 4 (j & 1) + (j >> 1) + 2 (e & 1) + 8 (e >> 1): the
+  //         rows of lanes 0..31 are 0,2,4,..,14, those of lanes 32..63 the
+  //         odd rows, one row of each slot pair per LDS cycle.
   uint32_t qk_off[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) qk_off[u] = 16u * ((4u * u + j) ^ c16);
-  const uint32_t pos_row = c16 * L::kPosRow;
+  for (int u = 0; u < 4; ++u) qk_off[u] = c16 * L::kLatRow + 16u * ((4u * u + j) ^ c16);
   uint32_t pos_off[KP];
 #pragma unroll
-  for (int ks = 0; ks < KP; ++ks) pos_off[ks] = 16u * L::pos_slot(4u * ks + j, c16);
-  const uint32_t vr = 4u * j + (c16 >> 2);
-  const uint32_t pv_row = vr * L::kLatRow + 8u * (c16 & 1u);
+  for (int ks = 0; ks < KP; ++ks) pos_off[ks] = c16 * L::kPosRow + 16u * L::pos_slot(4u * ks + j, c16);
+  const uint32_t e4 = c16 >> 2, q4 = c16 & 3u;
+  const uint32_t pv_row = 4u * (j & 1u) + (j >> 1) + 2u * (e4 & 1u) + 8u * (e4 >> 1);
   uint32_t pv_off[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) pv_off[u] = 16u * ((2u * u + ((c16 & 3u) >> 1)) ^ (vr & 15u));
+  for (int u = 0; u < 8; ++u)
+    pv_off[u] = pv_row * L::kLatRow + 8u * (q4 & 1u) + 16u * ((2u * u + (q4 >> 1)) ^ pv_row);
 
   const uint32_t n_tiles = t_hi > t_lo ? (t_hi - t_lo + kTT - 1) / kTT : 0u;
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) settle(qa[nt][ks]);
-#pragma unroll
-    for (int ks = 0; ks < KP; ++ks) settle(qp[nt][ks]);
-  }
   for (uint32_t kt = 0; kt < n_tiles && kt < uint32_t(kStages - 1); ++kt) {
     window_for(kt);
     issue(kt);
@@ -256,87 +271,90 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
     block_sync_lds();
 
     // S^T = latent . q_abs^T + k_pos . q_pos^T; M-tile mt holds tokens
-    // 16 mt + c16 (A rows), N-tile nt the heads.  Two accumulator chains
-    // (even and odd k-steps) per output tile keep the MFMA pipe fed.
-    f32x4_t s[2][kNT];
+    // 16 mt + c16 (A rows).  Both M-tiles advance together with four
+    // accumulators each (k-step mod 4): eight independent MFMA chains.
+    // Reads r = 0 .. 2 (KS + KP) - 1 go in order (k-step r / 2, M-tile
+    // r % 2); read r + kAhead is issued before the MFMA of read r, and the
+    // order is fenced so the LDS latency hides behind the MFMAs in flight.
+    constexpr int kCh = 4;
+    f32x4_t acc[2][kCh];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4_t acc[2][kNT];
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) acc[0][nt] = acc[1][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const unsigned char *lrow = st_lat + mt * (16 * L::kLatRow) + qk_row;
-      const unsigned char *prow_l = st_pos + mt * (16 * L::kPosRow) + pos_row;
-      // all A operands of this M-tile first (the reads overlap), then the MFMAs
-      uint4 ka[KS + KP];
+      for (int c = 0; c < kCh; ++c) acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      constexpr int kReads = 2 * (KS + KP), kAhead = 6;
+      auto load_a = [&](int r) -> uint4 {
+        const int ks = r >> 1, mt = r & 1;
+        if (ks < KS)
+          return *reinterpret_cast<const uint4 *>(st_lat + mt * (16 * L::kLatRow) + qk_off[ks & 3] +
+                                                  256 * (ks >> 2));
+        return *reinterpret_cast<const uint4 *>(st_pos + mt * (16 * L::kPosRow) + pos_off[ks - KS]);
+      };
+      uint4 ka[kAhead + 1];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[ks] = *reinterpret_cast<const uint4 *>(lrow + qk_off[ks & 3] + 256 * (ks >> 2));
+      for (int r = 0; r < kAhead; ++r) ka[r] = load_a(r);
 #pragma unroll
-      for (int ks = 0; ks < KP; ++ks) ka[KS + ks] = *reinterpret_cast<const uint4 *>(prow_l + pos_off[ks]);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) acc[ks & 1][nt] = M::qk(ka[ks], qa[nt][ks], acc[ks & 1][nt]);
-#pragma unroll
-      for (int ks = 0; ks < KP; ++ks)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) acc[ks & 1][nt] = M::qk(ka[KS + ks], qp[nt][ks], acc[ks & 1][nt]);
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) s[mt][nt] = acc[0][nt] + acc[1][nt];
+      for (int r = 0; r < kReads; ++r) {
+        if (r + kAhead < kReads) ka[(r + kAhead) % (kAhead + 1)] = load_a(r + kAhead);
+        const int ks = r >> 1, mt = r & 1;
+        acc[mt][ks % kCh] = M::qk(ka[r % (kAhead + 1)], ks < KS ? qa[ks] : qp[ks - KS], acc[mt][ks % kCh]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    f32x4_t s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) s[mt] = (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
 
     // online softmax per head; lane (j, c16) holds tokens 16 mt + 4 j + e
-    uint4 pb[kNT];
-    bool grow = false;
-    float alpha[kNT];
+    float x[2][4];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      float x[2][4];
-      float mt_max = -INFINITY;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int e = 0; e < 4; ++e) {
+        const bool vis = t0 + 16u * mt + 4u * j + e < t_hi;
+        x[mt][e] = vis ? s[mt][e] * sl2 : -INFINITY;
+        mx = fmaxf(mx, x[mt][e]);
+      }
+    mx = rows4_max(mx);
+    const float m_new = mx > m + kSlack ? mx : m;
+    const float alpha = fast_exp2(m - m_new);
+    const bool grow = m_new != m;
+    m = m_new;
+    float p[2][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool vis = t0 + 16u * mt + 4u * j + e < t_hi;
-          x[mt][e] = vis ? s[mt][nt][e] * sl2 : -INFINITY;
-          mt_max = fmaxf(mt_max, x[mt][e]);
-        }
-      mt_max = rows4_max(mt_max);
-      const float m_new = mt_max > m[nt] + kSlack ? mt_max : m[nt];
-      alpha[nt] = fast_exp2(m[nt] - m_new);
-      grow |= m_new != m[nt];
-      m[nt] = m_new;
-      float p[2][4];
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[mt][e] = fast_exp2(x[mt][e] - m_new);
-      lsum[nt] = lsum[nt] * alpha[nt] + (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-                                         ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
-      pb[nt].x = M::pack2(p[0][0], p[0][1]);
-      pb[nt].y = M::pack2(p[0][2], p[0][3]);
-      pb[nt].z = M::pack2(p[1][0], p[1][1]);
-      pb[nt].w = M::pack2(p[1][2], p[1][3]);
+      for (int e = 0; e < 4; ++e) p[mt][e] = fast_exp2(x[mt][e] - m_new);
+    lsum = lsum * alpha + (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                           ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+    // P^T operand in the value reads' row order: lane (j, c16) holds rows
+    // 4j .. 4j+3 of each M-tile and needs rows pv_row(j, 0..3).  Pack the
+    // even and odd rows separately; one swap of lanes 32..63 of the even
+    // pairs with lanes 0..31 of the odd pairs delivers them: lanes of j = 0
+    // get rows (0, 2) and (8, 10), j = 1 (4, 6) (12, 14), j = 2 (1, 3)
+    // (9, 11), j = 3 (5, 7) (13, 15).
+    uint4 pb;
+    {
+      const auto lo = __builtin_amdgcn_permlane32_swap(M::pack2(p[0][0], p[0][2]), M::pack2(p[0][1], p[0][3]),
+                                                       false, false);
+      const auto hi = __builtin_amdgcn_permlane32_swap(M::pack2(p[1][0], p[1][2]), M::pack2(p[1][1], p[1][3]),
+                                                       false, false);
+      pb = make_uint4(lo[0], lo[1], hi[0], hi[1]);
     }
     if (__any(grow)) {
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-        for (int b = 0; b < DB; ++b) o[nt][b] *= alpha[nt];
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;
     }
 
-    // O^T += latent^T . P^T over 32 tokens: K slots 8j .. 8j+3 are tokens
-    // 4j .. 4j+3 and slots 8j+4 .. 8j+7 tokens 16+4j .. 16+4j+3, matching
-    // the score layout.  Lane (j, c16) reads rows 4j + (c16 >> 2) and
-    // 16 + 4j + (c16 >> 2), columns 16b + 4(c16 & 3) .. +3 (transposed).
-    const unsigned char *v0 = st_lat + pv_row;
+    // O^T += latent^T . P^T over 32 tokens: K slots 8j .. 8j+3 are rows
+    // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16.
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      const unsigned char *p0 = v0 + pv_off[b & 7] + 256 * (b >> 3);
+      const unsigned char *p0 = st_lat + pv_off[b & 7] + 256 * (b >> 3);
       const uint2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * L::kLatRow);
-      const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) o[nt][b] = M::qk(va, pb[nt], o[nt][b]);
+      o[b] = M::qk(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[b]);
     }
     if (kt + kStages - 1 < n_tiles) {
       window_for(kt + kStages - 1);
@@ -344,30 +362,26 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
     }
   }
 
-  // normalise and write: lane holds O^T[d = 16b + 4j + e][head 16 nt + c16]
+  // normalise and write: lane holds O^T[d = 16b + 4j + e][head c16]
+  const float l_tot = rows4_sum(lsum);
+  const uint32_t h = h0 + c16;
+  if (h >= a.hq) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (a.splits == 1) {
+    T *out = static_cast<T *>(a.out) + (uint64_t(i) * a.hq + h) * R;
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const float l_tot = rows4_sum(lsum[nt]);
-    const uint32_t h = h0 + 16u * nt + c16;
-    if (h >= a.hq) continue;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (a.splits == 1) {
-      T *out = static_cast<T *>(a.out) + (uint64_t(i) * a.hq + h) * R;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        uint2 w;
-        w.x = M::pack2(o[nt][b][0] * inv, o[nt][b][1] * inv);
-        w.y = M::pack2(o[nt][b][2] * inv, o[nt][b][3] * inv);
-        *reinterpret_cast<uint2 *>(out + 16 * b + 4 * j) = w;
-      }
-    } else {
-      const uint64_t r = (uint64_t(i) * a.splits + part) * a.hq + h;
-      float *wo = a.ws_o + r * R;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-        *reinterpret_cast<f32x4_t *>(wo + 16 * b + 4 * j) = o[nt][b] * inv;
-      if (j == 0) a.ws_lse[r] = m[nt] + fast_log2(l_tot);
+    for (int b = 0; b < DB; ++b) {
+      uint2 w;
+      w.x = M::pack2(o[b][0] * inv, o[b][1] * inv);
+      w.y = M::pack2(o[b][2] * inv, o[b][3] * inv);
+      *reinterpret_cast<uint2 *>(out + 16 * b + 4 * j) = w;
     }
+  } else {
+    const uint64_t r = (uint64_t(i) * a.splits + part) * a.hq + h;
+    float *wo = a.ws_o + r * R;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) *reinterpret_cast<f32x4_t *>(wo + 16 * b + 4 * j) = o[b] * inv;
+    if (j == 0) a.ws_lse[r] = m + fast_log2(l_tot);
   }
 }
 
