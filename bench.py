@@ -1,28 +1,41 @@
-"""Benchmark: paged decode KV-read throughput on one MI355X.
+"""Benchmark: paged decode KV-read throughput and chunked-prefill MFMA rate on
+one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
-                    [--no-cpu-baseline] [--kernel-only]
+                    [--splits S] [--no-cpu-baseline] [--no-prefill]
+    python bench.py --copy-probe      (plain device copy of known size, for
+                                       calibrating HBM byte counters)
 
 A step is one pass of the hot path over one batch: pkv.attention on the
 bf16 GQA packed-decode workload (64 sequences, lengths ~U[512, 8192],
 Hq=32, Hkv=8, D=128, page size 16) with the split count pkv.suggest_splits
-chooses (split-KV partials, then the log-sum-exp merge).  Inputs are seeded
+chooses: split-KV partials, then the log-sum-exp merge.  Inputs are seeded
 synthetic tensors resident in HBM before timing starts.  `value` is the
 algorithmic K/V bytes of a step (every visible token row of every KV head
-read once) divided by the step time.
+read once) divided by the wall time per step.
 
 The JSON line also carries:
-  roofline      the dominant kernel (split decode) against the 8 TB/s HBM
-                peak, timed with HIP events on the plan's stream;
+  roofline      the dominant kernel (the split decode kernel) against the
+                8 TB/s HBM peak; its duration is measured live with HIP events
+                that the library records around that kernel on its stream
+                (pkv_plan_timing).  `traffic` is the HBM bytes per launch from
+                the committed rocprofv3 counter summary when it was taken on
+                the current kernel source, else null.
+  prefill       the chunked-prefill tile kernel on the mixed prefill + decode
+                workload (8 chunks x 512 queries + 120 decode rows): useful
+                FLOPs of the chunk queries / tile-kernel time, against the
+                dense bf16 MFMA peak.
   cpu_baseline  the float64 oracle timed on the host cores over a bounded
-                sample of the same workload (first sequences), in GB/s.
+                sample of the same workload, in GB/s.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +43,11 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "decode_bf16_gqa_64seq_hbm_traffic.md")
+# sources of the dominant (decode) kernel: the traffic figure is only used
+# while these are unchanged
+DECODE_SOURCES = ("decode_mfma.hip", "device_common.h", "mfma_common.h", "kernels.h")
 
 
 def _parse():
@@ -41,73 +59,134 @@ def _parse():
     p.add_argument("--splits", type=int, default=0, help="0: pkv.suggest_splits")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--copy-probe", action="store_true")
     return p.parse_args()
 
 
-def _traffic_from_profile(kernel_prefix: str):
-    """HBM bytes per launch from the committed counter summary, if current."""
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        "decode_bf16_gqa_64seq_traffic.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-        if rec.get("kernel_prefix") == kernel_prefix and rec.get("source_hash") == _kernel_hash():
-            return rec.get("bytes_per_launch")
-    except Exception:
-        pass
-    return None
-
-
-def _kernel_hash():
-    import hashlib
-    here = os.path.dirname(os.path.abspath(__file__))
+def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("rows_fast.hip", "rows_generic.hip", "device_common.h"):
-        with open(os.path.join(here, "paged_kv_cache_231_amd", "csrc", name), "rb") as f:
+    for name in DECODE_SOURCES:
+        with open(os.path.join(HERE, "paged_kv_cache_231_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def traffic_from_summary():
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current decode kernel source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    src = re.search(r"^source_hash:\s*(\w+)", text, re.M)
+    val = re.search(r"^hbm_bytes_per_launch:\s*(\d+)", text, re.M)
+    if not src or not val or src.group(1) != decode_source_hash():
+        return None
+    return int(val.group(1))
+
+
+def copy_probe(torch):
+    """Plain device-to-device copies of 1 GiB: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}),
+          flush=True)
+
+
 def cpu_baseline(wl, budget_s: float):
-    """Oracle throughput on the first sequences of the workload (bounded)."""
+    """Oracle throughput on a bounded sample: decode queries one at a time
+    (cycling through the batch) until the time budget is spent."""
     import oracle
-    from workloads import attention_bytes
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
     t = wl.tensors
-    done_bytes, elapsed, nq = 0, 0.0, 0
+    done_bytes, nq = 0, 0
     order = np.argsort(wl.qseq, kind="stable")
-    # take queries one at a time (cycling) until the time budget is spent
-    start = time.perf_counter()
-    for j in range(10 ** 9):
-        i = order[j % len(order)]
-        sl = np.array([i])
-        sub = dict(q=t["q"][sl], lens=wl.lens, qseq=wl.qseq[sl], qpos=wl.qpos[sl])
-        oracle.paged_attention(sub["q"], t["k"], t["v"], sub["lens"], sub["qseq"], sub["qpos"],
-                               wl.table, wl.page_size, wl.scale, wl.causal)
-        n_vis = (wl.qpos[i] + 1) if wl.causal else wl.lens[wl.qseq[i]]
+    if wl.kind == "attention":
         es = t["k"].element_size()
-        done_bytes += int(n_vis) * wl.info["hkv"] * (wl.info["d"] + wl.info["dv"]) * es
+        row_bytes = wl.info["hkv"] * (wl.info["d"] + wl.info["dv"]) * es
+    else:  # MLA: one latent row and one position row per token
+        es = t["latent"].element_size()
+        row_bytes = (wl.info["r"] + wl.info["p"]) * es
+    args = (wl.lens, None, None, wl.table, wl.page_size, wl.scale, wl.causal)
+    start = time.perf_counter()
+    elapsed = 0.0
+    while elapsed < budget_s:
+        i = order[nq % len(order)]
+        sl = np.array([i])
+        a = (args[0], wl.qseq[sl], wl.qpos[sl]) + args[3:]
+        if wl.kind == "attention":
+            oracle.paged_attention(t["q"][sl], t["k"], t["v"], *a)
+        else:
+            oracle.paged_mla(t["q_abs"][sl], t["q_pos"][sl], t["latent"], t["k_pos"], *a)
+        done_bytes += int(wl.visible()[i]) * row_bytes
         nq += 1
         elapsed = time.perf_counter() - start
-        if elapsed >= budget_s:
-            break
-    _ = attention_bytes
-    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": int(threads),
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{nq} query evaluations over the {wl.queries} decode queries "
-                      f"(float64 numpy oracle, "
-                      f"{elapsed:.1f} s, {done_bytes / 1e9:.3f} GB of K/V)"}
+            "sample": f"{nq} single-query oracle calls cycling over the {wl.queries} queries "
+                      f"(float64 numpy, {elapsed:.1f} s, {done_bytes / 1e9:.3f} GB of cache rows)"}
+
+
+def prefill_measure(torch, pkv, workloads, steps: int):
+    """Tile-kernel TFLOP/s on the mixed chunked-prefill workload."""
+    wl = workloads.config(4)
+    dev = {k: v.to("cuda") for k, v in wl.tensors.items()}
+    stream = torch.cuda.current_stream()
+    plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
+    hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
+    splits = pkv.suggest_splits(plan, hq, hkv, dv)
+    ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
+    out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
+
+    def step():
+        pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws, out=out)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    plan.timing(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    n_t, ms_t = plan.timing_read("tiles")
+    n_r, ms_r = plan.timing_read("rows")
+    plan.timing(False)
+    # useful FLOPs of the queries the tile kernel owns (every query that is
+    # not a decode row of the plan)
+    words = plan.words
+    R, T = int(words[7]), int(words[8])
+    S, Q = int(words[3]), int(words[2])
+    rows_off = 16 + S + 2 * Q
+    in_rows = np.zeros(Q, dtype=bool)
+    in_rows[np.asarray(words[rows_off:rows_off + R], dtype=np.int64)] = True
+    vis = wl.visible().astype(np.int64)
+    flops = int(vis[~in_rows].sum()) * hq * 2 * (d + dv)
+    avg_t = ms_t / max(1, n_t)
+    tfs = flops / (avg_t * 1e-3) / 1e12
+    return {"value": round(tfs, 1), "unit": "TFLOP/s", "peak": MFMA_BF16_PEAK_TFS,
+            "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "kernel": "chunked-prefill tiles",
+            "avg_launch_us": round(avg_t * 1e3, 2), "launches": n_t, "flops_per_launch": flops,
+            "tiles": T, "decode_rows_us": round(ms_r / max(1, n_r) * 1e3, 2),
+            "workload": wl.name}
 
 
 def main():
     args = _parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
-              "multi-GPU path; see the design notes for how it would shard.", file=sys.stderr)
+              "multi-GPU path; the design notes describe how it would shard.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -115,6 +194,10 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+
     wl = workloads.config(args.workload)
     dev = {k: v.to("cuda") for k, v in wl.tensors.items()}
     stream = torch.cuda.current_stream()
@@ -124,6 +207,7 @@ def main():
         splits = args.splits or pkv.suggest_splits(plan, hq, hkv, dv)
         ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
         out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
+        main_kernel = "tiles" if wl.info.get("prefill_queries") else "rows"
 
         def step():
             pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal,
@@ -133,6 +217,7 @@ def main():
         splits = args.splits or pkv.suggest_splits(plan, h, 1, r)
         ws = pkv.Workspace(wl.queries, h, r, splits) if splits > 1 else None
         out = torch.empty(wl.queries, h, r, dtype=wl.dtype, device="cuda")
+        main_kernel = "mla"
 
         def step():
             pkv.mla(plan, dev["q_abs"], dev["q_pos"], dev["latent"], dev["k_pos"], wl.scale,
@@ -142,30 +227,35 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    plan.timing(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for j in range(args.steps):
-        starts[j].record(stream)
+    for _ in range(args.steps):
         step()
-        ends[j].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kernels = {}
+    for name in ("rows", "tiles", "mla", "merge"):
+        n, ms = plan.timing_read(name)
+        if n:
+            kernels[name] = {"launches": n, "avg_us": round(ms / n * 1e3, 2)}
+    plan.timing(False)
     ms_per_step = wall * 1e3 / args.steps
-    avg_kernel_ms = float(np.mean(gpu_ms))
 
     nbytes = workloads.attention_bytes(wl)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / (avg_kernel_ms * 1e-3) / 1e9
+    if main_kernel not in kernels:  # e.g. a workload whose queries all went to tiles
+        main_kernel = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    avg_main_us = kernels[main_kernel]["avg_us"]
+    achieved = nbytes / (avg_main_us * 1e-6) / 1e9
+    traffic = traffic_from_summary() if args.workload == 2 and main_kernel == "rows" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": _traffic_from_profile("rows_fast_kernel"),
-                "kernel": "split decode + merge (one attention call)",
-                "avg_launch_us": round(avg_kernel_ms * 1e3, 2)}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": {"rows": "split-KV decode", "tiles": "chunked-prefill tiles",
+                           "mla": "MLA decode", "merge": "split merge"}[main_kernel],
+                "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": avg_main_us}
     line = {
-        "metric": "paged decode KV-read GB/s (% of HBM peak)",
+        "metric": "paged decode KV-read GB/s (% of HBM peak); chunked-prefill TFLOP/s (% MFMA)",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -180,7 +270,10 @@ def main():
         "config": {"workload": wl.name, "queries": wl.queries, "splits": splits,
                    "kv_bytes_per_step": nbytes, "parallelism": "single GPU"},
         "roofline": roofline,
+        "kernels": kernels,
     }
+    if not args.no_prefill and wl.kind == "attention":
+        line["prefill"] = prefill_measure(torch, pkv, workloads, args.prefill_steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -206,6 +206,30 @@ pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs,
                    void *out, uint32_t heads, uint32_t rank, uint32_t pos_dim,
                    float scale, int causal, pkv_workspace *ws, void *stream);
 
+/* ------------------------------------------------------------- timing
+ * Per-kernel timing, for benchmarks.  While enabled on a plan, every
+ * pkv_attention / pkv_mla call with that plan records a pair of HIP events
+ * around each kernel it launches, on the call's stream, so a kernel's
+ * duration is measured on the stream it runs on.  Kernels: the per-query
+ * row kernel (decode rows, split parts), the chunked-prefill tile kernel,
+ * the MLA kernel, and the split merge.  Enabling clears earlier records.
+ * Not for use while the stream is being captured into a graph (the event
+ * records would be captured too).  Errors: PKV_EINVAL (null plan, unknown
+ * kernel, null output), PKV_EHIP (event creation or query failure). */
+typedef enum {
+  PKV_KERNEL_ROWS = 0,
+  PKV_KERNEL_TILES = 1,
+  PKV_KERNEL_MLA = 2,
+  PKV_KERNEL_MERGE = 3
+} pkv_kernel;
+
+pkv_status pkv_plan_timing(pkv_plan *plan, int enable);
+
+/* Number of recorded launches of `kernel` and their summed duration in
+ * milliseconds (waits for the recorded events to complete). */
+pkv_status pkv_plan_timing_read(pkv_plan *plan, pkv_kernel kernel,
+                                uint32_t *launches, double *total_ms);
+
 /* Static message of the calling thread's last error ("" if none). */
 const char *pkv_last_error(void);
 

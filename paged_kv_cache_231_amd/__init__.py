@@ -152,6 +152,20 @@ class Plan:
                                             ctypes.c_void_p(self.stream)))
         self.words[int(index)] = int(value)
 
+    KERNELS = {"rows": 0, "tiles": 1, "mla": 2, "merge": 3}
+
+    def timing(self, enable: bool = True) -> None:
+        """Record HIP events around every kernel launched with this plan
+        (pkv_plan_timing); enabling clears earlier records."""
+        check(lib().pkv_plan_timing(self.handle, 1 if enable else 0))
+
+    def timing_read(self, kernel: str):
+        """(launches, summed milliseconds) of one kernel since timing was enabled."""
+        n = ctypes.c_uint32(0)
+        ms = ctypes.c_double(0.0)
+        check(lib().pkv_plan_timing_read(self.handle, self.KERNELS[kernel], ctypes.byref(n), ctypes.byref(ms)))
+        return int(n.value), float(ms.value)
+
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
             lib().pkv_plan_destroy(self._h)

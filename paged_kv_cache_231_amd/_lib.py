@@ -40,6 +40,8 @@ SIGNATURES = {
     "pkv_suggest_splits": (_u32, [_p, _u32, _u32, _u32]),
     "pkv_attention": (_i, [_p, _i, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _f, _i, _p, _p]),
     "pkv_mla": (_i, [_p, _i, _p, _p, _p, _p, _p, _u32, _u32, _u32, _f, _i, _p, _p]),
+    "pkv_plan_timing": (_i, [_p, _i]),
+    "pkv_plan_timing_read": (_i, [_p, _i, ctypes.POINTER(_u32), ctypes.POINTER(ctypes.c_double)]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }

@@ -22,6 +22,14 @@ struct pkv_plan {
   uint32_t *dev = nullptr;
   std::vector<uint32_t> host;
   pkv::PlanLayout L;
+  // per-kernel timing (pkv_plan_timing): event pairs recorded around launches
+  struct Rec {
+    int kernel;
+    hipEvent_t start, stop;
+  };
+  bool timing = false;
+  mutable std::vector<Rec> recs;
+  mutable std::vector<hipEvent_t> spare;
 };
 
 struct pkv_workspace {
@@ -91,22 +99,63 @@ pkv_status hip_fail(hipError_t e) {
   return fail(PKV_EHIP, "kernel launch failed");
 }
 
+hipEvent_t take_event(const pkv_plan *plan) {
+  if (!plan->spare.empty()) {
+    hipEvent_t e = plan->spare.back();
+    plan->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
+
+// Brackets one kernel launch with HIP events when the plan's timing is on.
+class Timed {
+ public:
+  Timed(const pkv_plan *plan, pkv_kernel kernel, hipStream_t st) : plan_(plan), st_(st) {
+    if (!plan_->timing) return;
+    rec_.kernel = int(kernel);
+    rec_.start = take_event(plan_);
+    rec_.stop = take_event(plan_);
+    if (rec_.start && rec_.stop && hipEventRecord(rec_.start, st_) == hipSuccess) on_ = true;
+  }
+  ~Timed() {
+    if (on_ && hipEventRecord(rec_.stop, st_) == hipSuccess) {
+      plan_->recs.push_back(rec_);
+    } else if (plan_->timing) {
+      if (rec_.start) plan_->spare.push_back(rec_.start);
+      if (rec_.stop) plan_->spare.push_back(rec_.stop);
+    }
+  }
+
+ private:
+  const pkv_plan *plan_;
+  hipStream_t st_;
+  pkv_plan::Rec rec_{};
+  bool on_ = false;
+};
+
 // Launches the row kernel (and the merge when split) over `qlist`.
-pkv_status run_rows(RowArgs ra, pkv_dtype dt, const pkv_workspace *ws, hipStream_t st) {
+pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_workspace *ws,
+                    hipStream_t st) {
   hipError_t e;
   if (ra.pdim != 0 && mla_mfma_supported(ra, dt)) {
     if (mla_mfma_blocks(ra) > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+    Timed t(plan, PKV_KERNEL_MLA, st);
     e = launch_mla_mfma(ra, dt, st);
   } else if (rows_mfma_supported(ra, dt)) {
     if (rows_mfma_blocks(ra) * 256u > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+    Timed t(plan, PKV_KERNEL_ROWS, st);
     e = launch_rows_mfma(ra, dt, st);
   } else if (rows_fast_supported(ra, dt)) {
     if (uint64_t(ra.n_queries) * ra.hq * ra.splits * 256u > kU32Max)
       return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+    Timed t(plan, PKV_KERNEL_ROWS, st);
     e = launch_rows_fast(ra, dt, st);
   } else {
     if (uint64_t(ra.n_queries) * ra.hq * ra.splits * 64u > kU32Max)
       return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
+    Timed t(plan, ra.pdim ? PKV_KERNEL_MLA : PKV_KERNEL_ROWS, st);
     e = launch_rows_generic(ra, dt, st);
   }
   if (e != hipSuccess) return hip_fail(e);
@@ -123,6 +172,7 @@ pkv_status run_rows(RowArgs ra, pkv_dtype dt, const pkv_workspace *ws, hipStream
     ma.ws_o = ra.ws_o;
     ma.ws_lse = ra.ws_lse;
     ma.out = ra.out;
+    Timed t(plan, PKV_KERNEL_MERGE, st);
     e = launch_merge(ma, dt, st);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -232,7 +282,45 @@ const uint32_t *pkv_plan_device_words(const pkv_plan *plan) { return plan ? plan
 void pkv_plan_destroy(pkv_plan *plan) {
   if (!plan) return;
   if (plan->dev) (void)hipFree(plan->dev);
+  for (const auto &r : plan->recs) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  for (hipEvent_t e : plan->spare) (void)hipEventDestroy(e);
   delete plan;
+}
+
+pkv_status pkv_plan_timing(pkv_plan *plan, int enable) {
+  clear_error();
+  if (!plan) return fail(PKV_EINVAL, "null plan");
+  for (const auto &r : plan->recs) {
+    plan->spare.push_back(r.start);
+    plan->spare.push_back(r.stop);
+  }
+  plan->recs.clear();
+  plan->timing = enable != 0;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_timing_read(pkv_plan *plan, pkv_kernel kernel, uint32_t *launches,
+                                double *total_ms) {
+  clear_error();
+  if (!plan || !launches || !total_ms) return fail(PKV_EINVAL, "null argument");
+  if (int(kernel) < int(PKV_KERNEL_ROWS) || int(kernel) > int(PKV_KERNEL_MERGE))
+    return fail(PKV_EINVAL, "unknown kernel");
+  uint32_t n = 0;
+  double ms = 0.0;
+  for (const auto &r : plan->recs) {
+    if (r.kernel != int(kernel)) continue;
+    float x = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&x, r.start, r.stop) != hipSuccess)
+      return fail(PKV_EHIP, "timing event query failed");
+    ++n;
+    ms += x;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return PKV_OK;
 }
 
 pkv_status pkv_workspace_create(uint32_t queries, uint32_t heads, uint32_t dv, uint32_t splits,
@@ -440,10 +528,11 @@ pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, c
   ra.n_queries = use_tiles ? L.R : L.Q;
 
   if (ra.n_queries) {
-    st = run_rows(ra, dtype, ws, stream);
+    st = run_rows(plan, ra, dtype, ws, stream);
     if (st != PKV_OK) return st;
   }
   if (use_tiles) {
+    Timed t(plan, PKV_KERNEL_TILES, stream);
     hipError_t e = launch_tiles(ta, dtype, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -506,7 +595,7 @@ pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs, con
   ra.qlist = nullptr;
   ra.n_queries = L.Q;
   fill_split(&ra, plan, ws);
-  return run_rows(ra, dtype, ws, stream);
+  return run_rows(plan, ra, dtype, ws, stream);
 }
 
 }  // extern "C"

@@ -100,6 +100,25 @@ def test_mla_latent512(dtype, h, ps):
     assert_close(run(wl, splits=16), want, dtype, "mla512 split 16")
 
 
+def test_kernel_timing_records_each_launch():
+    """pkv_plan_timing: one record per kernel launch, on the call's stream."""
+    wl = _decode_wl(torch.bfloat16, 16, 2, 128, 128, 16, [300, 77, 1000], seed=43)
+    dev = to_dev(wl)
+    plan = make_plan(wl)
+    plan.timing(True)
+    for _ in range(4):
+        run(wl, splits=3, plan=plan, dev=dev)
+    torch.cuda.synchronize()
+    n_rows, ms_rows = plan.timing_read("rows")
+    n_merge, ms_merge = plan.timing_read("merge")
+    assert n_rows == 4 and n_merge == 4
+    assert ms_rows > 0 and ms_merge > 0
+    assert plan.timing_read("tiles") == (0, 0.0)
+    plan.timing(False)
+    run(wl, plan=plan, dev=dev)
+    assert plan.timing_read("rows") == (0, 0.0)
+
+
 def test_page_permutation_is_bitwise_invariant():
     """Moving pages in the pool (same logical content) gives identical bits."""
     wl = _decode_wl(torch.bfloat16, 16, 2, 128, 128, 16, [300, 77, 1000], seed=41, pool_extra=0)
