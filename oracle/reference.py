@@ -1,8 +1,8 @@
 """Float64 oracle of paged attention (test infrastructure, not product code).
 
 Written from the ruDNN 0.1.7 ``paged_attention`` module page:
-  * module doc: one module serves MHA, GQA and MLA for packed decode and
-    chunked prefill, with no padded KV gather and no per-head KV repeat;
+  * module doc: a single module covers MHA, GQA and MLA, both packed decode
+    and chunked prefill, with no padded KV gather and no per-head KV repeat;
     non-finite inputs propagate through ordinary arithmetic;
   * ``DevicePlan::attention`` doc: packed Q ``[queries,Hq,D]``, paged K
     ``[pages,page_size,Hkv,D]``, V ``[pages,page_size,Hkv,Dv]``, output
@@ -206,8 +206,8 @@ def paged_mla(q_abs, q_pos, latent, k_pos, lens, qseq, qpos, table,
 def split_ranges(table_width: int, page_size: int, splits: int):
     """Logical token ranges of the parts of a split.
 
-    Reading of the ``attention_into_split`` doc ("split the visible history
-    over multiple planes"): part ``j`` covers the contiguous, page-aligned
+    Reading of the ``attention_into_split`` doc, which divides a query's
+    visible keys among several parts: part ``j`` covers the contiguous, page-aligned
     pages ``[j*pp, (j+1)*pp)`` of the block-table row, ``pp = ceil(W/splits)``,
     i.e. tokens ``[j*pp*ps, (j+1)*pp*ps)``.  The partition depends only on
     the table width, so it is fixed for a plan's shape; parts past a query's
@@ -224,7 +224,7 @@ def merge_partials(o_parts, lse_parts):
     o_parts [S, ..., Dv], lse_parts [S, ...] (natural log, -inf = empty part):
         M = max_s lse_s,  w_s = exp(lse_s - M)
         out = sum_s w_s o_s / sum_s w_s,   lse = M + log(sum_s w_s)
-    This is the "merge FP32 statistics" step of the ``attention_into_split``
+    This is the float32-statistics merge of the ``attention_into_split``
     doc, here in float64.
     """
     o_parts = np.asarray(o_parts, dtype=np.float64)

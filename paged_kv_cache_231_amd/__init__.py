@@ -229,17 +229,17 @@ def _dtype_code(*ts) -> int:
 def attention(plan: Plan, q, k, v, scale: float, causal: bool = True, workspace=None, out=None):
     """Paged MHA/GQA attention; returns ``out`` [Q, Hq, Dv]."""
     if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
-        raise PKVError("EINVAL", "invalid paged tensor ranks")
+        raise PKVError("EINVAL", "q must be 3-D and the caches 4-D")
     qn, hq, d = q.shape
     n, ps, hkv, dk = k.shape
     dv = v.shape[3]
     if qn != plan.queries or n != plan.pages or ps != plan.page_size or dk != d \
             or tuple(v.shape[:3]) != (n, ps, hkv):
-        raise PKVError("ESHAPE", "incompatible paged head/cache/output shape")
+        raise PKVError("ESHAPE", "head counts, head dims or tensor shapes do not fit together")
     if out is None:
         out = torch.empty((qn, hq, dv), dtype=q.dtype, device=q.device)
     elif tuple(out.shape) != (qn, hq, dv):
-        raise PKVError("ESHAPE", "incompatible paged head/cache/output shape")
+        raise PKVError("ESHAPE", "head counts, head dims or tensor shapes do not fit together")
     code = _dtype_code(q, k, v, out)
     check(lib().pkv_attention(plan.handle, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                               out.data_ptr(), hq, hkv, d, dv, float(scale), int(bool(causal)),
@@ -252,20 +252,20 @@ def mla(plan: Plan, q_abs, q_pos, latent, k_pos, scale: float, causal: bool = Tr
         workspace=None, out=None):
     """Absorbed MLA over one shared latent head; returns ``out`` [Q, H, R]."""
     if latent.dim() != 4 or latent.shape[2] != 1:
-        raise PKVError("EINVAL", "MLA latent cache must have one shared head")
+        raise PKVError("EINVAL", "the latent cache is [pages, page_size, 1, rank]: one head")
     if q_abs.dim() != 3 or q_pos.dim() != 3 or k_pos.dim() != 4:
-        raise PKVError("EINVAL", "invalid paged tensor ranks")
+        raise PKVError("EINVAL", "q must be 3-D and the caches 4-D")
     qn, h, r = q_abs.shape
     p = q_pos.shape[2]
     n, ps = latent.shape[0], latent.shape[1]
     if qn != plan.queries or n != plan.pages or ps != plan.page_size or latent.shape[3] != r \
             or tuple(q_pos.shape[:2]) != (qn, h) or tuple(k_pos.shape[:3]) != (n, ps, 1) \
             or k_pos.shape[3] != p:
-        raise PKVError("ESHAPE", "incompatible MLA positional dimensions")
+        raise PKVError("ESHAPE", "position dim must be 1..256 and match between q_pos and k_pos")
     if out is None:
         out = torch.empty((qn, h, r), dtype=q_abs.dtype, device=q_abs.device)
     elif tuple(out.shape) != (qn, h, r):
-        raise PKVError("ESHAPE", "incompatible paged head/cache/output shape")
+        raise PKVError("ESHAPE", "head counts, head dims or tensor shapes do not fit together")
     code = _dtype_code(q_abs, q_pos, latent, k_pos, out)
     check(lib().pkv_mla(plan.handle, code, q_abs.data_ptr(), q_pos.data_ptr(), latent.data_ptr(),
                         k_pos.data_ptr(), out.data_ptr(), h, r, p, float(scale),

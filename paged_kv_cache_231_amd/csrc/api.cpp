@@ -68,7 +68,7 @@ pkv_status check_binding(const pkv_plan *plan, hipStream_t stream) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(PKV_EHIP, "hipGetDevice failed");
   if (dev != plan->device || stream != plan->stream)
-    return fail(PKV_EDEVICE, "metadata belongs to another device/stream");
+    return fail(PKV_EDEVICE, "call made on another device or stream than the plan");
   return PKV_OK;
 }
 
@@ -463,12 +463,12 @@ pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, c
   if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
     return fail(PKV_EINVAL, "paged operands must be F32, F16 or BF16");
   if (hq == 0 || hkv == 0 || hq % hkv != 0 || d == 0 || dv == 0 || d > 1024 || dv > 1024)
-    return fail(PKV_ESHAPE, "incompatible paged head/cache/output shape");
+    return fail(PKV_ESHAPE, "head counts, head dims or tensor shapes do not fit together");
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PKV_EINVAL, "scale must be finite and positive");
   const PlanLayout &L = plan->L;
   if (!u32_elems({L.Q, hq, d}) || !u32_elems({L.N, L.ps, hkv, d}) || !u32_elems({L.N, L.ps, hkv, dv}) ||
       !u32_elems({L.Q, hq, dv}))
-    return fail(PKV_ERANGE, "paged tensor exceeds U32 indexing");
+    return fail(PKV_ERANGE, "a tensor has more than 2^32 - 1 elements");
   pkv_status st = check_binding(plan, stream);
   if (st != PKV_OK) return st;
   st = check_workspace(ws, plan, hq, dv, stream);
@@ -548,13 +548,13 @@ pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs, con
   if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
     return fail(PKV_EINVAL, "paged operands must be F32, F16 or BF16");
   if (heads == 0 || rank == 0 || rank > 1024)
-    return fail(PKV_ESHAPE, "incompatible paged head/cache/output shape");
-  if (pos_dim == 0 || pos_dim > 256) return fail(PKV_ESHAPE, "incompatible MLA positional dimensions");
+    return fail(PKV_ESHAPE, "head counts, head dims or tensor shapes do not fit together");
+  if (pos_dim == 0 || pos_dim > 256) return fail(PKV_ESHAPE, "position dim must be 1..256 and match between q_pos and k_pos");
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PKV_EINVAL, "scale must be finite and positive");
   const PlanLayout &L = plan->L;
   if (!u32_elems({L.Q, heads, rank}) || !u32_elems({L.Q, heads, pos_dim}) ||
       !u32_elems({L.N, L.ps, 1, rank}) || !u32_elems({L.N, L.ps, 1, pos_dim}))
-    return fail(PKV_ERANGE, "paged tensor exceeds U32 indexing");
+    return fail(PKV_ERANGE, "a tensor has more than 2^32 - 1 elements");
   pkv_status st = check_binding(plan, stream);
   if (st != PKV_OK) return st;
   st = check_workspace(ws, plan, heads, rank, stream);
