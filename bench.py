@@ -8,8 +8,9 @@ one MI355X.
 
 A step is one pass of the hot path over one batch: pkv.attention on the
 bf16 GQA packed-decode workload (64 sequences, lengths ~U[512, 8192],
-Hq=32, Hkv=8, D=128, page size 16) with the split count pkv.suggest_splits
-chooses: split-KV partials, then the log-sum-exp merge.  Inputs are seeded
+Hq=32, Hkv=8, D=128, page size 16) with the split count pkv.tune_splits
+measures fastest before timing starts: split-KV partials, then the
+log-sum-exp merge.  Inputs are seeded
 synthetic tensors resident in HBM before timing starts.  `value` is the
 algorithmic K/V bytes of a step (every visible token row of every KV head
 read once) divided by the wall time per step.
@@ -56,7 +57,8 @@ def _parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    p.add_argument("--splits", type=int, default=0, help="0: pkv.suggest_splits")
+    p.add_argument("--splits", type=int, default=0,
+                   help="0: measured choice (pkv.tune_splits); -1: pkv.suggest_splits")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-prefill", action="store_true")
@@ -146,9 +148,9 @@ def prefill_measure(torch, pkv, workloads, steps: int):
     stream = torch.cuda.current_stream()
     plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
     hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
-    splits = pkv.suggest_splits(plan, hq, hkv, dv)
-    ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
     out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
+    splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
+    ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
 
     def step():
         pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws, out=out)
@@ -204,9 +206,14 @@ def main():
     plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
     if wl.kind == "attention":
         hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
-        splits = args.splits or pkv.suggest_splits(plan, hq, hkv, dv)
-        ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
         out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
+        if args.splits > 0:
+            splits = args.splits
+        elif args.splits < 0:
+            splits = pkv.suggest_splits(plan, hq, hkv, dv)
+        else:
+            splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
+        ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
         main_kernel = "tiles" if wl.info.get("prefill_queries") else "rows"
 
         def step():
@@ -214,9 +221,15 @@ def main():
                           workspace=ws, out=out)
     else:
         h, r = wl.info["h"], wl.info["r"]
-        splits = args.splits or pkv.suggest_splits(plan, h, 1, r)
-        ws = pkv.Workspace(wl.queries, h, r, splits) if splits > 1 else None
         out = torch.empty(wl.queries, h, r, dtype=wl.dtype, device="cuda")
+        if args.splits > 0:
+            splits = args.splits
+        elif args.splits < 0:
+            splits = pkv.suggest_splits(plan, h, 1, r)
+        else:
+            splits = pkv.tune_splits_mla(plan, dev["q_abs"], dev["q_pos"], dev["latent"],
+                                         dev["k_pos"], wl.scale, wl.causal, out=out)
+        ws = pkv.Workspace(wl.queries, h, r, splits) if splits > 1 else None
         main_kernel = "mla"
 
         def step():

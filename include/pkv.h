@@ -168,6 +168,29 @@ void pkv_workspace_destroy(pkv_workspace *ws);
 uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads,
                             uint32_t kv_heads, uint32_t value_dim);
 
+/* Measured split choice: runs pkv_attention on the caller's tensors with
+ * each candidate split count (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, up
+ * to W, PKV_MAX_SPLITS and the workspace limit) `reps` times after one
+ * warm-up call, times each candidate with HIP events on `stream`, and
+ * writes the fastest count to *splits (a count with more splits must be
+ * more than 2% faster to win).  Uses a temporary workspace of its own;
+ * `out` receives the attention result.  Synchronises the stream; not for
+ * use under graph capture.  Errors: those of pkv_attention, PKV_EINVAL for
+ * a null plan or splits, PKV_EHIP. */
+pkv_status pkv_tune_splits(const pkv_plan *plan, pkv_dtype dtype, const void *q,
+                           const void *k, const void *v, void *out,
+                           uint32_t q_heads, uint32_t kv_heads, uint32_t head_dim,
+                           uint32_t value_dim, float scale, int causal,
+                           uint32_t reps, void *stream, uint32_t *splits);
+
+/* The same for pkv_mla. */
+pkv_status pkv_tune_splits_mla(const pkv_plan *plan, pkv_dtype dtype,
+                               const void *q_abs, const void *q_pos,
+                               const void *latent, const void *k_pos, void *out,
+                               uint32_t heads, uint32_t rank, uint32_t pos_dim,
+                               float scale, int causal, uint32_t reps,
+                               void *stream, uint32_t *splits);
+
 /* ------------------------------------------------------------- attention
  * out[i,h,:] = softmax_t(scale * <q[i,h,:], k_t>) . v_t over the visible
  * keys t of query i, with k_t = k[table[s][t/ps], t%ps, g, :] and

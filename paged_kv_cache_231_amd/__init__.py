@@ -214,13 +214,45 @@ def suggest_splits(plan: Plan, q_heads: int, kv_heads: int, value_dim: int) -> i
     return int(lib().pkv_suggest_splits(plan.handle, int(q_heads), int(kv_heads), int(value_dim)))
 
 
+def tune_splits(plan: Plan, q, k, v, scale: float, causal: bool = True, out=None,
+                reps: int = 5) -> int:
+    """Fastest split count for this call, measured on these tensors
+    (pkv_tune_splits); synchronises the plan's stream."""
+    qn, hq, d = q.shape
+    hkv, dv = k.shape[2], v.shape[3]
+    if out is None:
+        out = torch.empty((qn, hq, dv), dtype=q.dtype, device=q.device)
+    code = _dtype_code(q, k, v, out)
+    s = ctypes.c_uint32(1)
+    check(lib().pkv_tune_splits(plan.handle, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), hq, hkv, d, dv, float(scale), int(bool(causal)),
+                                int(reps), ctypes.c_void_p(plan.stream), ctypes.byref(s)))
+    return int(s.value)
+
+
+def tune_splits_mla(plan: Plan, q_abs, q_pos, latent, k_pos, scale: float, causal: bool = True,
+                    out=None, reps: int = 5) -> int:
+    """Fastest split count for this MLA call (pkv_tune_splits_mla)."""
+    qn, h, r = q_abs.shape
+    p = q_pos.shape[2]
+    if out is None:
+        out = torch.empty((qn, h, r), dtype=q_abs.dtype, device=q_abs.device)
+    code = _dtype_code(q_abs, q_pos, latent, k_pos, out)
+    s = ctypes.c_uint32(1)
+    check(lib().pkv_tune_splits_mla(plan.handle, code, q_abs.data_ptr(), q_pos.data_ptr(),
+                                    latent.data_ptr(), k_pos.data_ptr(), out.data_ptr(), h, r, p,
+                                    float(scale), int(bool(causal)), int(reps),
+                                    ctypes.c_void_p(plan.stream), ctypes.byref(s)))
+    return int(s.value)
+
+
 def _dtype_code(*ts) -> int:
     dt = ts[0].dtype
     for t in ts:
         if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
-            raise PKVError("EINVAL", "paged operands require contiguous, same-device, same-dtype float tensors")
+            raise PKVError("EINVAL", "operands must be contiguous device tensors of one float dtype on one device")
         if t.device != ts[0].device:
-            raise PKVError("EINVAL", "paged operands require contiguous, same-device, same-dtype float tensors")
+            raise PKVError("EINVAL", "operands must be contiguous device tensors of one float dtype on one device")
     if dt not in _DTYPES:
         raise PKVError("EINVAL", "paged operands must be F32, F16 or BF16")
     return _DTYPES[dt]

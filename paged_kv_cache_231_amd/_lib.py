@@ -38,6 +38,10 @@ SIGNATURES = {
     "pkv_workspace_splits": (_u32, [_p]),
     "pkv_workspace_destroy": (None, [_p]),
     "pkv_suggest_splits": (_u32, [_p, _u32, _u32, _u32]),
+    "pkv_tune_splits": (_i, [_p, _i, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _f, _i, _u32, _p,
+                             ctypes.POINTER(_u32)]),
+    "pkv_tune_splits_mla": (_i, [_p, _i, _p, _p, _p, _p, _p, _u32, _u32, _u32, _f, _i, _u32, _p,
+                                 ctypes.POINTER(_u32)]),
     "pkv_attention": (_i, [_p, _i, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _f, _i, _p, _p]),
     "pkv_mla": (_i, [_p, _i, _p, _p, _p, _p, _p, _u32, _u32, _u32, _f, _i, _p, _p]),
     "pkv_plan_timing": (_i, [_p, _i]),

@@ -599,3 +599,93 @@ pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs, con
 }
 
 }  // extern "C"
+
+namespace {
+
+// Times `call(ws)` for each candidate split count and returns the fastest;
+// fewer splits win unless another count is more than 2% faster.
+template <class Call>
+pkv_status tune_splits(const pkv_plan *plan, uint32_t heads, uint32_t dv, uint32_t reps,
+                       hipStream_t stream, Call call, uint32_t *best_out) {
+  const PlanLayout &L = plan->L;
+  *best_out = 1;
+  if (L.Q == 0 || L.W == 0) return PKV_OK;
+  reps = std::max(1u, std::min(reps, 100u));
+  const uint32_t cand[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+  const uint64_t per_split = uint64_t(L.Q) * heads * (uint64_t(dv) + 1) * sizeof(float);
+  uint32_t max_s = 1;
+  for (uint32_t c : cand)
+    if (c <= L.W && c <= PKV_MAX_SPLITS && uint64_t(c) * per_split <= PKV_WORKSPACE_LIMIT_BYTES) max_s = c;
+  pkv_workspace ws;
+  ws.device = plan->device;
+  ws.stream = stream;
+  ws.queries = L.Q;
+  ws.heads = heads;
+  ws.dv = dv;
+  ws.bytes = size_t(uint64_t(max_s) * per_split);
+  if (max_s > 1 && hipMalloc(&ws.buf, ws.bytes) != hipSuccess) return fail(PKV_EHIP, "hipMalloc of workspace failed");
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  pkv_status st = PKV_OK;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) st = fail(PKV_EHIP, "hipEventCreate failed");
+  float best_ms = 0.f;
+  for (uint32_t c : cand) {
+    if (st != PKV_OK || c > max_s) break;
+    ws.splits = c;
+    pkv_workspace *w = c > 1 ? &ws : nullptr;
+    st = call(w);  // warm-up (and validation)
+    if (st != PKV_OK) break;
+    if (hipEventRecord(e0, stream) != hipSuccess) { st = fail(PKV_EHIP, "hipEventRecord failed"); break; }
+    for (uint32_t r = 0; r < reps && st == PKV_OK; ++r) st = call(w);
+    if (st != PKV_OK) break;
+    float ms = 0.f;
+    if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      st = fail(PKV_EHIP, "timing the candidates failed");
+      break;
+    }
+    if (c == 1 || ms < best_ms * 0.98f) {
+      best_ms = ms;
+      *best_out = c;
+    }
+  }
+  if (hipStreamSynchronize(stream) != hipSuccess && st == PKV_OK) st = fail(PKV_EHIP, "hipStreamSynchronize failed");
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (ws.buf) (void)hipFree(ws.buf);
+  ws.buf = nullptr;
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_tune_splits(const pkv_plan *plan, pkv_dtype dtype, const void *q, const void *k,
+                           const void *v, void *out, uint32_t q_heads, uint32_t kv_heads,
+                           uint32_t head_dim, uint32_t value_dim, float scale, int causal,
+                           uint32_t reps, void *stream, uint32_t *splits) {
+  clear_error();
+  if (!plan || !splits) return fail(PKV_EINVAL, "null argument");
+  return tune_splits(plan, q_heads, value_dim, reps, static_cast<hipStream_t>(stream),
+                     [&](pkv_workspace *ws) {
+                       return pkv_attention(plan, dtype, q, k, v, out, q_heads, kv_heads, head_dim,
+                                            value_dim, scale, causal, ws, stream);
+                     },
+                     splits);
+}
+
+pkv_status pkv_tune_splits_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs,
+                               const void *q_pos, const void *latent, const void *k_pos, void *out,
+                               uint32_t heads, uint32_t rank, uint32_t pos_dim, float scale,
+                               int causal, uint32_t reps, void *stream, uint32_t *splits) {
+  clear_error();
+  if (!plan || !splits) return fail(PKV_EINVAL, "null argument");
+  return tune_splits(plan, heads, rank, reps, static_cast<hipStream_t>(stream),
+                     [&](pkv_workspace *ws) {
+                       return pkv_mla(plan, dtype, q_abs, q_pos, latent, k_pos, out, heads, rank,
+                                      pos_dim, scale, causal, ws, stream);
+                     },
+                     splits);
+}
+
+}  // extern "C"

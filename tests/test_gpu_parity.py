@@ -119,6 +119,27 @@ def test_kernel_timing_records_each_launch():
     assert plan.timing_read("rows") == (0, 0.0)
 
 
+def test_tune_splits_picks_a_candidate_and_leaves_the_result():
+    """pkv_tune_splits / pkv_tune_splits_mla: the chosen count is one of the
+    candidates, and `out` holds a correct result afterwards."""
+    wl = _decode_wl(torch.bfloat16, 32, 8, 128, 128, 16, [3000, 77, 1000, 4096], seed=47)
+    dev = to_dev(wl)
+    plan = make_plan(wl)
+    out = torch.empty(wl.queries, 32, 128, dtype=torch.bfloat16, device="cuda")
+    s = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out, reps=2)
+    assert s in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64) and s <= wl.table_width
+    assert_close(out.double().cpu().numpy(), expected(wl), torch.bfloat16, "tuned attention")
+    lens = [700, 64]
+    mw = build_mla("tune", 31, torch.bfloat16, lens, decode_queries(lens), 128, 512, 64, 64)
+    mdev = to_dev(mw)
+    mplan = make_plan(mw)
+    mout = torch.empty(2, 128, 512, dtype=torch.bfloat16, device="cuda")
+    ms = pkv.tune_splits_mla(mplan, mdev["q_abs"], mdev["q_pos"], mdev["latent"], mdev["k_pos"],
+                             mw.scale, mw.causal, out=mout, reps=2)
+    assert ms >= 1 and ms <= mw.table_width
+    assert_close(mout.double().cpu().numpy(), expected(mw), torch.bfloat16, "tuned mla")
+
+
 def test_page_permutation_is_bitwise_invariant():
     """Moving pages in the pool (same logical content) gives identical bits."""
     wl = _decode_wl(torch.bfloat16, 16, 2, 128, 128, 16, [300, 77, 1000], seed=41, pool_extra=0)
@@ -244,25 +265,30 @@ def test_graph_capture_replays_with_new_lengths():
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
 def test_full_size_workloads_sampled(n):
     """The benchmark workloads at full size, in the launch configuration the
-    benchmark times (split count from pkv.suggest_splits), checked on sampled
-    (query, head) rows against the oracle computed one row at a time."""
+    benchmark times (split count measured by pkv.tune_splits) and with the
+    heuristic's count (pkv.suggest_splits), checked on sampled (query, head)
+    rows against the oracle computed one row at a time."""
     wl = config(n)
     dev = to_dev(wl)
     plan = make_plan(wl)
     if wl.kind == "attention":
-        splits = pkv.suggest_splits(plan, wl.info["hq"], wl.info["hkv"], wl.info["dv"])
         heads = wl.info["hq"]
+        tuned = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, reps=2)
+        suggested = pkv.suggest_splits(plan, heads, wl.info["hkv"], wl.info["dv"])
     else:
-        splits = pkv.suggest_splits(plan, wl.info["h"], 1, wl.info["r"])
         heads = wl.info["h"]
-    got = run(wl, splits=splits, plan=plan, dev=dev)
+        tuned = pkv.tune_splits_mla(plan, dev["q_abs"], dev["q_pos"], dev["latent"], dev["k_pos"],
+                                    wl.scale, wl.causal, reps=2)
+        suggested = pkv.suggest_splits(plan, heads, 1, wl.info["r"])
     rng = np.random.default_rng(n)
     idx = sorted(set(int(x) for x in rng.integers(0, wl.queries, size=12)) | {0, wl.queries - 1})
     pairs = [(i, int(rng.integers(0, heads))) for i in idx]
     want = expected_rows(wl, pairs)
-    sel = np.stack([got[i, h] for i, h in pairs])
-    assert_close(sel, want, wl.dtype, f"config {n} (splits={splits})")
-    assert np.isfinite(got).all()
+    for splits in sorted({tuned, suggested}):
+        got = run(wl, splits=splits, plan=plan, dev=dev)
+        sel = np.stack([got[i, h] for i, h in pairs])
+        assert_close(sel, want, wl.dtype, f"config {n} (splits={splits})")
+        assert np.isfinite(got).all()
 
 
 def _prefill_wl(dtype, hq, hkv, d, ps, chunks, dec_lens, seed, causal=True):
