@@ -5,10 +5,12 @@
 // query and one KV head, the G q heads of its group (no per-head KV repeat,
 // module doc) form a dense contraction: S^T[tokens x heads] = K . Q^T over
 // the head dimension, then O^T[d x heads] += V^T . P^T over the tokens.  Both
-// run on 16x16 MFMA tiles with the tokens on the M side, so the paged K rows
-// feed the A operand with plain 16-byte loads and the softmax probabilities
-// come out of the first product already in the B-operand layout of the
-// second.  Only V needs a transpose, done through LDS.
+// run on 16x16 MFMA tiles with the tokens on the M side, so the softmax
+// probabilities come out of the first product already in the B-operand
+// layout of the second.  K and V rows are read whole from HBM (16 bytes per
+// lane, streaming hint, one instruction per few rows), written to a per-wave
+// LDS tile, and read back in the MFMA layouts: K rows as the A operand, V^T
+// with transposed LDS reads.
 //
 // A block of four waves owns one (query, KV head, group of up to 16 q heads,
 // split part); its waves take 16-token tiles of the part in turn, each with

@@ -309,8 +309,8 @@ def test_invisible_nan_is_never_read_and_visible_nan_propagates():
 # --------------------------------------------------------- planted mistakes
 
 def test_planted_mistakes_trip_a_pin(monkeypatch):
-    """A dropped '+1' in the causal count, a lost scale and a swapped gather
-    index each make a pin above fail."""
+    """A dropped '+1' in the causal count, swapped page/slot indices in the
+    gather and an lse without its max term each make a pin above fail."""
     # 1. dropped +1: a causal query at position 0 would see nothing
     monkeypatch.setattr(ref, "visible_count",
                         lambda lens, qseq, qpos, i, causal: int(qpos[i]) if causal else int(lens[qseq[i]]))
@@ -339,4 +339,46 @@ def test_planted_mistakes_trip_a_pin(monkeypatch):
     monkeypatch.setattr(ref, "_softmax_pv", bad_softmax)
     with pytest.raises(AssertionError):
         test_two_keys_closed_form()
+    monkeypatch.undo()
+
+
+def _some_pin_fails(pins):
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            return True
+    return False
+
+
+def test_planted_operand_mistakes_trip_a_pin(monkeypatch):
+    """A lost scale, a wrong q-head -> KV-head map (h % Hkv) and K/V used in
+    each other's place each make at least one pin fail."""
+    real = oracle.paged_attention
+    pins = [test_single_visible_key_returns_its_value, test_two_keys_closed_form,
+            test_gqa_head_map_is_contiguous_groups, lambda: test_matches_torch_sdpa_on_a_chunk(True)]
+
+    # 1. scale dropped
+    monkeypatch.setattr(oracle, "paged_attention",
+                        lambda q, k, v, lens, qseq, qpos, table, ps, scale, causal, token_range=None:
+                        real(q, k, v, lens, qseq, qpos, table, ps, 1.0, causal, token_range))
+    assert _some_pin_fails(pins)
+    monkeypatch.undo()
+
+    # 2. q head h served by KV head h % Hkv (tiled instead of grouped heads)
+    def tiled(q, k, v, lens, qseq, qpos, table, ps, scale, causal, token_range=None):
+        g = q.shape[1] // k.shape[2]
+        return real(q, k.repeat(1, 1, g, 1), v.repeat(1, 1, g, 1), lens, qseq, qpos, table, ps,
+                    scale, causal, token_range)
+    monkeypatch.setattr(oracle, "paged_attention", tiled)
+    assert _some_pin_fails(pins)
+    monkeypatch.undo()
+
+    # 3. K and V exchanged where their shapes allow it
+    def swapped(q, k, v, lens, qseq, qpos, table, ps, scale, causal, token_range=None):
+        if k.shape == v.shape:
+            k, v = v, k
+        return real(q, k, v, lens, qseq, qpos, table, ps, scale, causal, token_range)
+    monkeypatch.setattr(oracle, "paged_attention", swapped)
+    assert _some_pin_fails(pins)
     monkeypatch.undo()
