@@ -88,7 +88,7 @@ __device__ __forceinline__ void wait_vm() {
 
 template <class DT, int D>
 __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub,
-                                                      uint32_t n_blocks, uint32_t per_xcd) {
+                                                      uint32_t n_groups) {
   using M = Mfma<DT>;
   using L = PLds<D>;
   using T = typename DT::T;
@@ -97,13 +97,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
   __shared__ __align__(1024) unsigned char lds[L::kBytes];
   __shared__ uint32_t tcache[kTableCache];
 
-  // blocks sharing a (tile, KV head) get consecutive logical numbers on the
-  // XCD that blockIdx.x % 8 selects
-  const uint32_t logical = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
-  if (logical >= n_blocks) return;
-  const uint32_t sub = logical % n_sub;
-  const uint32_t kvh = (logical / n_sub) % a.hkv;
-  const uint32_t tile = logical / n_sub / a.hkv;
+  // Blocks are dispatched round-robin over the eight XCDs (blockIdx.x % 8).
+  // The (tile, KV head) groups are dealt to the XCDs in turn, group g to XCD
+  // g % 8, and the n_sub blocks of a group run back to back on its XCD, so
+  // they share the group's K/V rows in that XCD's L2.  Dealing groups (not
+  // contiguous ranges) spreads every tile's work over all XCDs: tiles of
+  // one chunk have similar key counts while chunks differ widely.
+  const uint32_t k = blockIdx.x / 8u;
+  const uint32_t group = (k / n_sub) * 8u + blockIdx.x % 8u;
+  if (group >= n_groups) return;
+  const uint32_t sub = k % n_sub;
+  const uint32_t kvh = group % a.hkv;
+  const uint32_t tile = group / a.hkv;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -192,6 +197,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     }
   };
 
+  // Transposed value reads: lane (j, c16) supplies key row pv_row(j,
+  // c16 >> 2) (+16 for the second read), value dims 16b + 4 (c16 & 3) .. +3.
+  // pv_row(j, e) = 4 (j & 1) + (j >> 1) + 2 (e & 1) + 8 (e >> 1) puts rows
+  // 0,2,..,14 on lanes 0..31 and the odd rows on lanes 32..63, so the eight
+  // rows one LDS cycle serves land in distinct 32-byte slot pairs.
+  uint32_t pv_off[DB];
+  {
+    const uint32_t e4 = c16 >> 2, q4 = c16 & 3u;
+    const uint32_t pr = 4u * (j & 1u) + (j >> 1) + 2u * (e4 & 1u) + 8u * (e4 >> 1);
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+      pv_off[b] = pr * L::kRowB + 8u * (q4 & 1u) + 16u * ((2u * b + (q4 >> 1)) ^ L::swz(pr));
+  }
+
   const uint32_t n_tiles = (k_end + kTT - 1) / kTT;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
@@ -221,41 +240,65 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     }
     block_sync_lds();  // tile kt visible to all waves; stage of kt-1 free
 
-    // scores for both 16-row halves and both N-tiles
+    // scores for both 16-row halves and both N-tiles; each (half, N-tile)
+    // output runs two accumulator chains (even and odd k-steps), eight
+    // independent MFMA chains per wave
     f32x4_t s[2][2];
+    {
+      uint4 ka[2][KS];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const uint32_t r = 16u * mb + c16;
-      uint4 ka[KS];
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint32_t r = 16u * mb + c16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ka[mb][ks] = *reinterpret_cast<const uint4 *>(kt_lds + r * L::kRowB +
+                                                        16u * ((4u * ks + j) ^ L::swz(r)));
+      }
+      f32x4_t acc[2][2][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mb][nt][0] = acc[mb][nt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        ka[ks] = *reinterpret_cast<const uint4 *>(kt_lds + r * L::kRowB +
-                                                  16u * ((4u * ks + j) ^ L::swz(r)));
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = M::qk(ka[ks], qb[nt][ks], acc);
-        s[mb][nt] = acc;
-      }
+          for (int nt = 0; nt < 2; ++nt)
+            acc[mb][nt][ks & 1] = M::qk(ka[mb][ks], qb[nt][ks], acc[mb][nt][ks & 1]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) s[mb][nt] = acc[mb][nt][0] + acc[mb][nt][1];
     }
     const bool full = a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
                                : (t0 + kTT <= k_end);
-    uint2 pb[2][2];
+    // online softmax (base 2); the max is taken on raw scores (scale > 0),
+    // and each probability is exp2(score * scale_log2 - m) with one FMA
+    uint4 pb[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float x[2][4];
       float mt = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[mb][e] = s[mb][nt][e];
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t tok = t0 + 16u * mb + 4u * j + e;
+            const bool vis = tok < k_end && (!a.causal || tok <= pos[nt]);
+            x[mb][e] = vis ? s[mb][nt][e] : -INFINITY;
+          }
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t tok = t0 + 16u * mb + 4u * j + e;
-          const bool vis = full || (tok < k_end && (!a.causal || tok <= pos[nt]));
-          x[mb][e] = vis ? s[mb][nt][e] * sl2 : -INFINITY;
-          mt = fmaxf(mt, x[mb][e]);
-        }
-      mt = rows4_max(mt);
+        mt = fmaxf(fmaxf(mt, fmaxf(x[mb][0], x[mb][1])), fmaxf(x[mb][2], x[mb][3]));
+      mt = rows4_max(mt) * sl2;
       // Lazy rescaling: the reference max only moves when a tile's max
       // exceeds it by more than kSlack (base 2), so probabilities stay
       // below 2^kSlack and most tiles skip rescaling O.  The result is the
@@ -263,39 +306,36 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
       const float m_new = mt > m[nt] + kSlack ? mt : m[nt];
       const float alpha = fast_exp2(m[nt] - m_new);
       m[nt] = m_new;
-      float p_sum = 0.f;
+      float p[2][4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        float p[4];
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(x[mb][e] - m_new);
-          p_sum += p[e];
-        }
-        pb[mb][nt].x = M::pack2(p[0], p[1]);
-        pb[mb][nt].y = M::pack2(p[2], p[3]);
-      }
-      lsum[nt] = lsum[nt] * alpha + p_sum;
+        for (int e = 0; e < 4; ++e) p[mb][e] = fast_exp2(__builtin_fmaf(x[mb][e], sl2, -m_new));
+      lsum[nt] = lsum[nt] * alpha + (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                                     ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+      // P^T operand in the value reads' row order (see pv_off): pack even
+      // and odd rows of each half, then one swap of lanes 32..63 of the even
+      // pairs with lanes 0..31 of the odd pairs
+      const auto lo = __builtin_amdgcn_permlane32_swap(M::pack2(p[0][0], p[0][2]),
+                                                       M::pack2(p[0][1], p[0][3]), false, false);
+      const auto hi = __builtin_amdgcn_permlane32_swap(M::pack2(p[1][0], p[1][2]),
+                                                       M::pack2(p[1][1], p[1][3]), false, false);
+      pb[nt] = make_uint4(lo[0], lo[1], hi[0], hi[1]);
       if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int b = 0; b < DB; ++b) o[nt][b] *= alpha;
       }
     }
 
-    // O^T += V^T . P^T over both halves: lane (j, c16) reads row
-    // 16mb + 4j + (c16 >> 2), value columns 16b + 4(c16 & 3) .. +3
+    // O^T += V^T . P^T over the 32 keys: K slots 8j .. 8j+3 are key rows
+    // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const uint32_t r = 16u * mb + 4u * j + (c16 >> 2);
-      const unsigned char *vrow = vt_lds + r * L::kRowB + 8u * (c16 & 1u);
-      const uint32_t key = L::swz(r);
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const uint32_t chunk = 2u * b + ((c16 & 3u) >> 1);
-        const uint2 va = lds_read_tr16(vrow + 16u * (chunk ^ key));
-        o[0][b] = M::pv(va, pb[mb][0], o[0][b]);
-        o[1][b] = M::pv(va, pb[mb][1], o[1][b]);
-      }
+    for (int b = 0; b < DB; ++b) {
+      const unsigned char *p0 = vt_lds + pv_off[b];
+      const uint2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * L::kRowB);
+      const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      o[0][b] = M::qk(va, pb[0], o[0][b]);
+      o[1][b] = M::qk(va, pb[1], o[1][b]);
     }
     // refill the stage of tile kt-1 (every wave passed this iteration's
     // barrier, so none still reads it)
@@ -336,17 +376,19 @@ hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st) {
   const uint32_t grp = a.hq / a.hkv;
   const uint32_t qb_n = kRowsPerBlock / grp;
   const uint32_t n_sub = (PKV_TILE_MAX + qb_n - 1) / qb_n;
-  const uint64_t n_blocks = uint64_t(a.n_tiles) * a.hkv * n_sub;
-  if (n_blocks == 0) return hipSuccess;
-  const uint32_t per_xcd = uint32_t((n_blocks + 7) / 8);
-  const dim3 grid(8u * per_xcd);
-  const uint32_t nb = uint32_t(n_blocks);
+  const uint64_t n_groups = uint64_t(a.n_tiles) * a.hkv;
+  if (n_groups == 0) return hipSuccess;
+  // eight XCD lanes of ceil(groups / 8) groups, n_sub blocks each
+  const uint64_t blocks = (n_groups + 7) / 8 * 8 * n_sub;
+  if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  const uint32_t ng = uint32_t(n_groups);
   if (dt == PKV_BF16) {
-    if (a.d == 64) hipLaunchKernelGGL((prefill_kernel<BF16, 64>), grid, dim3(256), 0, st, a, n_sub, nb, per_xcd);
-    else hipLaunchKernelGGL((prefill_kernel<BF16, 128>), grid, dim3(256), 0, st, a, n_sub, nb, per_xcd);
+    if (a.d == 64) hipLaunchKernelGGL((prefill_kernel<BF16, 64>), grid, dim3(256), 0, st, a, n_sub, ng);
+    else hipLaunchKernelGGL((prefill_kernel<BF16, 128>), grid, dim3(256), 0, st, a, n_sub, ng);
   } else {
-    if (a.d == 64) hipLaunchKernelGGL((prefill_kernel<F16, 64>), grid, dim3(256), 0, st, a, n_sub, nb, per_xcd);
-    else hipLaunchKernelGGL((prefill_kernel<F16, 128>), grid, dim3(256), 0, st, a, n_sub, nb, per_xcd);
+    if (a.d == 64) hipLaunchKernelGGL((prefill_kernel<F16, 64>), grid, dim3(256), 0, st, a, n_sub, ng);
+    else hipLaunchKernelGGL((prefill_kernel<F16, 128>), grid, dim3(256), 0, st, a, n_sub, ng);
   }
   return hipGetLastError();
 }
