@@ -51,6 +51,27 @@ struct PLds {
   }
 };
 
+// Float max without IEEE canonicalisation of the inputs (fmaxf quiets both
+// operands first): the running max is only a reference point, and a NaN
+// score still reaches the output through its exponent.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max over the four 16-lane rows (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float rows4_vmax(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Compiler-level memory barriers around the raw hardware barrier: LDS loads
 // and stores may not move across, and no wait for outstanding global loads
 // is implied (the ring waits for those explicitly).
@@ -133,10 +154,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
 
   // block table of the sequence, first kTableCache entries, into LDS
   const uint32_t *table = pv.words + pv.table + uint64_t(seq) * pv.W;
+  // (each entry holds the element offset of the page's first row: K and V
+  // share their strides since head_dim == value_dim)
+  const uint32_t page_elems = uint32_t(a.k_page);
   const uint32_t n_lp = (k_end + ps - 1) / ps;
   for (uint32_t e = tid; e < n_lp && e < uint32_t(kTableCache); e += 256) {
     const uint32_t pg = table[e];
-    tcache[e] = pg < pv.N ? pg : 0u;  // never read outside the pool
+    tcache[e] = (pg < pv.N ? pg : 0u) * page_elems;  // never read outside the pool
   }
 
   // this wave's q-rows: N-tile nt, column c16 -> q-row 32*wv + 16*nt + c16
@@ -159,6 +183,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
   // smallest position among the block's queries: key tiles wholly at or
   // below it need no causal mask
   const uint32_t pos_min = p0 + q_lo;
+  // last visible key of each q-row: position (causal) or the last key
+  uint32_t lim[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) lim[nt] = a.causal && pos[nt] < k_end - 1u ? pos[nt] : k_end - 1u;
 
   f32x4_t o[2][DB];
 #pragma unroll
@@ -175,25 +203,51 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
   // RPW*(NI*wv + n) .. +RPW-1; lane -> row r0 + lane / CPR, slot lane % CPR,
   // which holds chunk slot ^ swz(row) of the cache row.  Rows past the end
   // read row 0 of page 0 (inside the pool) and are zeroed before use.
+  // Per-lane parts of the DMA addresses: load n of a wave covers rows
+  // r0(n) .. r0(n)+RPW-1, lane -> row r0(n) + lane / CPR and slot lane % CPR,
+  // which holds chunk slot ^ swz(row) of the cache row.  For a power-of-two
+  // page size the token's slot in its page is (kt*kTT mod ps) + (row mod ps),
+  // so its element offset splits into a per-tile uniform part and the
+  // per-lane part kept here.
+  const uint32_t tok_elems = uint32_t(a.k_tok);
+  uint32_t lane_off[L::NI];
+#pragma unroll
+  for (int n = 0; n < L::NI; ++n) {
+    const uint32_t r = L::RPW * (L::NI * wv + n) + lane / L::CPR;
+    const uint32_t chunk = (lane % L::CPR) ^ L::swz(r);
+    lane_off[n] = (pow2 ? (r & (ps - 1u)) * tok_elems : 0u) + 8u * chunk;
+  }
+  // DMA of key tile kt into its ring stage.  Rows past the end read row 0 of
+  // page 0 (inside the pool) and are zeroed before use.
   auto issue = [&](uint32_t kt) {
     unsigned char *stage = lds + (kt % kStages) * L::kStage;
+    const uint32_t tok0 = kt * kTT;
+    const uint32_t tile_off = pow2 ? (tok0 & (ps - 1u)) * tok_elems : 0u;
 #pragma unroll
     for (int n = 0; n < L::NI; ++n) {
       const uint32_t r0 = L::RPW * (L::NI * wv + n);
       const uint32_t r = r0 + lane / L::CPR;
-      const uint32_t tok = kt * kTT + r;
+      const uint32_t tok = tok0 + r;
       const bool ok = tok < k_end;
-      const uint32_t lp = ok ? (pow2 ? tok >> ps_shift : tok / ps) : 0u;
-      const uint32_t slot = ok ? tok - lp * ps : 0u;
-      const uint32_t page = ok ? (lp < uint32_t(kTableCache) ? tcache[lp]
-                                                             : (table[lp] < pv.N ? table[lp] : 0u))
-                               : 0u;
-      const uint32_t chunk = (lane % L::CPR) ^ L::swz(r);
-      const uint32_t ko = page * uint32_t(a.k_page) + slot * uint32_t(a.k_tok) + 8u * chunk;
-      const uint32_t vo = page * uint32_t(a.v_page) + slot * uint32_t(a.v_tok) + 8u * chunk;
+      uint32_t off;
+      if (pow2) {
+        const uint32_t lp = ok ? tok >> ps_shift : 0u;  // entry 0 exists whenever a tile does
+        const uint32_t pbase = lp < uint32_t(kTableCache)
+                                   ? tcache[lp]
+                                   : (table[lp] < pv.N ? table[lp] : 0u) * page_elems;
+        off = ok ? pbase + tile_off + lane_off[n] : lane_off[n] - (r & (ps - 1u)) * tok_elems;
+      } else {
+        const uint32_t lp = ok ? tok / ps : 0u;
+        const uint32_t slot = ok ? tok - lp * ps : 0u;
+        const uint32_t pbase = !ok ? 0u
+                               : lp < uint32_t(kTableCache)
+                                   ? tcache[lp]
+                                   : (table[lp] < pv.N ? table[lp] : 0u) * page_elems;
+        off = pbase + slot * tok_elems + lane_off[n];
+      }
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + r0 * L::kRowB));
-      dma16(kbase + ko, dst);
-      dma16(vbase + vo, dst + uint32_t(L::kTile));
+      dma16(kbase + off, dst);
+      dma16(vbase + off, dst + uint32_t(L::kTile));
     }
   };
 
@@ -279,26 +333,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float x[2][4];
-      float mt = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[mb][e] = s[mb][nt][e];
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t tok = t0 + 16u * mb + 4u * j + e;
-            const bool vis = tok < k_end && (!a.causal || tok <= pos[nt]);
-            x[mb][e] = vis ? s[mb][nt][e] : -INFINITY;
-          }
-      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
-        mt = fmaxf(fmaxf(mt, fmaxf(x[mb][0], x[mb][1])), fmaxf(x[mb][2], x[mb][3]));
-      mt = rows4_max(mt) * sl2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[mb][e] = s[mb][nt][e];
+      if (!full) {
+        // key row 16mb + 4j + e of the tile is visible iff its index is at
+        // most lim[nt] - t0 - 4j (one signed compare per score)
+        const int d = int(lim[nt]) - int(t0) - int(4u * j);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[mb][e] = 16 * mb + e <= d ? x[mb][e] : -INFINITY;
+      }
+      float mt = vmax3(vmax3(x[0][0], x[0][1], x[0][2]), vmax3(x[0][3], x[1][0], x[1][1]),
+                       vmax3(x[1][2], x[1][3], -INFINITY));
+      mt = rows4_vmax(mt) * sl2;
       // Lazy rescaling: the reference max only moves when a tile's max
       // exceeds it by more than kSlack (base 2), so probabilities stay
       // below 2^kSlack and most tiles skip rescaling O.  The result is the
