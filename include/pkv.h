@@ -69,7 +69,9 @@ typedef struct pkv_workspace pkv_workspace; /* opaque; f32 split partials      *
  * Tiles: scanning queries in order, a run is a maximal range of queries of
  * one sequence whose positions increase by one.  Runs of at least
  * PKV_TILE_MIN queries are cut from their first query into tiles of at most
- * PKV_TILE_MAX; queries of shorter runs are rows.
+ * PKV_TILE_MAX; queries of shorter runs are rows.  Tiles are listed
+ * heaviest first: by decreasing sum of (position + 1) over their queries,
+ * ties by increasing first query (kernels start long tiles first).
  *
  * Visible keys of query i: positions 0..qpos[i] when causal (absolute
  * positions, prefill chunks included: `DevicePlan::attention` doc), all

@@ -30,7 +30,10 @@ Spec v1 (little-endian u32 words):
 Tiles: scanning the queries in order, a run is a maximal range of queries of
 one sequence whose positions increase by one from query to query.  A run of
 at least TILE_MIN queries is cut, from its first query, into tiles of at
-most TILE_MAX queries; the queries of shorter runs are rows.
+most TILE_MAX queries; the queries of shorter runs are rows.  Tiles are
+listed heaviest first: by decreasing work, the sum over the tile's queries
+of (position + 1), then by increasing first query (kernels take tiles in
+list order, so long tiles start first).
 
 Validation (each failure raises ``PlanError`` with the status name the C
 ABI returns for it):
@@ -85,6 +88,12 @@ def split_rows_tiles(qseq, qpos):
                 tiles.append((first, min(TILE_MAX, b - first)))
         else:
             rows.extend(range(a, b))
+
+    def work(tile):  # sum of (position + 1) over the tile's queries
+        first, count = tile
+        return count * int(qpos[first]) + count * (count + 1) // 2
+
+    tiles.sort(key=lambda t: (-work(t), t[0]))
     return rows, tiles
 
 

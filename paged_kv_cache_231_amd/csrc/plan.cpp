@@ -7,6 +7,7 @@
 // so kernels can index the cache with the words without further checks.
 
 #include <cstring>
+#include <algorithm>
 #include <vector>
 
 #include "common.h"
@@ -23,6 +24,11 @@ uint32_t ceil_div(uint32_t a, uint32_t b) { return a / b + (a % b != 0); }
 // run rule of spec v1.
 void cut_runs(uint32_t q_count, const uint32_t *qseq, const uint32_t *qpos,
               std::vector<uint32_t> *rows, std::vector<uint32_t> *tiles) {
+  struct Tile {
+    uint32_t first, count;
+    uint64_t work;  // sum of (position + 1) over the tile's queries
+  };
+  std::vector<Tile> found;
   uint32_t a = 0;
   while (a < q_count) {
     uint32_t b = a + 1;
@@ -30,13 +36,21 @@ void cut_runs(uint32_t q_count, const uint32_t *qseq, const uint32_t *qpos,
     const uint32_t len = b - a;
     if (len >= PKV_TILE_MIN) {
       for (uint32_t f = a; f < b; f += PKV_TILE_MAX) {
-        tiles->push_back(f);
-        tiles->push_back(b - f < PKV_TILE_MAX ? b - f : PKV_TILE_MAX);
+        const uint32_t c = b - f < PKV_TILE_MAX ? b - f : PKV_TILE_MAX;
+        found.push_back({f, c, uint64_t(c) * qpos[f] + uint64_t(c) * (c + 1) / 2});
       }
     } else {
       for (uint32_t i = a; i < b; ++i) rows->push_back(i);
     }
     a = b;
+  }
+  // heaviest first (kernels take tiles in list order), ties by first query
+  std::sort(found.begin(), found.end(), [](const Tile &x, const Tile &y) {
+    return x.work != y.work ? x.work > y.work : x.first < y.first;
+  });
+  for (const Tile &t : found) {
+    tiles->push_back(t.first);
+    tiles->push_back(t.count);
   }
 }
 }  // namespace

@@ -44,11 +44,17 @@ def test_tile_rule_boundaries():
     assert rows == list(range(n - 1)) and tiles == []
     # a gap in positions or a change of sequence ends a run
     rows, tiles = op.split_rows_tiles([0] * 20 + [1] * 20, list(range(10)) + list(range(11, 21)) + list(range(20)))
-    assert tiles == [(0, 10), (10, 10), (20, 20)] and rows == []
+    # listed heaviest first: works 20*0 + 210 = 210, 10*11 + 55 = 165, 55
+    assert tiles == [(20, 20), (10, 10), (0, 10)] and rows == []
+    # equal work: the earlier first query comes first
+    rows, tiles = op.split_rows_tiles([0] * 10 + [1] * 10, list(range(10)) * 2)
+    assert tiles == [(0, 10), (10, 10)] and rows == []
     # 2 * TILE_MAX + 1 consecutive queries -> 3 tiles
     m = 2 * op.TILE_MAX + 1
     rows, tiles = op.split_rows_tiles([0] * m, list(range(m)))
-    assert tiles == [(0, op.TILE_MAX), (op.TILE_MAX, op.TILE_MAX), (2 * op.TILE_MAX, 1)]
+    # cut from the first query; the later full tile sees more keys, so it
+    # is listed first
+    assert tiles == [(op.TILE_MAX, op.TILE_MAX), (0, op.TILE_MAX), (2 * op.TILE_MAX, 1)]
 
 
 def _ok_args():
