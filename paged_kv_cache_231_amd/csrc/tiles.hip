@@ -193,7 +193,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int b = 0; b < DB; ++b) o[nt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kNoMax, kNoMax}, lsum[2] = {0.f, 0.f};
+  float m[2] = {kNoMax, kNoMax};
+  // Softmax denominators on the matrix core: one more 16-row output block
+  // per N-tile whose A operand is all ones, so each of its rows accumulates
+  // the sum of P over the keys for the lane's q-row (rescaled with O).
+  f32x4_t lacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  uint4 ones;
+  ones.x = ones.y = ones.z = ones.w = M::pack2(1.f, 1.f);
   const float sl2 = a.scale_log2;
   const T *kbase = static_cast<const T *>(a.k) + uint64_t(kvh) * D;
   const T *vbase = static_cast<const T *>(a.v) + uint64_t(kvh) * D;
@@ -272,19 +278,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     for (int ks = 0; ks < KS; ++ks) settle(qb[nt][ks]);
   for (uint32_t kt = 0; kt < n_tiles && kt < uint32_t(kStages - 1); ++kt) issue(kt);
 
-  for (uint32_t kt = 0; kt < n_tiles; ++kt) {
-    const uint32_t t0 = kt * kTT;
-    // this thread's loads of tile kt are done once at most the loads of the
-    // tiles issued after it are outstanding
-    const uint32_t ahead = n_tiles - 1 - kt;
-    if (ahead >= 2) wait_vm<2 * kLoadsPerTile>();
-    else if (ahead == 1) wait_vm<kLoadsPerTile>();
+  // Tile kt's ring stage is complete and visible to every wave once each
+  // thread has seen its own loads of kt land and the block has passed a
+  // barrier (which also means every wave finished reading the stage the next
+  // refill overwrites).  `later` = tiles issued after kt that may still be
+  // in flight.
+  auto ready = [&](uint32_t kt, uint32_t later) {
+    if (later >= 2) wait_vm<2 * kLoadsPerTile>();
+    else if (later == 1) wait_vm<kLoadsPerTile>();
     else wait_vm<0>();
-    unsigned char *kt_lds = lds + (kt % kStages) * L::kStage;
-    unsigned char *vt_lds = kt_lds + L::kTile;
+    const uint32_t t0 = kt * kTT;
     if (t0 + kTT > k_end) {
       // last tile: rows past the end hold whatever row 0 of page 0 holds;
       // zero their V (a NaN there must not reach the product)
+      unsigned char *vt_lds = lds + (kt % kStages) * L::kStage + L::kTile;
       block_sync_lds();
       for (uint32_t e = tid; e < uint32_t(kTT * L::CPR); e += 256) {
         const uint32_t r = e / L::CPR;
@@ -292,77 +299,97 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
           *reinterpret_cast<uint4 *>(vt_lds + r * L::kRowB + 16u * (e % L::CPR)) = make_uint4(0, 0, 0, 0);
       }
     }
-    block_sync_lds();  // tile kt visible to all waves; stage of kt-1 free
-
-    // scores for both 16-row halves and both N-tiles; each (half, N-tile)
-    // output runs two accumulator chains (even and odd k-steps), eight
-    // independent MFMA chains per wave
-    f32x4_t s[2][2];
-    {
-      uint4 ka[2][KS];
+    block_sync_lds();
+  };
+  // S^T of key tile kt for both 16-row halves and both N-tiles (four
+  // independent MFMA chains)
+  auto scores = [&](uint32_t kt, f32x4_t (&sc)[2][2]) {
+    const unsigned char *kt_lds = lds + (kt % kStages) * L::kStage;
+    uint4 ka[2][KS];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const uint32_t r = 16u * mb + c16;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[mb][ks] = *reinterpret_cast<const uint4 *>(kt_lds + r * L::kRowB +
-                                                        16u * ((4u * ks + j) ^ L::swz(r)));
-      }
-      f32x4_t acc[2][2][2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mb][nt][0] = acc[mb][nt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint32_t r = 16u * mb + c16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
+        ka[mb][ks] = *reinterpret_cast<const uint4 *>(kt_lds + r * L::kRowB +
+                                                      16u * ((4u * ks + j) ^ L::swz(r)));
+    }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            acc[mb][nt][ks & 1] = M::qk(ka[mb][ks], qb[nt][ks], acc[mb][nt][ks & 1]);
+      for (int nt = 0; nt < 2; ++nt) sc[mb][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) s[mb][nt] = acc[mb][nt][0] + acc[mb][nt][1];
-    }
+        for (int nt = 0; nt < 2; ++nt) sc[mb][nt] = M::qk(ka[mb][ks], qb[nt][ks], sc[mb][nt]);
+  };
+
+  // Software pipeline: the scores of tile kt+1 are issued before the
+  // softmax and value product of tile kt, so the matrix core works on the
+  // next tile while the VALU computes this tile's exponentials.
+  f32x4_t s[2][2];
+  if (n_tiles) {
+    ready(0, n_tiles - 1 < 2u ? n_tiles - 1 : 2u);
+    scores(0, s);
+  }
+  for (uint32_t kt = 0; kt < n_tiles; ++kt) {
+    const uint32_t t0 = kt * kTT;
+    unsigned char *vt_lds = lds + (kt % kStages) * L::kStage + L::kTile;
+    // issued so far: tiles 0 .. kt+2
+    if (kt + 1 < n_tiles) ready(kt + 1, kt + 2 < n_tiles ? 1u : 0u);
+
+    // scores of tile kt, masked where a key is not visible
+    float x[2][2][4];  // [N-tile][half][row]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[nt][mb][e] = s[mb][nt][e];
     const bool full = a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
                                : (t0 + kTT <= k_end);
-    // online softmax (base 2); the max is taken on raw scores (scale > 0),
-    // and each probability is exp2(score * scale_log2 - m) with one FMA
-    uint4 pb[2];
+    if (!full) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float x[2][4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[mb][e] = s[mb][nt][e];
-      if (!full) {
+      for (int nt = 0; nt < 2; ++nt) {
         // key row 16mb + 4j + e of the tile is visible iff its index is at
         // most lim[nt] - t0 - 4j (one signed compare per score)
         const int d = int(lim[nt]) - int(t0) - int(4u * j);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[mb][e] = 16 * mb + e <= d ? x[mb][e] : -INFINITY;
+          for (int e = 0; e < 4; ++e) x[nt][mb][e] = 16 * mb + e <= d ? x[nt][mb][e] : -INFINITY;
       }
-      float mt = vmax3(vmax3(x[0][0], x[0][1], x[0][2]), vmax3(x[0][3], x[1][0], x[1][1]),
-                       vmax3(x[1][2], x[1][3], -INFINITY));
+    }
+
+    // One straight-line block: the MFMAs of tile kt+1's scores interleaved
+    // with tile kt's softmax arithmetic.  After the last tile the scores
+    // read a ring stage whose contents are not used (in bounds).
+    f32x4_t s_next[2][2];
+    scores(kt + 1, s_next);
+    // online softmax (base 2); the max is taken on raw scores (scale > 0),
+    // and each probability is exp2(score * scale_log2 - m) with one FMA
+    uint4 pb[2];
+    float alpha[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mt = vmax3(vmax3(x[nt][0][0], x[nt][0][1], x[nt][0][2]),
+                       vmax3(x[nt][0][3], x[nt][1][0], x[nt][1][1]),
+                       vmax3(x[nt][1][2], x[nt][1][3], -INFINITY));
       mt = rows4_vmax(mt) * sl2;
       // Lazy rescaling: the reference max only moves when a tile's max
       // exceeds it by more than kSlack (base 2), so probabilities stay
       // below 2^kSlack and most tiles skip rescaling O.  The result is the
       // same softmax: numerator and denominator share the reference.
       const float m_new = mt > m[nt] + kSlack ? mt : m[nt];
-      const float alpha = fast_exp2(m[nt] - m_new);
+      alpha[nt] = fast_exp2(m[nt] - m_new);
       m[nt] = m_new;
       float p[2][4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[mb][e] = fast_exp2(__builtin_fmaf(x[mb][e], sl2, -m_new));
-      lsum[nt] = lsum[nt] * alpha + (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-                                     ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+        for (int e = 0; e < 4; ++e) p[mb][e] = fast_exp2(__builtin_fmaf(x[nt][mb][e], sl2, -m_new));
       // P^T operand in the value reads' row order (see pv_off): pack even
       // and odd rows of each half, then one swap of lanes 32..63 of the even
       // pairs with lanes 0..31 of the odd pairs
@@ -371,9 +398,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
       const auto hi = __builtin_amdgcn_permlane32_swap(M::pack2(p[1][0], p[1][2]),
                                                        M::pack2(p[1][1], p[1][3]), false, false);
       pb[nt] = make_uint4(lo[0], lo[1], hi[0], hi[1]);
-      if (__any(alpha != 1.f)) {
+    }
+    // schedule of the block: the key-tile reads first, then one MFMA per
+    // five VALU instructions
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
 #pragma unroll
-        for (int b = 0; b < DB; ++b) o[nt][b] *= alpha;
+    for (int i = 0; i < 4 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[nt][b] *= alpha[nt];
+        lacc[nt] *= alpha[nt];
       }
     }
 
@@ -387,15 +426,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
       o[0][b] = M::qk(va, pb[0], o[0][b]);
       o[1][b] = M::qk(va, pb[1], o[1][b]);
     }
+    lacc[0] = M::qk(ones, pb[0], lacc[0]);
+    lacc[1] = M::qk(ones, pb[1], lacc[1]);
     // refill the stage of tile kt-1 (every wave passed this iteration's
     // barrier, so none still reads it)
     if (kt + kStages - 1 < n_tiles) issue(kt + kStages - 1);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) s[mb][nt] = s_next[mb][nt];
   }
 
   // normalise and write: lane holds O^T[d = 16b + 4j + e][q-row c16]
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const float l_tot = rows4_sum(lsum[nt]);
+    const float l_tot = lacc[nt][0];  // every row of the ones block holds the sum
     if (!row_ok[nt]) continue;
     const uint32_t r = 32u * wv + 16u * nt + c16;
     const uint32_t qq = r / grp, h = r % grp;
