@@ -323,3 +323,49 @@ def test_prefill_tiles_page_sizes(causal, ps):
                      causal=causal)
     assert_close(run(wl), expected(wl), torch.bfloat16, f"prefill ps={ps}")
     assert_close(run(wl, splits=3), expected(wl), torch.bfloat16, f"prefill ps={ps} split")
+
+
+def test_graph_capture_mixed_prefill_and_decode():
+    """A plan with prefill tiles, decode rows and a split merge, captured once
+    into a graph and replayed after rebinding shorter priors and lengths
+    (tile order and table lookups change), with eager work in between: every
+    replay equals an eager call bit for bit and the oracle within
+    tolerance."""
+    chunks = [(200, 40), (90, 24)]
+    dec_lens = [500, 77, 1200]
+    wl = _prefill_wl(torch.bfloat16, 32, 8, 128, 16, chunks, dec_lens, seed=97)
+    dev = to_dev(wl)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        plan = make_plan(wl, stream=s)
+        assert plan.n_tiles > 0 and plan.n_rows > 0
+        ws = pkv.Workspace(wl.queries, 32, 128, 3, stream=s)
+        out = torch.empty(wl.queries, 32, 128, dtype=torch.bfloat16, device="cuda")
+        eager = torch.empty_like(out)
+        pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, True, workspace=ws, out=out)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, True, workspace=ws,
+                          out=out)
+        n_chunk = sum(c for _, c in chunks)
+        for step in range(3):
+            shift = 30 * step
+            new_chunks = [(p - shift, c) for p, c in chunks]
+            new_dec = [L - 7 * step for L in dec_lens]
+            lens = np.array([p + c for p, c in new_chunks] + new_dec)
+            qpos = np.concatenate([np.arange(p, p + c) for p, c in new_chunks] +
+                                  [np.array(new_dec) - 1])
+            plan.rebind(lens, wl.qseq, qpos, wl.table)
+            g.replay()
+            s.synchronize()
+            got = out.double().cpu().numpy()
+            # eager call on the same plan, then some unrelated eager work
+            pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, True, workspace=ws,
+                          out=eager)
+            s.synchronize()
+            _ = (dev["q"] * 2).sum().item()
+            np.testing.assert_array_equal(got, eager.double().cpu().numpy())
+            wl.lens, wl.qpos = lens, qpos
+            assert_close(got, expected(wl), wl.dtype, f"mixed replay {step}")
+            assert qpos.shape[0] == n_chunk + len(dec_lens)
