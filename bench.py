@@ -57,14 +57,25 @@ def _parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    p.add_argument("--splits", type=int, default=0,
-                   help="0: measured choice (pkv.tune_splits); -1: pkv.suggest_splits")
+    p.add_argument("--splits", default="tune",
+                   help="tune: measured choice (pkv.tune_splits, balanced schedule included); "
+                        "suggest: pkv.suggest_splits; balanced: balanced workspace; N: N parts")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--copy-probe", action="store_true")
     return p.parse_args()
+
+
+def _fixed_splits(arg: str) -> int:
+    """'balanced' -> 0 (balanced workspace), else a part count >= 1."""
+    if arg == "balanced":
+        return 0
+    n = int(arg)
+    if n < 1:
+        raise SystemExit("--splits takes tune, suggest, balanced or a count >= 1")
+    return n
 
 
 def decode_source_hash() -> str:
@@ -150,7 +161,7 @@ def prefill_measure(torch, pkv, workloads, steps: int):
     hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
     out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
     splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
-    ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
+    ws = pkv.Workspace.for_splits(wl.queries, hq, dv, splits)
 
     def step():
         pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws, out=out)
@@ -207,13 +218,13 @@ def main():
     if wl.kind == "attention":
         hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
         out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
-        if args.splits > 0:
-            splits = args.splits
-        elif args.splits < 0:
+        if args.splits == "tune":
+            splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
+        elif args.splits == "suggest":
             splits = pkv.suggest_splits(plan, hq, hkv, dv)
         else:
-            splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
-        ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
+            splits = _fixed_splits(args.splits)
+        ws = pkv.Workspace.for_splits(wl.queries, hq, dv, splits)
         main_kernel = "tiles" if wl.info.get("prefill_queries") else "rows"
 
         def step():
@@ -222,14 +233,14 @@ def main():
     else:
         h, r = wl.info["h"], wl.info["r"]
         out = torch.empty(wl.queries, h, r, dtype=wl.dtype, device="cuda")
-        if args.splits > 0:
-            splits = args.splits
-        elif args.splits < 0:
-            splits = pkv.suggest_splits(plan, h, 1, r)
-        else:
+        if args.splits == "tune":
             splits = pkv.tune_splits_mla(plan, dev["q_abs"], dev["q_pos"], dev["latent"],
                                          dev["k_pos"], wl.scale, wl.causal, out=out)
-        ws = pkv.Workspace(wl.queries, h, r, splits) if splits > 1 else None
+        elif args.splits == "suggest":
+            splits = pkv.suggest_splits(plan, h, 1, r)
+        else:
+            splits = _fixed_splits(args.splits)
+        ws = pkv.Workspace.for_splits(wl.queries, h, r, splits)
         main_kernel = "mla"
 
         def step():
@@ -280,7 +291,8 @@ def main():
         "vs_baseline": None,
         "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[wl.dtype],
         "data": "synthetic (seeded N(0,1) Q/K/V, shuffled pages)",
-        "config": {"workload": wl.name, "queries": wl.queries, "splits": splits,
+        "config": {"workload": wl.name, "queries": wl.queries,
+                   "splits": "balanced" if splits == 0 else splits,
                    "kv_bytes_per_step": nbytes, "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": kernels,

@@ -158,6 +158,29 @@ void pkv_plan_destroy(pkv_plan *plan);
 pkv_status pkv_workspace_create(uint32_t queries, uint32_t heads, uint32_t dv,
                                 uint32_t splits, void *stream,
                                 pkv_workspace **out);
+
+/* Balanced workspace (this library's schedule; the page's split workspace
+ * fixes a part count instead).  pkv_attention with it runs the row queries
+ * on the MFMA decode kernel in a balanced schedule: the tile positions (16
+ * visible keys) of all row queries, query after query, are cut into equal
+ * contiguous ranges, one per group of waves that attend the same keys for
+ * the KV heads (and 16-head groups) of the call, so every wave streams the
+ * same number of tiles whatever the length mix, and the heads of a page are
+ * read side by side.  The f32 partials of the pieces a range boundary cuts
+ * (two 16-head slots per wave) are merged by a second kernel.  Memory:
+ * 2 * waves * 16 * (dv + 1) f32 + (2 * queries + 1) u32, waves = CUs *
+ * resident waves per CU (about 17 MB at dv = 128 on 256 CUs).  Calls whose
+ * rows the MFMA decode kernel does not take (f32, head dims other than
+ * 64/128/256 or head_dim != value_dim, pkv_mla, 2^31 or more tile
+ * positions, more KV heads x 16-head groups than waves) run unsplit with
+ * it.  Same sharing rules as a split workspace: calls that overlap on one
+ * workspace race.  Errors: PKV_EINVAL (a zero dimension, null out),
+ * PKV_ERANGE (above PKV_WORKSPACE_LIMIT_BYTES), PKV_EHIP. */
+pkv_status pkv_workspace_create_balanced(uint32_t queries, uint32_t heads,
+                                         uint32_t dv, void *stream,
+                                         pkv_workspace **out);
+
+/* Split count of a workspace; 0 for a balanced workspace or NULL. */
 uint32_t pkv_workspace_splits(const pkv_workspace *ws);
 void pkv_workspace_destroy(pkv_workspace *ws);
 
@@ -175,7 +198,9 @@ uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads,
  * to W, PKV_MAX_SPLITS and the workspace limit) `reps` times after one
  * warm-up call, times each candidate with HIP events on `stream`, and
  * writes the fastest count to *splits (a count with more splits must be
- * more than 2% faster to win).  Uses a temporary workspace of its own;
+ * more than 2% faster to win).  The balanced schedule is the last
+ * candidate, reported as 0 (it too must be more than 2% faster than the
+ * best count before it).  Uses temporary workspaces of its own;
  * `out` receives the attention result.  Synchronises the stream; not for
  * use under graph capture.  Errors: those of pkv_attention, PKV_EINVAL for
  * a null plan or splits, PKV_EHIP. */
@@ -185,7 +210,7 @@ pkv_status pkv_tune_splits(const pkv_plan *plan, pkv_dtype dtype, const void *q,
                            uint32_t value_dim, float scale, int causal,
                            uint32_t reps, void *stream, uint32_t *splits);
 
-/* The same for pkv_mla. */
+/* The same for pkv_mla (split counts only). */
 pkv_status pkv_tune_splits_mla(const pkv_plan *plan, pkv_dtype dtype,
                                const void *q_abs, const void *q_pos,
                                const void *latent, const void *k_pos, void *out,

@@ -180,15 +180,29 @@ class Plan:
 
 class Workspace:
     """f32 split partials for ``splits`` parts; reusable across plans with the
-    same queries, heads and value dim on the same stream."""
+    same queries, heads and value dim on the same stream.  ``splits=0`` makes
+    a balanced workspace (pkv_workspace_create_balanced): the row queries'
+    tiles are cut into equal ranges, one per resident wave."""
 
     def __init__(self, queries: int, heads: int, dv: int, splits: int, stream=None):
         self.stream = _stream_handle(stream)
         self.queries, self.heads, self.dv, self.splits = int(queries), int(heads), int(dv), int(splits)
         h = ctypes.c_void_p()
-        check(lib().pkv_workspace_create(self.queries, self.heads, self.dv, self.splits,
-                                         ctypes.c_void_p(self.stream), ctypes.byref(h)))
+        if self.splits == 0:
+            check(lib().pkv_workspace_create_balanced(self.queries, self.heads, self.dv,
+                                                      ctypes.c_void_p(self.stream), ctypes.byref(h)))
+        else:
+            check(lib().pkv_workspace_create(self.queries, self.heads, self.dv, self.splits,
+                                             ctypes.c_void_p(self.stream), ctypes.byref(h)))
         self._h = h
+
+    @classmethod
+    def for_splits(cls, queries: int, heads: int, dv: int, splits: int, stream=None):
+        """Workspace for a split choice as pkv_tune_splits reports it: None for
+        1 (unsplit), balanced for 0, else ``splits`` parts."""
+        if splits == 1:
+            return None
+        return cls(queries, heads, dv, splits, stream=stream)
 
     @property
     def handle(self):
@@ -217,7 +231,8 @@ def suggest_splits(plan: Plan, q_heads: int, kv_heads: int, value_dim: int) -> i
 def tune_splits(plan: Plan, q, k, v, scale: float, causal: bool = True, out=None,
                 reps: int = 5) -> int:
     """Fastest split count for this call, measured on these tensors
-    (pkv_tune_splits); synchronises the plan's stream."""
+    (pkv_tune_splits): 0 means the balanced schedule (``Workspace.for_splits``
+    turns the answer into a workspace); synchronises the plan's stream."""
     qn, hq, d = q.shape
     hkv, dv = k.shape[2], v.shape[3]
     if out is None:

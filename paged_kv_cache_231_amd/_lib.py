@@ -35,6 +35,7 @@ SIGNATURES = {
     "pkv_plan_device_words": (_p, [_p]),
     "pkv_plan_destroy": (None, [_p]),
     "pkv_workspace_create": (_i, [_u32, _u32, _u32, _u32, _p, ctypes.POINTER(_p)]),
+    "pkv_workspace_create_balanced": (_i, [_u32, _u32, _u32, _p, ctypes.POINTER(_p)]),
     "pkv_workspace_splits": (_u32, [_p]),
     "pkv_workspace_destroy": (None, [_p]),
     "pkv_suggest_splits": (_u32, [_p, _u32, _u32, _u32]),

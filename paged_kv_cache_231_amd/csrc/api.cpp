@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -35,9 +36,14 @@ struct pkv_plan {
 struct pkv_workspace {
   int device = -1;
   hipStream_t stream = nullptr;
-  uint32_t queries = 0, heads = 0, dv = 0, splits = 0;
+  uint32_t queries = 0, heads = 0, dv = 0, splits = 0;  // splits 0: balanced
   float *buf = nullptr;
   size_t bytes = 0;
+  // balanced schedule: up to max_waves wave ranges (two 16-row slots each),
+  // then {first tile, tiles} per query and the total
+  uint32_t max_waves = 0, cus = 0;
+  float *slot_lse = nullptr;
+  uint32_t *rec = nullptr;
 };
 
 namespace pkv {
@@ -135,10 +141,73 @@ class Timed {
   bool on_ = false;
 };
 
+// Waves per CU of a balanced launch: one per SIMD.  Fewer concurrent page
+// streams keep more DRAM rows open; 8 or 12 waves per CU measured slower.
+constexpr uint32_t kBalancedWavesPerCu = 4;
+
+// Resident waves per CU of the balanced kernel, cached per (dtype, d, page
+// uniformity); 0 for shapes it does not take.
+int bal_waves_per_cu(uint32_t d, uint32_t ps, pkv_dtype dt) {
+  if (dt != PKV_F16 && dt != PKV_BF16) return 0;
+  const int di = d == 64 ? 0 : d == 128 ? 1 : d == 256 ? 2 : -1;
+  if (di < 0) return 0;
+  const int pu = (ps & (ps - 1)) == 0 && ps >= 16u ? 1 : 0;
+  static std::atomic<int> cache[2][3][2];
+  std::atomic<int> &c = cache[dt == PKV_BF16][di][pu];
+  int v = c.load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = balanced_waves_per_cu(d, ps, dt);
+    c.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Waves of a balanced launch, or 0 when the call cannot use the balanced
+// schedule (then the rows run unsplit).
+uint32_t balanced_waves(const RowArgs &ra, pkv_dtype dt, const pkv_workspace *ws) {
+  if (!ws || ws->splits != 0 || ws->max_waves == 0 || ra.pdim != 0) return 0;
+  if (!rows_mfma_supported(ra, dt)) return 0;
+  // every tile number and k * (tiles per group) must stay below 2^31
+  const uint64_t grp = ra.hq / ra.hkv;
+  const uint64_t segq = uint64_t(ra.hkv) * ((grp + 15) / 16);
+  const uint64_t max_tiles = (uint64_t(ra.plan.W) * ra.plan.ps + 15) / 16;
+  if (uint64_t(ra.n_queries) * max_tiles >= (1ull << 31)) return 0;
+  const uint64_t per_cu = std::min<uint64_t>(kBalancedWavesPerCu, bal_waves_per_cu(ra.d, ra.plan.ps, dt));
+  uint64_t w = std::min<uint64_t>(ws->max_waves, per_cu * ws->cus);
+  w -= w % 4;
+  if (segq > w) return 0;  // not one group of segq waves
+  return uint32_t(w);
+}
+
 // Launches the row kernel (and the merge when split) over `qlist`.
 pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_workspace *ws,
                     hipStream_t st) {
   hipError_t e;
+  ra.bal_waves = balanced_waves(ra, dt, ws);
+  if (ra.bal_waves) {
+    {
+      Timed t(plan, PKV_KERNEL_ROWS, st);
+      e = launch_rows_balanced(ra, dt, st);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    MergeArgs ma{};
+    ma.plan = ra.plan;
+    ma.qlist = ra.qlist;
+    ma.n_queries = ra.n_queries;
+    ma.hq = ra.hq;
+    ma.hkv = ra.hkv;
+    ma.dv = ra.dv;
+    ma.splits = 1;
+    ma.pages_per_split = ra.pages_per_split;
+    ma.causal = ra.causal;
+    ma.ws_o = ra.ws_o;
+    ma.ws_lse = ra.ws_lse;
+    ma.out = ra.out;
+    ma.bal_rec = ra.bal_rec;
+    ma.bal_waves = ra.bal_waves;
+    Timed t(plan, PKV_KERNEL_MERGE, st);
+    return hip_fail(launch_merge_balanced(ma, dt, st));
+  }
   if (ra.pdim != 0 && mla_mfma_supported(ra, dt)) {
     if (mla_mfma_blocks(ra) > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
     Timed t(plan, PKV_KERNEL_MLA, st);
@@ -160,11 +229,12 @@ pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_wo
   }
   if (e != hipSuccess) return hip_fail(e);
   if (ws && ra.splits > 1) {
-    MergeArgs ma;
+    MergeArgs ma{};
     ma.plan = ra.plan;
     ma.qlist = ra.qlist;
     ma.n_queries = ra.n_queries;
     ma.hq = ra.hq;
+    ma.hkv = ra.hkv;
     ma.dv = ra.dv;
     ma.splits = ra.splits;
     ma.pages_per_split = ra.pages_per_split;
@@ -180,11 +250,18 @@ pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_wo
 }
 
 void fill_split(RowArgs *ra, const pkv_plan *plan, pkv_workspace *ws) {
-  const uint32_t splits = ws ? ws->splits : 1u;
+  // a balanced workspace runs the kernels without a balanced schedule unsplit
+  const uint32_t splits = ws && ws->splits ? ws->splits : 1u;
   ra->splits = splits;
   const uint32_t W = plan->L.W ? plan->L.W : 1u;
   ra->pages_per_split = W / splits + (W % splits != 0);
-  if (ws && splits > 1) {
+  ra->bal_rec = nullptr;
+  ra->bal_waves = 0;
+  if (ws && ws->splits == 0) {
+    ra->ws_o = ws->buf;
+    ra->ws_lse = ws->slot_lse;
+    ra->bal_rec = ws->rec;
+  } else if (ws && splits > 1) {
     ra->ws_o = ws->buf;
     ra->ws_lse = ws->buf + uint64_t(ws->queries) * splits * ws->heads * ws->dv;
   } else {
@@ -347,6 +424,46 @@ pkv_status pkv_workspace_create(uint32_t queries, uint32_t heads, uint32_t dv, u
     delete w;
     return fail(PKV_EHIP, "hipMalloc of workspace failed");
   }
+  *out = w;
+  return PKV_OK;
+}
+
+pkv_status pkv_workspace_create_balanced(uint32_t queries, uint32_t heads, uint32_t dv,
+                                         void *stream, pkv_workspace **out) {
+  clear_error();
+  if (!out) return fail(PKV_EINVAL, "out must not be null");
+  *out = nullptr;
+  if (queries == 0 || heads == 0 || dv == 0) return fail(PKV_EINVAL, "workspace dimensions must be positive");
+  int dev = -1, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PKV_EHIP, "hipGetDevice failed");
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return fail(PKV_EHIP, "hipDeviceGetAttribute failed");
+  // the most waves a balanced launch uses for any page size or half-precision type
+  uint32_t per_cu = 0;
+  for (pkv_dtype dt : {PKV_F16, PKV_BF16})
+    for (uint32_t ps : {16u, 3u})
+      per_cu = std::max<uint32_t>(per_cu, uint32_t(bal_waves_per_cu(dv, ps, dt)));
+  per_cu = std::min(per_cu, kBalancedWavesPerCu);
+  const uint64_t waves = uint64_t(per_cu) * uint32_t(cus);
+  const uint64_t rows = 2 * waves * 16;  // two 16-head slots per wave
+  const uint64_t bytes = rows * (uint64_t(dv) + 1) * sizeof(float) + (2 * uint64_t(queries) + 1) * 4;
+  if (bytes > PKV_WORKSPACE_LIMIT_BYTES) return fail(PKV_ERANGE, "workspace above PKV_WORKSPACE_LIMIT_BYTES");
+  auto *w = new pkv_workspace;
+  w->device = dev;
+  w->stream = static_cast<hipStream_t>(stream);
+  w->queries = queries;
+  w->heads = heads;
+  w->dv = dv;
+  w->splits = 0;
+  w->max_waves = uint32_t(waves);
+  w->cus = uint32_t(cus);
+  w->bytes = size_t(bytes);
+  if (hipMalloc(&w->buf, w->bytes) != hipSuccess) {
+    delete w;
+    return fail(PKV_EHIP, "hipMalloc of workspace failed");
+  }
+  w->slot_lse = w->buf + rows * dv;
+  w->rec = reinterpret_cast<uint32_t *>(w->slot_lse + rows);
   *out = w;
   return PKV_OK;
 }
@@ -606,7 +723,7 @@ namespace {
 // fewer splits win unless another count is more than 2% faster.
 template <class Call>
 pkv_status tune_splits(const pkv_plan *plan, uint32_t heads, uint32_t dv, uint32_t reps,
-                       hipStream_t stream, Call call, uint32_t *best_out) {
+                       hipStream_t stream, bool try_balanced, Call call, uint32_t *best_out) {
   const PlanLayout &L = plan->L;
   *best_out = 1;
   if (L.Q == 0 || L.W == 0) return PKV_OK;
@@ -648,11 +765,31 @@ pkv_status tune_splits(const pkv_plan *plan, uint32_t heads, uint32_t dv, uint32
       *best_out = c;
     }
   }
+  // the balanced schedule, reported as 0
+  pkv_workspace *bw = nullptr;
+  if (st == PKV_OK && try_balanced)
+    st = pkv_workspace_create_balanced(L.Q, heads, dv, stream, &bw);
+  if (st == PKV_OK && bw) {
+    st = call(bw);
+    float ms = 0.f;
+    if (st == PKV_OK) {
+      if (hipEventRecord(e0, stream) != hipSuccess) st = fail(PKV_EHIP, "hipEventRecord failed");
+      for (uint32_t r = 0; r < reps && st == PKV_OK; ++r) st = call(bw);
+      if (st == PKV_OK && (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                           hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+        st = fail(PKV_EHIP, "timing the candidates failed");
+    }
+    if (st == PKV_OK && ms < best_ms * 0.98f) {
+      best_ms = ms;
+      *best_out = 0;
+    }
+  }
   if (hipStreamSynchronize(stream) != hipSuccess && st == PKV_OK) st = fail(PKV_EHIP, "hipStreamSynchronize failed");
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
   if (ws.buf) (void)hipFree(ws.buf);
   ws.buf = nullptr;
+  pkv_workspace_destroy(bw);
   return st;
 }
 
@@ -666,7 +803,7 @@ pkv_status pkv_tune_splits(const pkv_plan *plan, pkv_dtype dtype, const void *q,
                            uint32_t reps, void *stream, uint32_t *splits) {
   clear_error();
   if (!plan || !splits) return fail(PKV_EINVAL, "null argument");
-  return tune_splits(plan, q_heads, value_dim, reps, static_cast<hipStream_t>(stream),
+  return tune_splits(plan, q_heads, value_dim, reps, static_cast<hipStream_t>(stream), true,
                      [&](pkv_workspace *ws) {
                        return pkv_attention(plan, dtype, q, k, v, out, q_heads, kv_heads, head_dim,
                                             value_dim, scale, causal, ws, stream);
@@ -680,7 +817,7 @@ pkv_status pkv_tune_splits_mla(const pkv_plan *plan, pkv_dtype dtype, const void
                                int causal, uint32_t reps, void *stream, uint32_t *splits) {
   clear_error();
   if (!plan || !splits) return fail(PKV_EINVAL, "null argument");
-  return tune_splits(plan, heads, rank, reps, static_cast<hipStream_t>(stream),
+  return tune_splits(plan, heads, rank, reps, static_cast<hipStream_t>(stream), false,
                      [&](pkv_workspace *ws) {
                        return pkv_mla(plan, dtype, q_abs, q_pos, latent, k_pos, out, heads, rank,
                                       pos_dim, scale, causal, ws, stream);

@@ -62,15 +62,18 @@ struct TileRegs {
 // power of two >= 16) every tile lies inside one page; the page numbers of
 // up to 64 consecutive tiles of the wave are held one per lane and read with
 // readlane, so the token loop issues no table loads.
+// The wave's k-th tile starts at token t_lo + 16 (first + step k): step 4
+// when the four waves of a block interleave over one range, 1 when a wave
+// owns a contiguous range.
 template <bool PAGE_UNIFORM>
 struct TileMap {
   const uint32_t *table;
-  uint32_t t_lo, t_hi, wv, ps, ps_shift, n_pages_pool;
+  uint32_t t_lo, t_hi, first, step, ps, ps_shift, n_pages_pool;
   uint32_t lane_page;  // page of tile (base + lane)
   uint32_t base;       // first tile held in lane_page
 
   __device__ __forceinline__ uint32_t tile_start(uint32_t k) const {
-    return t_lo + (wv + 4u * k) * 16u;
+    return t_lo + (first + step * k) * 16u;
   }
   __device__ __forceinline__ void fill(uint32_t k0, uint32_t lane) {
     base = k0;
@@ -203,6 +206,83 @@ __device__ __forceinline__ void attend_tile(WaveState<D> &st, const TileRegs<D> 
   for (int b = 0; b < DB; ++b) st.o[b] = M::pv(lds_read_tr16(vrow + 32 * b), pb, st.o[b]);
 }
 
+// Q^T of heads h0 .. h0 + nh - 1 of query i as the B operand of q.k:
+// column = head c16, K-slot chunk 4 ks + j; absent heads are zero.
+template <class DT, int D>
+__device__ __forceinline__ void load_q(uint4 (&qb)[D / 32], const RowArgs &a, uint32_t i,
+                                       uint32_t h0, uint32_t nh, uint32_t lane) {
+  const uint32_t c16 = lane & 15u, j = lane >> 4;
+  const typename DT::T *qrow =
+      static_cast<const typename DT::T *>(a.q) + (uint64_t(i) * a.hq + h0 + c16) * D;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qb[ks] = c16 < nh ? *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j))
+                      : make_uint4(0, 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void reset_state(WaveState<D> &st) {
+#pragma unroll
+  for (int b = 0; b < D / 16; ++b) st.o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = kNoMax;
+  st.lsum = 0.f;
+}
+
+// Attends the wave's n_tiles tiles of `map` with a software pipeline, two
+// tiles in flight: while one tile is attended the next one's loads run.  The
+// steady-state loop issues its loads unconditionally, so the wait before
+// each tile covers only that tile's loads; page numbers are refilled once
+// per 64 tiles, outside the loop.
+template <class DT, int D, bool PU>
+__device__ __forceinline__ void stream_tiles(WaveState<D> &st, TileMap<PU> &map,
+                                             uint32_t n_tiles, const RowArgs &a,
+                                             const typename DT::T *kbase,
+                                             const typename DT::T *vbase, const uint4 *qb,
+                                             unsigned char *vt, float sl2, uint32_t lane) {
+  TileRegs<D> ta, tb;
+  for (uint32_t c0 = 0; c0 < n_tiles; c0 += 64) {
+    const uint32_t cn = n_tiles - c0 < 64u ? n_tiles - c0 : 64u;
+    map.fill(c0, lane);
+    uint32_t k = 0;
+    if (cn >= 4) {
+      load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0, lane);
+      load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + 1, lane);
+      for (; k + 3 < cn; k += 2) {
+        attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
+        load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
+        attend_tile<DT, D>(st, tb, qb, vt, sl2, lane);
+        load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + k + 3, lane);
+      }
+    } else {
+      load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0, lane);
+      if (cn > 1) load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + 1, lane);
+    }
+    // at most three tiles left: k in ta, k + 1 in tb
+    if (k < cn) {
+      attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
+      if (k + 2 < cn) load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
+    }
+    if (k + 1 < cn) attend_tile<DT, D>(st, tb, qb, vt, sl2, lane);
+    if (k + 2 < cn) attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
+  }
+}
+
+template <bool PU>
+__device__ __forceinline__ void init_map(TileMap<PU> &map, const RowArgs &a, uint32_t seq,
+                                         uint32_t t_lo, uint32_t t_hi, uint32_t first,
+                                         uint32_t step) {
+  const uint32_t ps = a.plan.ps;
+  map.table = a.plan.words + a.plan.table + uint64_t(seq) * a.plan.W;
+  map.t_lo = t_lo;
+  map.t_hi = t_hi;
+  map.first = first;
+  map.step = step;
+  map.ps = ps;
+  const bool pow2 = (ps & (ps - 1)) == 0;
+  map.ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 32u;
+  map.n_pages_pool = a.plan.N;
+}
+
 template <class DT, int D, bool PU>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
   using M = Mfma<DT>;
@@ -237,69 +317,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
   const uint32_t h0 = kvh * grp + sub * kHeads;               // first q head of the block
   const uint32_t nh = grp - sub * kHeads < kHeads ? grp - sub * kHeads : kHeads;
 
-  // Q^T as the B operand of q.k: column = head c16, K-slot chunk 4*ks + j.
   uint4 qb[KS];
-  {
-    const typename DT::T *qrow =
-        static_cast<const typename DT::T *>(a.q) + (uint64_t(i) * a.hq + h0 + c16) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qb[ks] = c16 < nh ? *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j))
-                        : make_uint4(0, 0, 0, 0);
-  }
-
+  load_q<DT, D>(qb, a, i, h0, nh, lane);
   WaveState<D> st;
-#pragma unroll
-  for (int b = 0; b < DB; ++b) st.o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = kNoMax;
-  st.lsum = 0.f;
+  reset_state<D>(st);
 
   const typename DT::T *kbase = static_cast<const typename DT::T *>(a.k) + uint64_t(kvh) * D;
   const typename DT::T *vbase = static_cast<const typename DT::T *>(a.v) + uint64_t(kvh) * D;
   unsigned char *vt = lds + wv * L::kTileBytes;  // this wave's V tile
   TileMap<PU> map;
-  map.table = a.plan.words + a.plan.table + uint64_t(seq) * a.plan.W;
-  map.t_lo = t_lo;
-  map.t_hi = t_hi;
-  map.wv = wv;
-  map.ps = ps;
-  const bool pow2 = (ps & (ps - 1)) == 0;
-  map.ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 32u;
-  map.n_pages_pool = a.plan.N;
+  init_map<PU>(map, a, seq, t_lo, t_hi, wv, 4u);
   const uint32_t first = t_lo + wv * 16u;
   const uint32_t n_tiles = first < t_hi ? (t_hi - first + 63u) / 64u : 0u;
-  const float sl2 = a.scale_log2;
-
-  // Software pipeline, two tiles in flight: while one tile is attended the
-  // next one's loads run.  The steady-state loop issues its loads
-  // unconditionally, so the wait before each tile covers only that tile's
-  // loads; page numbers are refilled once per 64 tiles, outside the loop.
-  TileRegs<D> ta, tb;
-  for (uint32_t c0 = 0; c0 < n_tiles; c0 += 64) {
-    const uint32_t cn = n_tiles - c0 < 64u ? n_tiles - c0 : 64u;
-    map.fill(c0, lane);
-    uint32_t k = 0;
-    if (cn >= 4) {
-      load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0, lane);
-      load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + 1, lane);
-      for (; k + 3 < cn; k += 2) {
-        attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
-        load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
-        attend_tile<DT, D>(st, tb, qb, vt, sl2, lane);
-        load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + k + 3, lane);
-      }
-    } else {
-      load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0, lane);
-      if (cn > 1) load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + 1, lane);
-    }
-    // at most three tiles left: k in ta, k + 1 in tb
-    if (k < cn) {
-      attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
-      if (k + 2 < cn) load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
-    }
-    if (k + 1 < cn) attend_tile<DT, D>(st, tb, qb, vt, sl2, lane);
-    if (k + 2 < cn) attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
-  }
+  stream_tiles<DT, D, PU>(st, map, n_tiles, a, kbase, vbase, qb, vt, a.scale_log2, lane);
 
   // per-head sum over the four lane groups (m is already uniform across them)
   const float lsum = rows4_sum(st.lsum);
@@ -341,6 +371,251 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced schedule.  With the block-per-part grid above, the work of a CU
+// is whatever lengths its resident blocks happen to draw, and the kernel
+// lasts as long as the busiest CU.  Here the row queries' 16-key tiles are
+// numbered query after query (one number per tile position, shared by the
+// query's segq = KV heads x 16-head groups segments) and cut into equal
+// contiguous ranges, one per group of segq consecutive waves; wave g of a
+// group attends segment g over its group's range.  Every wave so streams the
+// same number of tiles, and the segq waves that read the same cache pages
+// (one KV head each) run side by side, which keeps DRAM rows open for all
+// heads of a page.  Each wave finds its range from a prefix of the tile
+// counts it computes itself; wave 0 also stores, per row query, its first
+// tile and tile count for the merge.  A range is a list of pieces, one per
+// query it touches.  A piece that is a whole query writes the output
+// directly.  A piece cut by a range boundary writes f32 partials (normalised
+// o and lse) to a slot: slot 2w when it is the first piece of wave w and
+// its query began in an earlier range, else slot 2w + 1 (its query goes on
+// into the next range).  A second, small kernel merges the cut pieces.
+
+// Tiles of 16 keys of row query r.
+__device__ __forceinline__ uint32_t row_tiles(const RowArgs &a, uint32_t r) {
+  const uint32_t i = a.qlist ? a.qlist[r] : r;
+  uint32_t seq;
+  return ceil_div_u(visible_keys(a.plan, i, a.causal, &seq), 16u);
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= uint32_t(o)) x += y;
+  }
+  return x;
+}
+
+// Tile prefix over 64 consecutive row queries base .. base + 63: lane l
+// holds v = tiles of query base + l (0 past the end) and excl = first tile
+// of that query; end = first tile after the chunk.
+struct Chunk {
+  uint32_t base, end;
+  uint32_t v, excl;
+};
+
+__device__ __forceinline__ void scan_chunk(Chunk &c, const RowArgs &a, uint32_t base,
+                                           uint32_t carry, uint32_t lane) {
+  const uint32_t r = base + lane;
+  const uint32_t v = r < a.n_queries ? row_tiles(a, r) : 0u;
+  const uint32_t x = wave_incl_scan(v, lane);
+  c.base = base;
+  c.v = v;
+  c.excl = carry + x - v;
+  c.end = carry + __builtin_amdgcn_readlane(x, 63);
+}
+
+// Launched with one block of four waves per CU (one wave per SIMD): fewer
+// concurrent page streams keep more DRAM rows open, and more waves per CU
+// or a third tile in flight per wave measured no faster.
+template <class DT, int D, bool PU>
+__global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
+  using M = Mfma<DT>;
+  constexpr int KS = D / 32;
+  constexpr int DB = D / 16;
+  using L = Lds<D>;
+  __shared__ __align__(16) unsigned char lds[kWaves * L::kTileBytes];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t c16 = lane & 15u, j = lane >> 4;
+  const uint32_t grp = a.hq / a.hkv;
+  const uint32_t hgk = (grp + kHeads - 1) / kHeads;
+  const uint32_t segq = a.hkv * hgk;
+  const uint32_t groups = a.bal_waves / segq;  // >= 1 (checked by the host)
+  const uint32_t w = blockIdx.x * kWaves + wv;
+  const uint32_t grp_k = w / segq, g = w % segq;
+  if (grp_k >= groups) return;
+  const uint32_t R = a.n_queries;
+
+  // Total tiles T and the super-chunk of row queries holding this group's
+  // first tile: chunks of 64 queries (coalesced loads, one wave sum each);
+  // lane l adds up chunks l*m .. l*m + m - 1.
+  const uint32_t nch = (R + 63u) / 64u;
+  const uint32_t m = (nch + 63u) / 64u;
+  uint32_t s = 0, carry = 0;
+  for (uint32_t c = 0; c < nch; ++c) {
+    const uint32_t r = c * 64u + lane;
+    const uint32_t v = r < R ? row_tiles(a, r) : 0u;
+    const uint32_t x = wave_incl_scan(v, lane);
+    const uint32_t tot = __builtin_amdgcn_readlane(x, 63);
+    if (c / m == lane) s += tot;
+    if (w == 0u && r < R) {  // {first tile, tiles} of every row query, for the merge
+      a.bal_rec[2u * r] = carry + x - v;
+      a.bal_rec[2u * r + 1u] = v;
+    }
+    carry += tot;
+  }
+  const uint32_t sx = wave_incl_scan(s, lane);
+  const uint32_t T = __builtin_amdgcn_readlane(sx, 63);
+  if (w == 0u && lane == 0u) a.bal_rec[2u * R] = T;
+  const uint32_t tpg = T / groups + (T % groups != 0u);
+  // tpg * groups < T + groups <= 2^31 + groups: no overflow (checked by the host)
+  uint32_t t = grp_k * tpg;
+  if (t >= T) return;
+  const uint32_t t_w0 = t;
+  const uint32_t t_end = T - t < tpg ? T : t + tpg;
+
+  // super-chunk lane: the last one starting at or before t (its sum is > 0)
+  const uint64_t sel = __ballot(sx - s <= t);
+  const uint32_t lb = 63u - uint32_t(__builtin_clzll(sel));
+  Chunk ch;
+  scan_chunk(ch, a, lb * m * 64u, __builtin_amdgcn_readlane(sx - s, lb), lane);
+  while (ch.end <= t) scan_chunk(ch, a, ch.base + 64u, ch.end, lane);
+  uint32_t qi = ch.base + 63u - uint32_t(__builtin_clzll(__ballot(ch.excl <= t)));
+
+  unsigned char *vt = lds + wv * L::kTileBytes;
+  const uint32_t kvh = g / hgk, sub = g % hgk;
+  const uint32_t h0 = kvh * grp + sub * kHeads;
+  const uint32_t nh = grp - sub * kHeads < kHeads ? grp - sub * kHeads : kHeads;
+  const typename DT::T *kbase = static_cast<const typename DT::T *>(a.k) + uint64_t(kvh) * D;
+  const typename DT::T *vbase = static_cast<const typename DT::T *>(a.v) + uint64_t(kvh) * D;
+
+  while (t < t_end) {
+    if (qi - ch.base >= 64u) scan_chunk(ch, a, ch.base + 64u, ch.end, lane);
+    const uint32_t li = qi - ch.base;
+    const uint32_t c0 = __builtin_amdgcn_readlane(ch.excl, li);
+    const uint32_t ntq = __builtin_amdgcn_readlane(ch.v, li);  // tiles of this query
+    if (c0 + ntq <= t) {  // a query with no tiles
+      ++qi;
+      continue;
+    }
+    const uint32_t tt0 = t - c0;
+    const uint32_t tt1 = ntq - tt0 < t_end - t ? ntq : tt0 + (t_end - t);
+    const uint32_t i = __builtin_amdgcn_readfirstlane(a.qlist ? a.qlist[qi] : qi);
+    uint32_t seq;
+    const uint32_t n = __builtin_amdgcn_readfirstlane(visible_keys(a.plan, i, a.causal, &seq));
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    const uint32_t t_hi = tt1 * 16u < n ? tt1 * 16u : n;
+
+    uint4 qb[KS];
+    load_q<DT, D>(qb, a, i, h0, nh, lane);
+    WaveState<D> st;
+    reset_state<D>(st);
+    TileMap<PU> map;
+    init_map<PU>(map, a, seq, tt0 * 16u, t_hi, 0u, 1u);
+    stream_tiles<DT, D, PU>(st, map, tt1 - tt0, a, kbase, vbase, qb, vt, a.scale_log2, lane);
+
+    const float lsum = rows4_sum(st.lsum);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (tt0 == 0u && tt1 == ntq) {
+      if (c16 < nh) {
+        uint16_t *orow = static_cast<uint16_t *>(a.out) + (uint64_t(i) * a.hq + h0 + c16) * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          uint2 v2;
+          v2.x = M::pack2(st.o[b][0] * inv, st.o[b][1] * inv);
+          v2.y = M::pack2(st.o[b][2] * inv, st.o[b][3] * inv);
+          *reinterpret_cast<uint2 *>(orow + 16 * b + 4 * j) = v2;
+        }
+      }
+    } else {
+      const uint32_t slot = (t == t_w0 && tt0 > 0u) ? 2u * w : 2u * w + 1u;
+      if (c16 < nh) {
+        const uint64_t row = uint64_t(slot) * kHeads + c16;
+        float *wo = a.ws_o + row * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) *reinterpret_cast<f32x4_t *>(wo + 16 * b + 4 * j) = st.o[b] * inv;
+        if (j == 0) a.ws_lse[row] = st.m + fast_log2(lsum);
+      }
+    }
+    t += tt1 - tt0;
+    if (tt1 == ntq) ++qi;
+  }
+}
+
+// Merge of the cut pieces of one (query, head): out = sum_p 2^(lse_p - M)
+// o_p / sum_p 2^(lse_p - M), M = max_p lse_p, over the slots of that head's
+// waves in the groups k0..k1 the query spans.  Queries inside one range
+// were written by the wave-range kernel; queries with no tiles get zeros.
+template <class DT>
+__global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
+  using T = typename DT::T;
+  __shared__ float s_w[256];
+  __shared__ float s_red[8];
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+  const uint32_t h = blockIdx.x % a.hq;
+  const uint32_t qi = blockIdx.x / a.hq;
+  const uint32_t grp = a.hq / a.hkv;
+  const uint32_t hgk = (grp + kHeads - 1) / kHeads;
+  const uint32_t segq = a.hkv * hgk;
+  const uint32_t g = (h / grp) * hgk + (h % grp) / kHeads, hl = (h % grp) % kHeads;
+  const uint32_t c0 = a.bal_rec[2u * qi], ntq = a.bal_rec[2u * qi + 1u];
+  const uint32_t total_tiles = a.bal_rec[2u * a.n_queries];
+  const uint32_t i = a.qlist ? a.qlist[qi] : qi;
+  T *out = static_cast<T *>(a.out) + (uint64_t(i) * a.hq + h) * a.dv;
+  if (ntq == 0u) {
+    for (uint32_t d = tid; d < a.dv; d += 256) out[d] = DT::from_f(0.f);
+    return;
+  }
+  const uint32_t groups = a.bal_waves / segq;
+  const uint32_t tpg = total_tiles / groups + (total_tiles % groups != 0u);
+  const uint32_t k0 = c0 / tpg, k1 = (c0 + ntq - 1u) / tpg;
+  if (k0 == k1) return;  // whole query in one range: already written
+  const uint32_t np = k1 - k0 + 1u;
+  // piece p: wave (k0 + p) segq + g; slot 2w + 1 for p = 0, else 2w
+  auto row_of = [&](uint32_t p) -> uint64_t {
+    const uint32_t w = (k0 + p) * segq + g;
+    const uint32_t slot = p == 0u ? 2u * w + 1u : 2u * w;
+    return uint64_t(slot) * kHeads + hl;
+  };
+
+  float mx = kNoMax;
+  for (uint32_t p = tid; p < np; p += 256) mx = fmaxf(mx, a.ws_lse[row_of(p)]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wv] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float ws = 0.f;
+  for (uint32_t p = tid; p < np; p += 256) ws += fast_exp2(a.ws_lse[row_of(p)] - mx);
+  ws = wave_sum(ws);
+  if (lane == 0) s_red[4 + wv] = ws;
+  __syncthreads();
+  const float total = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
+  const float inv = total > 0.f ? 1.f / total : 0.f;
+
+  // value elements d = tid, tid + 256, ... (dv <= 1024); pieces in chunks of
+  // 256 weights
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (uint32_t p0 = 0; p0 < np; p0 += 256) {
+    const uint32_t pc = np - p0 < 256u ? np - p0 : 256u;
+    __syncthreads();  // the previous chunk's weights are no longer read
+    s_w[tid] = tid < pc ? fast_exp2(a.ws_lse[row_of(p0 + tid)] - mx) : 0.f;
+    __syncthreads();
+    for (uint32_t d = tid, e = 0; d < a.dv && e < 4; d += 256, ++e) {
+      float x0 = 0.f, x1 = 0.f;
+      uint32_t p = 0;
+      for (; p + 2 <= pc; p += 2) {
+        x0 = fmaf(s_w[p], a.ws_o[row_of(p0 + p) * a.dv + d], x0);
+        x1 = fmaf(s_w[p + 1], a.ws_o[row_of(p0 + p + 1) * a.dv + d], x1);
+      }
+      if (p < pc) x0 = fmaf(s_w[p], a.ws_o[row_of(p0 + p) * a.dv + d], x0);
+      acc[e] += x0 + x1;
+    }
+  }
+  for (uint32_t d = tid, e = 0; d < a.dv && e < 4; d += 256, ++e) out[d] = DT::from_f(acc[e] * inv);
+}
+
 template <class DT, bool PU>
 hipError_t launch_d(const RowArgs &a, dim3 grid, hipStream_t st) {
   switch (a.d) {
@@ -350,6 +625,27 @@ hipError_t launch_d(const RowArgs &a, dim3 grid, hipStream_t st) {
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
+}
+
+template <class DT, bool PU>
+hipError_t launch_bal_d(const RowArgs &a, dim3 grid, hipStream_t st) {
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((decode_balanced_kernel<DT, 64, PU>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((decode_balanced_kernel<DT, 128, PU>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((decode_balanced_kernel<DT, 256, PU>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+template <class DT, bool PU>
+int bal_blocks_per_cu(uint32_t d) {
+  int blocks = 0;
+  hipError_t e = hipErrorNotSupported;
+  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 64, PU>, 256, 0);
+  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 128, PU>, 256, 0);
+  if (d == 256) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 256, PU>, 256, 0);
+  return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -399,6 +695,35 @@ hipError_t launch_rows_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
   const bool pu = (ps & (ps - 1)) == 0 && ps >= 16u;
   if (dt == PKV_BF16) return pu ? launch_d<BF16, true>(a, grid, st) : launch_d<BF16, false>(a, grid, st);
   return pu ? launch_d<F16, true>(a, grid, st) : launch_d<F16, false>(a, grid, st);
+}
+
+int balanced_waves_per_cu(uint32_t d, uint32_t ps, pkv_dtype dt) {
+  const bool pu = (ps & (ps - 1)) == 0 && ps >= 16u;
+  int b;
+  if (dt == PKV_BF16) b = pu ? bal_blocks_per_cu<BF16, true>(d) : bal_blocks_per_cu<BF16, false>(d);
+  else b = pu ? bal_blocks_per_cu<F16, true>(d) : bal_blocks_per_cu<F16, false>(d);
+  return b * kWaves;
+}
+
+hipError_t launch_rows_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
+  if (a.bal_waves == 0 || a.bal_waves % kWaves != 0) return hipErrorInvalidValue;
+  const dim3 grid(a.bal_waves / kWaves);
+  const uint32_t ps = a.plan.ps;
+  const bool pu = (ps & (ps - 1)) == 0 && ps >= 16u;
+  if (dt == PKV_BF16) return pu ? launch_bal_d<BF16, true>(a, grid, st) : launch_bal_d<BF16, false>(a, grid, st);
+  return pu ? launch_bal_d<F16, true>(a, grid, st) : launch_bal_d<F16, false>(a, grid, st);
+}
+
+hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, hipStream_t st) {
+  const uint64_t blocks = uint64_t(a.n_queries) * a.hq;
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  switch (dt) {
+    case PKV_F16: hipLaunchKernelGGL(merge_balanced_kernel<F16>, grid, dim3(256), 0, st, a); break;
+    case PKV_BF16: hipLaunchKernelGGL(merge_balanced_kernel<BF16>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace pkv

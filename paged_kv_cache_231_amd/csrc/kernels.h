@@ -33,16 +33,25 @@ struct RowArgs {
   uint64_t kp_page, kp_tok;
   void *out;                 // [Q, hq, dv] in the input dtype
   float *ws_o, *ws_lse;      // [Q, splits, hq, dv], [Q, splits, hq] (splits > 1)
+  // Balanced schedule (bal_waves > 0): the row queries' tile positions are
+  // cut into equal ranges, one per group of segq waves (segq = KV heads x
+  // 16-head groups); pieces cut by a range boundary go to ws_o/ws_lse slots
+  // (2 per wave, 16 head rows each).  bal_rec[2r], bal_rec[2r + 1]: first
+  // tile and tile count of row query r; bal_rec[2 n_queries]: total tiles.
+  uint32_t *bal_rec;
+  uint32_t bal_waves;
 };
 
 struct MergeArgs {
   PlanView plan;
   const uint32_t *qlist;
   uint32_t n_queries;
-  uint32_t hq, dv, splits, pages_per_split;
+  uint32_t hq, hkv, dv, splits, pages_per_split;
   int causal;
   const float *ws_o, *ws_lse;
   void *out;
+  const uint32_t *bal_rec;  // balanced schedule (bal_waves > 0), as in RowArgs
+  uint32_t bal_waves;
 };
 
 // Query tiles of the chunked-prefill kernel.
@@ -68,6 +77,12 @@ bool rows_mfma_supported(const RowArgs &a, pkv_dtype dt);
 uint64_t rows_mfma_blocks(const RowArgs &a);
 int rows_mfma_blocks_per_cu(const RowArgs &a, pkv_dtype dt);
 hipError_t launch_rows_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st);
+// Balanced MFMA decode: the wave-range kernel, then the merge of the pieces
+// cut by range boundaries.  balanced_waves_per_cu: resident waves per CU of
+// the wave-range kernel.
+int balanced_waves_per_cu(uint32_t d, uint32_t ps, pkv_dtype dt);
+hipError_t launch_rows_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st);
+hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, pkv_dtype dt, hipStream_t st);
 // MLA on MFMA (F16/BF16, rank 512, position dim 64): one block per
 // (query, 128-head group, split part).

@@ -20,17 +20,18 @@ def make_plan(wl, stream=None):
 
 
 def run(wl, splits=1, plan=None, dev=None, out=None):
-    """Library output for a workload, as a float64 numpy array."""
+    """Library output for a workload, as a float64 numpy array (splits: 1
+    unsplit, 0 balanced workspace, else that many parts)."""
     dev = dev if dev is not None else to_dev(wl)
     plan = plan if plan is not None else make_plan(wl)
     if wl.kind == "attention":
         hq, dv = wl.info["hq"], wl.info["dv"]
-        ws = pkv.Workspace(wl.queries, hq, dv, splits) if splits > 1 else None
+        ws = pkv.Workspace.for_splits(wl.queries, hq, dv, splits)
         o = pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal,
                           workspace=ws, out=out)
     else:
         h, r = wl.info["h"], wl.info["r"]
-        ws = pkv.Workspace(wl.queries, h, r, splits) if splits > 1 else None
+        ws = pkv.Workspace.for_splits(wl.queries, h, r, splits)
         o = pkv.mla(plan, dev["q_abs"], dev["q_pos"], dev["latent"], dev["k_pos"], wl.scale,
                     wl.causal, workspace=ws, out=out)
     torch.cuda.synchronize()

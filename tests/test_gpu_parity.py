@@ -127,7 +127,7 @@ def test_tune_splits_picks_a_candidate_and_leaves_the_result():
     plan = make_plan(wl)
     out = torch.empty(wl.queries, 32, 128, dtype=torch.bfloat16, device="cuda")
     s = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out, reps=2)
-    assert s in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64) and s <= wl.table_width
+    assert s in (0, 1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64) and s <= wl.table_width
     assert_close(out.double().cpu().numpy(), expected(wl), torch.bfloat16, "tuned attention")
     lens = [700, 64]
     mw = build_mla("tune", 31, torch.bfloat16, lens, decode_queries(lens), 128, 512, 64, 64)
@@ -194,9 +194,12 @@ def test_validation_errors_launch_nothing():
     torch.cuda.synchronize()
     assert (out == 7.0).all(), "a rejected call wrote the output"
     with pytest.raises(pkv.PKVError):
-        pkv.Workspace(wl.queries, 8, 128, 0)
+        pkv.Workspace(wl.queries, 0, 128, 0)  # balanced, zero heads
     with pytest.raises(pkv.PKVError):
         pkv.Workspace(wl.queries, 8, 128, 257)
+    ws_bal = pkv.Workspace(wl.queries, 4, 128, 0)
+    assert lib.pkv_workspace_splits(ws_bal.handle) == 0
+    assert call(ws=ws_bal.handle) == "EWORKSPACE"  # built for 4 heads
 
 
 def test_rebind_and_set_word():
