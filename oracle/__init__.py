@@ -11,9 +11,12 @@ does not import it.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 Modules
   reference  dense softmax attention over gathered pages, split + merge, MLA
   plan       an independent encoder/decoder of the u32 plan words (spec v1)
+  append     the cache append: write targets, validate_writes, the copy-on-
+             write report (``DevicePlan::append_with_report``)
 
 Pins: every function here is checked by the ``-m "not gpu"`` tests in
-``tests/test_oracle_pins.py`` and ``tests/test_oracle_plan.py`` against
+``tests/test_oracle_pins.py``, ``tests/test_oracle_plan.py`` and
+``tests/test_oracle_append.py`` against
 closed forms, brute force, a library routine (torch SDPA in float64) and
 hand-derived golden word lists; none is "parity unpinned".
 """
@@ -30,3 +33,10 @@ from .reference import (  # noqa: F401
     mla_one,
 )
 from .plan import encode_plan, decode_plan, PlanError  # noqa: F401
+from .append import (  # noqa: F401
+    WriteConflict,
+    write_targets,
+    validate_writes,
+    paged_append,
+    append_report,
+)

@@ -46,3 +46,23 @@ def read_plan_fixture(name):
 
 
 FIXTURES = sorted(f for f in os.listdir(GOLDEN) if f.startswith("plan_"))
+
+
+def read_append_fixture(name):
+    """Return dict(lens, qseq, qpos, table, page_size, pages, targets)."""
+    fields, cur = {}, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].rstrip()
+            if not line.strip():
+                continue
+            cur, rest = line.split(":", 1)
+            fields[cur] = rest
+    out = {key: [x for tok in fields[key].split() for x in _expand(tok)]
+           for key in ("lens", "qseq", "qpos")}
+    out["table"] = np.array([[x for tok in r.split() for x in _expand(tok)]
+                             for r in fields["table"].split("/")], dtype=np.int64)
+    out["page_size"] = int(fields["page_size"])
+    out["pages"] = int(fields["pages"])
+    out["targets"] = [tuple(int(x) for x in t.split(":")) for t in fields["targets"].split()]
+    return out
