@@ -195,6 +195,34 @@ def prefill_measure(torch, pkv, workloads, steps: int):
             "workload": wl.name}
 
 
+def append_measure(torch, pkv, workloads, steps: int):
+    """Cache-append GB/s on the mixed workload's plan: every one of its 4216
+    queries stores its new K/V rows (read once, written once)."""
+    wl = workloads.config(4)
+    dev = {k: v.to("cuda") for k, v in wl.tensors.items() if k in ("k", "v")}
+    stream = torch.cuda.current_stream()
+    plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
+    hkv, d, dv = (wl.info[x] for x in ("hkv", "d", "dv"))
+    nk = torch.randn(wl.queries, hkv, d, device="cuda").to(wl.dtype)
+    nv = torch.randn(wl.queries, hkv, dv, device="cuda").to(wl.dtype)
+    for _ in range(3):
+        pkv.append(plan, nk, nv, dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    plan.timing(True)
+    for _ in range(steps):
+        pkv.append(plan, nk, nv, dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    n, ms = plan.timing_read("append")
+    plan.timing(False)
+    nbytes = 2 * (nk.numel() + nv.numel()) * nk.element_size()
+    avg_us = ms / max(1, n) * 1e3
+    gbs = nbytes / (avg_us * 1e-6) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "cache append",
+            "avg_launch_us": round(avg_us, 2), "launches": n, "bytes_per_launch": nbytes,
+            "workload": f"append of the {wl.queries} queries of: {wl.name}"}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -299,6 +327,7 @@ def main():
     }
     if not args.no_prefill and wl.kind == "attention":
         line["prefill"] = prefill_measure(torch, pkv, workloads, args.prefill_steps)
+        line["append"] = append_measure(torch, pkv, workloads, args.prefill_steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

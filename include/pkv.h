@@ -110,6 +110,14 @@ pkv_status pkv_plan_encode(uint32_t sequences, const uint32_t *seq_lens,
 /* Check that n_words host words are a valid spec-v1 plan (host only). */
 pkv_status pkv_plan_validate(const uint32_t *words, size_t n_words);
 
+/* Check the write plan of an append on valid plan words (host only;
+ * `validate_writes` on the ruDNN page, shown by name): every query writes
+ * the cache slot of its own position, and no two queries may write one
+ * physical (page, slot), neither through one (sequence, position) nor
+ * through a page two sequences share.  Errors: those of pkv_plan_validate,
+ * PKV_EINVAL "two queries write one cache slot". */
+pkv_status pkv_plan_validate_writes(const uint32_t *words, size_t n_words);
+
 /* Validate host words, copy them to a new device buffer on `stream` (one
  * H2D copy, `DevicePlan::upload`) and return the plan.  The plan keeps its
  * own host copy, is bound to the current device and to `stream`, and must be
@@ -256,21 +264,54 @@ pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs,
                    void *out, uint32_t heads, uint32_t rank, uint32_t pos_dim,
                    float scale, int causal, pkv_workspace *ws, void *stream);
 
+/* ------------------------------------------------------------- append
+ * Cache append (ruDNN `DevicePlan::append`, `append_with_report`,
+ * `CacheAppendReport`): query i stores new_k[i] and new_v[i] (all KV heads)
+ * at slot qpos[i] % ps of page table[qseq[i]][qpos[i] / ps] of the caches.
+ *   new_k [Q, kv_heads, head_dim], new_v [Q, kv_heads, value_dim]  device
+ *   k [N, ps, kv_heads, head_dim], v [N, ps, kv_heads, value_dim]  device
+ * k_copy / v_copy: NULL to append in place; otherwise a buffer of the
+ * cache's size into which the cache is copied first (device to device, on
+ * `stream`) and the append then goes, leaving k / v unchanged (the page's
+ * copy-on-write for a cache that is not uniquely owned; which caches are
+ * shared is the caller's knowledge here).  report (may be NULL): which
+ * caches were copied and the bytes copied.  Q == 0 launches and copies
+ * nothing (report all zero).  The write plan is checked on the plan's host
+ * words at call time (pkv_plan_validate_writes) before anything is
+ * launched.  Captured into a graph, the copies and the append replay with
+ * the plan words of replay time; the check ran at capture time.
+ * Errors: PKV_EINVAL (null pointer, bad dtype, a conflicting write plan,
+ * new rows, caches or copies overlapping each other, K and V caches
+ * overlapping), PKV_ESHAPE (a zero head count or dim, a dim above 1024),
+ * PKV_ERANGE (a tensor above u32 elements), PKV_EDEVICE, PKV_EHIP. */
+typedef struct {
+  uint32_t key_copied;    /* the key cache was copied before the append   */
+  uint32_t value_copied;  /* the value cache was copied before the append */
+  uint64_t copied_bytes;  /* bytes of the copied caches                    */
+} pkv_append_report;
+
+pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k,
+                      const void *new_v, void *k, void *v, void *k_copy,
+                      void *v_copy, uint32_t kv_heads, uint32_t head_dim,
+                      uint32_t value_dim, pkv_append_report *report,
+                      void *stream);
+
 /* ------------------------------------------------------------- timing
  * Per-kernel timing, for benchmarks.  While enabled on a plan, every
- * pkv_attention / pkv_mla call with that plan records a pair of HIP events
- * around each kernel it launches, on the call's stream, so a kernel's
- * duration is measured on the stream it runs on.  Kernels: the per-query
- * row kernel (decode rows, split parts), the chunked-prefill tile kernel,
- * the MLA kernel, and the split merge.  Enabling clears earlier records.
- * Not for use while the stream is being captured into a graph (the event
+ * pkv_attention / pkv_mla / pkv_append call with that plan records a pair
+ * of HIP events around each kernel it launches, on the call's stream, so a
+ * kernel's duration is measured on the stream it runs on.  Kernels: the
+ * per-query row kernel (decode rows, split parts), the chunked-prefill tile
+ * kernel, the MLA kernel, the split merge, and the cache append.  Enabling
+ * clears earlier records.  Not for use while the stream is being captured into a graph (the event
  * records would be captured too).  Errors: PKV_EINVAL (null plan, unknown
  * kernel, null output), PKV_EHIP (event creation or query failure). */
 typedef enum {
   PKV_KERNEL_ROWS = 0,
   PKV_KERNEL_TILES = 1,
   PKV_KERNEL_MLA = 2,
-  PKV_KERNEL_MERGE = 3
+  PKV_KERNEL_MERGE = 3,
+  PKV_KERNEL_APPEND = 4
 } pkv_kernel;
 
 pkv_status pkv_plan_timing(pkv_plan *plan, int enable);

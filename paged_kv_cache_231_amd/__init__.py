@@ -10,6 +10,7 @@ library's HIP kernels; there is no Python or CPU fallback.
     ws = Workspace(plan.queries, q_heads, value_dim, splits)
     out = attention(plan, q, k, v, scale, workspace=ws)       # split-KV
     out = mla(plan, q_abs, q_pos, latent, k_pos, scale)
+    k, v, report = append(plan, new_k, new_v, k, v)          # cache append
 
 Shapes (ruDNN 0.1.7 ``paged_attention`` page, ``DevicePlan::attention`` and
 ``DevicePlan::mla`` docs): q [Q,Hq,D], k [N,ps,Hkv,D], v [N,ps,Hkv,Dv],
@@ -24,10 +25,11 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import LIB_PATH, PKVError, STATUS, check, lib  # noqa: F401
+from ._lib import LIB_PATH, AppendReport, PKVError, STATUS, check, lib  # noqa: F401
 
-__all__ = ["Plan", "Workspace", "attention", "mla", "encode_plan", "validate_plan",
-           "suggest_splits", "PKVError", "LIB_PATH", "lib", "HEADER_WORDS", "MAX_SPLITS"]
+__all__ = ["Plan", "Workspace", "attention", "mla", "append", "encode_plan", "validate_plan",
+           "validate_writes", "suggest_splits", "PKVError", "LIB_PATH", "lib", "HEADER_WORDS",
+           "MAX_SPLITS"]
 
 HEADER_WORDS = 16
 MAX_SPLITS = 256
@@ -152,7 +154,7 @@ class Plan:
                                             ctypes.c_void_p(self.stream)))
         self.words[int(index)] = int(value)
 
-    KERNELS = {"rows": 0, "tiles": 1, "mla": 2, "merge": 3}
+    KERNELS = {"rows": 0, "tiles": 1, "mla": 2, "merge": 3, "append": 4}
 
     def timing(self, enable: bool = True) -> None:
         """Record HIP events around every kernel launched with this plan
@@ -319,3 +321,39 @@ def mla(plan: Plan, q_abs, q_pos, latent, k_pos, scale: float, causal: bool = Tr
                         int(bool(causal)), workspace.handle if workspace is not None else None,
                         ctypes.c_void_p(plan.stream)))
     return out
+
+
+def append(plan: Plan, new_k, new_v, k, v, copy=False):
+    """Cache append (pkv_append): query i's new_k[i] / new_v[i] ([Hkv, D] /
+    [Hkv, Dv]) go to the cache slot of its own position.  ``copy`` (a bool,
+    or a (key, value) pair of bools): copy that cache first and append into
+    the copy (copy-on-write for a cache that is not uniquely owned), leaving
+    the original unchanged.  Returns (k, v, report) with the caches written
+    and the report as a dict."""
+    if new_k.dim() != 3 or new_v.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise PKVError("EINVAL", "invalid cache append ranks")
+    copy_k, copy_v = (copy, copy) if isinstance(copy, bool) else (bool(copy[0]), bool(copy[1]))
+    n, ps, hkv, d = k.shape
+    dv = v.shape[3]
+    if (n, ps) != (plan.pages, plan.page_size) or tuple(v.shape[:3]) != (n, ps, hkv) \
+            or tuple(new_k.shape) != (plan.queries, hkv, d) \
+            or tuple(new_v.shape) != (plan.queries, hkv, dv):
+        raise PKVError("ESHAPE", "incompatible cache append shapes")
+    code = _dtype_code(new_k, new_v, k, v)
+    kc = torch.empty_like(k) if copy_k and plan.queries else None
+    vc = torch.empty_like(v) if copy_v and plan.queries else None
+    rep = AppendReport()
+    check(lib().pkv_append(plan.handle, code, new_k.data_ptr(), new_v.data_ptr(), k.data_ptr(),
+                           v.data_ptr(), kc.data_ptr() if kc is not None else None,
+                           vc.data_ptr() if vc is not None else None, hkv, d, dv,
+                           ctypes.byref(rep), ctypes.c_void_p(plan.stream)))
+    report = {"key_copied": bool(rep.key_copied), "value_copied": bool(rep.value_copied),
+              "copied_bytes": int(rep.copied_bytes)}
+    return (kc if kc is not None else k), (vc if vc is not None else v), report
+
+
+def validate_writes(words) -> None:
+    """pkv_plan_validate_writes on plan words (host only): raises PKVError
+    when two queries would write one cache slot."""
+    w = _u32_array(words)
+    check(lib().pkv_plan_validate_writes(_ptr32(w), w.size))

@@ -23,11 +23,18 @@ _size = ctypes.c_size_t
 _f = ctypes.c_float
 _i = ctypes.c_int
 
+class AppendReport(ctypes.Structure):
+    """pkv_append_report."""
+    _fields_ = [("key_copied", ctypes.c_uint32), ("value_copied", ctypes.c_uint32),
+                ("copied_bytes", ctypes.c_uint64)]
+
+
 # name: (restype, argtypes) for every function of include/pkv.h
 SIGNATURES = {
     "pkv_plan_encode": (_i, [_u32, _pu32, _u32, _pu32, _pu32, _u32, _pu32, _u32, _u32, _pu32,
                              ctypes.POINTER(_size)]),
     "pkv_plan_validate": (_i, [_pu32, _size]),
+    "pkv_plan_validate_writes": (_i, [_pu32, _size]),
     "pkv_plan_create": (_i, [_pu32, _size, _p, ctypes.POINTER(_p)]),
     "pkv_plan_rebind_async": (_i, [_p, _p, _size, _p]),
     "pkv_plan_set_word_async": (_i, [_p, _size, _u32, _p]),
@@ -45,6 +52,8 @@ SIGNATURES = {
                                  ctypes.POINTER(_u32)]),
     "pkv_attention": (_i, [_p, _i, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _f, _i, _p, _p]),
     "pkv_mla": (_i, [_p, _i, _p, _p, _p, _p, _p, _u32, _u32, _u32, _f, _i, _p, _p]),
+    "pkv_append": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _u32, _u32, _u32,
+                        ctypes.POINTER(AppendReport), _p]),
     "pkv_plan_timing": (_i, [_p, _i]),
     "pkv_plan_timing_read": (_i, [_p, _i, ctypes.POINTER(_u32), ctypes.POINTER(ctypes.c_double)]),
     "pkv_last_error": (ctypes.c_char_p, []),

@@ -383,7 +383,7 @@ pkv_status pkv_plan_timing_read(pkv_plan *plan, pkv_kernel kernel, uint32_t *lau
                                 double *total_ms) {
   clear_error();
   if (!plan || !launches || !total_ms) return fail(PKV_EINVAL, "null argument");
-  if (int(kernel) < int(PKV_KERNEL_ROWS) || int(kernel) > int(PKV_KERNEL_MERGE))
+  if (int(kernel) < int(PKV_KERNEL_ROWS) || int(kernel) > int(PKV_KERNEL_APPEND))
     return fail(PKV_EINVAL, "unknown kernel");
   uint32_t n = 0;
   double ms = 0.0;
@@ -653,6 +653,75 @@ pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, c
     hipError_t e = launch_tiles(ta, dtype, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
+  return PKV_OK;
+}
+
+pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k, const void *new_v,
+                      void *k, void *v, void *k_copy, void *v_copy, uint32_t hkv, uint32_t d,
+                      uint32_t dv, pkv_append_report *report, void *stream_) {
+  clear_error();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (report) *report = pkv_append_report{0, 0, 0};
+  if (!plan) return fail(PKV_EINVAL, "null plan");
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "paged operands must be F32, F16 or BF16");
+  if (hkv == 0 || d == 0 || dv == 0 || d > 1024 || dv > 1024)
+    return fail(PKV_ESHAPE, "incompatible cache append shapes");
+  const PlanLayout &L = plan->L;
+  if (!u32_elems({L.Q, hkv, d}) || !u32_elems({L.Q, hkv, dv}) || !u32_elems({L.N, L.ps, hkv, d}) ||
+      !u32_elems({L.N, L.ps, hkv, dv}))
+    return fail(PKV_ERANGE, "a tensor has more than 2^32 - 1 elements");
+  pkv_status st = check_binding(plan, stream);
+  if (st != PKV_OK) return st;
+  st = validate_writes(plan->host.data(), L);
+  if (st != PKV_OK) return st;
+  if (L.Q == 0) return PKV_OK;  // a no-op append copies nothing
+  if (!new_k || !new_v || !k || !v) return fail(PKV_EINVAL, "null tensor pointer");
+  const uint64_t es = elem_size(dtype);
+  const uint64_t kb = uint64_t(hkv) * d * es, vb = uint64_t(hkv) * dv * es;  // one slot / query
+  const uint64_t k_bytes = uint64_t(L.N) * L.ps * kb, v_bytes = uint64_t(L.N) * L.ps * vb;
+  const uint64_t nk_bytes = uint64_t(L.Q) * kb, nv_bytes = uint64_t(L.Q) * vb;
+  void *kd = k_copy ? k_copy : k, *vd = v_copy ? v_copy : v;
+  if (overlaps(kd, k_bytes, vd, v_bytes) || overlaps(k, k_bytes, v, v_bytes))
+    return fail(PKV_EINVAL, "K and V caches overlap");
+  if ((k_copy && (overlaps(k_copy, k_bytes, k, k_bytes) || overlaps(k_copy, k_bytes, v, v_bytes))) ||
+      (v_copy && (overlaps(v_copy, v_bytes, v, v_bytes) || overlaps(v_copy, v_bytes, k, k_bytes))))
+    return fail(PKV_EINVAL, "a cache copy overlaps a cache");
+  for (const void *src : {new_k, new_v}) {
+    const uint64_t sb = src == new_k ? nk_bytes : nv_bytes;
+    if (overlaps(src, sb, kd, k_bytes) || overlaps(src, sb, vd, v_bytes))
+      return fail(PKV_EINVAL, "new rows overlap a cache they are written to");
+  }
+  if (overlaps(new_k, nk_bytes, new_v, nv_bytes) && new_k != new_v)
+    return fail(PKV_EINVAL, "new K and V rows overlap");
+
+  pkv_append_report rep{0, 0, 0};
+  if (k_copy) {
+    if (hipMemcpyAsync(k_copy, k, k_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return fail(PKV_EHIP, "copying the key cache failed");
+    rep.key_copied = 1;
+    rep.copied_bytes += k_bytes;
+  }
+  if (v_copy) {
+    if (hipMemcpyAsync(v_copy, v, v_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return fail(PKV_EHIP, "copying the value cache failed");
+    rep.value_copied = 1;
+    rep.copied_bytes += v_bytes;
+  }
+  AppendArgs aa{};
+  aa.plan = view_of(plan);
+  aa.n_queries = L.Q;
+  aa.new_k = new_k;
+  aa.new_v = new_v;
+  aa.k = kd;
+  aa.v = vd;
+  hipError_t e;
+  {
+    Timed t(plan, PKV_KERNEL_APPEND, stream);
+    e = launch_append(aa, kb, vb, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  if (report) *report = rep;
   return PKV_OK;
 }
 

@@ -25,4 +25,8 @@ pkv_status read_layout(const uint32_t *words, size_t n_words, PlanLayout *out);
 // Full check of a spec-v1 plan (header, every section, row/tile cover).
 pkv_status validate_plan(const uint32_t *words, size_t n_words, PlanLayout *out);
 
+// Write plan of an append on a valid plan: no two queries target one
+// physical (page, slot).
+pkv_status validate_writes(const uint32_t *words, const PlanLayout &L);
+
 }  // namespace pkv

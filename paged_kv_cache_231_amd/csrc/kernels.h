@@ -67,6 +67,18 @@ struct TileArgs {
   void *out;
 };
 
+// Cache append: query i's new K/V blocks (Hkv * D, Hkv * Dv elements) to
+// the slot of its position; k_units / v_units are set by the launcher.
+struct AppendArgs {
+  PlanView plan;
+  uint32_t n_queries;
+  uint32_t k_units, v_units;  // copy units per query's K and V block
+  const void *new_k, *new_v;
+  void *k, *v;                // the caches written (in place or copies)
+};
+
+hipError_t launch_append(AppendArgs a, uint64_t k_block_bytes, uint64_t v_block_bytes,
+                         hipStream_t st);
 hipError_t launch_rows_generic(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 // Fast VALU decode; returns hipErrorNotSupported when the shape is not one
 // of its specialisations (the caller then uses the generic kernel).

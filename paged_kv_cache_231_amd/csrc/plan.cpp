@@ -125,6 +125,26 @@ pkv_status validate_plan(const uint32_t *w, size_t n, PlanLayout *out) {
 
 }  // namespace pkv
 
+namespace pkv {
+
+// Slot keys page * ps + slot of every query's own position (positions are
+// inside their sequences and used table entries inside the pool: the plan
+// is valid), sorted; a repeated key is a conflict.
+pkv_status validate_writes(const uint32_t *w, const PlanLayout &L) {
+  std::vector<uint64_t> keys(L.Q);
+  for (uint32_t i = 0; i < L.Q; ++i) {
+    const uint32_t s = w[L.qseq + i], p = w[L.qpos + i];
+    const uint32_t page = w[L.table + size_t(s) * L.W + p / L.ps];
+    keys[i] = uint64_t(page) * L.ps + p % L.ps;
+  }
+  std::sort(keys.begin(), keys.end());
+  for (size_t i = 1; i < keys.size(); ++i)
+    if (keys[i] == keys[i - 1]) return fail(PKV_EINVAL, "two queries write one cache slot");
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 const char *pkv_last_error(void) { return pkv::last_error(); }
@@ -180,6 +200,14 @@ pkv_status pkv_plan_encode(uint32_t S, const uint32_t *lens, uint32_t Q, const u
 pkv_status pkv_plan_validate(const uint32_t *words, size_t n_words) {
   pkv::clear_error();
   return pkv::validate_plan(words, n_words, nullptr);
+}
+
+pkv_status pkv_plan_validate_writes(const uint32_t *words, size_t n_words) {
+  pkv::clear_error();
+  pkv::PlanLayout L;
+  const pkv_status st = pkv::validate_plan(words, n_words, &L);
+  if (st != PKV_OK) return st;
+  return pkv::validate_writes(words, L);
 }
 
 }  // extern "C"

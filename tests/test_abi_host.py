@@ -153,3 +153,41 @@ def test_validator_rejects_corrupt_words():
     with pytest.raises(pkv.PKVError):
         pkv.validate_plan(good[:-1])
     assert d["tiles"] == [(1, 10)]
+
+
+def test_cpp_validate_writes_matches_the_oracle():
+    """pkv_plan_validate_writes accepts exactly the write plans the oracle's
+    validate_writes accepts: random schedules (chunks may overlap, single
+    queries may repeat a position) with and without a page two sequences
+    share."""
+    from oracle import append as oa
+    rng = np.random.default_rng(77)
+    seen = {True: 0, False: 0}
+    for trial in range(400):
+        lens, qseq, qpos, table, ps, pages = _random_schedule(rng)
+        if len(lens) > 1 and trial % 2:
+            table = table.copy()
+            table[1, 0] = table[0, 0]  # sequences 0 and 1 share a page
+        words = op.encode_plan(lens, qseq, qpos, table, ps, pages)
+        try:
+            oa.validate_writes(lens, qseq, qpos, table, ps, pages)
+            ok = True
+        except oa.WriteConflict:
+            ok = False
+        if ok:
+            pkv.validate_writes(words)
+        else:
+            with pytest.raises(pkv.PKVError) as e:
+                pkv.validate_writes(words)
+            assert e.value.code == "EINVAL"
+        seen[ok] += 1
+    assert seen[True] > 50 and seen[False] > 50
+
+
+def test_append_rejects_without_a_gpu_call():
+    """Argument errors of pkv_append come back before any HIP call."""
+    lib = pkv.lib()
+    rep = _lib.AppendReport()
+    assert _lib.STATUS[lib.pkv_append(None, 2, None, None, None, None, None, None, 1, 1, 1,
+                                      ctypes.byref(rep), None)] == "EINVAL"
+    assert "null plan" in lib.pkv_last_error().decode()
