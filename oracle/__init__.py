@@ -23,6 +23,7 @@ hand-derived golden word lists; none is "parity unpinned".
 
 from .reference import (  # noqa: F401
     visible_count,
+    window_start,
     paged_attention,
     paged_attention_split,
     merge_partials,

@@ -118,12 +118,26 @@ def _queries_by_sequence(qseq):
     return groups
 
 
-def _visible_range(n: int, token_range):
-    """Logical positions ``[lo, hi)`` a query uses: ``[0, n)`` cut to the part."""
+def window_start(n: int, window: int) -> int:
+    """First visible position under a sliding window of ``window`` keys.
+
+    Reading of the ``window`` field of the libmir-cuda 0.1.0 decode-attention
+    geometry (its `Geometry` struct; the page shows the field, not its
+    use): a query whose visible keys are positions ``[0, n)`` sees only the
+    last ``window`` of them, ``[max(0, n - window), n)``; 0 means no window.
+    """
+    return max(0, n - window) if window > 0 else 0
+
+
+def _visible_range(n: int, token_range, window: int = 0):
+    """Logical positions ``[lo, hi)`` a query uses: ``[0, n)`` cut to the
+    sliding window, then to the part."""
+    w0 = window_start(n, window)
     if token_range is None:
-        return 0, n
+        return w0, n
     lo, hi = token_range
-    return min(max(lo, 0), n), min(max(hi, 0), n)
+    lo, hi = min(max(lo, w0), n), min(max(hi, 0), n)
+    return lo, max(lo, hi)
 
 
 def _is_torch(x) -> bool:
@@ -138,14 +152,15 @@ def _rows(x, idx):
 
 
 def paged_attention(q, k, v, lens, qseq, qpos, table, page_size: int,
-                    scale: float, causal: bool, token_range=None):
+                    scale: float, causal: bool, token_range=None, window: int = 0):
     """Paged MHA/GQA attention in float64.
 
     q [Q,Hq,D], k [N,ps,Hkv,D], v [N,ps,Hkv,Dv] (numpy or CPU torch);
     lens [S], qseq [Q], qpos [Q], table [S,W] integers.
     ``token_range = (lo, hi)`` restricts every query to the visible keys with
     logical position in ``[lo, hi)`` (one part of a split); parts with no
-    visible key give out = 0 and lse = -inf.
+    visible key give out = 0 and lse = -inf.  ``window`` > 0 keeps only the
+    last ``window`` visible keys (``window_start``).
     Returns (out [Q,Hq,Dv] float64, lse [Q,Hq] float64, natural log).
     """
     qn = int(q.shape[0])
@@ -162,7 +177,7 @@ def paged_attention(q, k, v, lens, qseq, qpos, table, page_size: int,
         vv = _gather_tokens(v, table[s], n_max, page_size)  # [n, Hkv, Dv]
         qq = _rows(q, idx)                                  # [nq, Hq, D]
         for j, i in enumerate(idx):
-            lo, hi = _visible_range(visible_count(lens, qseq, qpos, i, causal), token_range)
+            lo, hi = _visible_range(visible_count(lens, qseq, qpos, i, causal), token_range, window)
             kg = kk[lo:hi].transpose(1, 2, 0)       # [Hkv, D, t]
             vg = vv[lo:hi].transpose(1, 0, 2)       # [Hkv, t, Dv]
             qg = qq[j].reshape(hkv, grp, -1)        # head h = g*G + r -> [g, r, :]
@@ -241,11 +256,11 @@ def merge_partials(o_parts, lse_parts):
 
 
 def paged_attention_split(q, k, v, lens, qseq, qpos, table, page_size: int,
-                          scale: float, causal: bool, splits: int):
+                          scale: float, causal: bool, splits: int, window: int = 0):
     """Split-KV attention: per-part attention, then ``merge_partials``."""
     w = int(np.asarray(table).shape[1])
     parts = [paged_attention(q, k, v, lens, qseq, qpos, table, page_size, scale,
-                             causal, token_range=rg)
+                             causal, token_range=rg, window=window)
              for rg in split_ranges(w, page_size, splits)]
     return merge_partials([p[0] for p in parts], [p[1] for p in parts])
 
@@ -260,7 +275,8 @@ def paged_mla_split(q_abs, q_pos, latent, k_pos, lens, qseq, qpos, table,
     return merge_partials([p[0] for p in parts], [p[1] for p in parts])
 
 
-def attention_one(q, k, v, lens, qseq, qpos, table, page_size, scale, causal, i, h):
+def attention_one(q, k, v, lens, qseq, qpos, table, page_size, scale, causal, i, h,
+                  window: int = 0):
     """One output row ``out[i, h, :]`` computed on its own (for sampling big
     workloads): the same definition as ``paged_attention``, one query, one head.
     """
@@ -268,8 +284,9 @@ def attention_one(q, k, v, lens, qseq, qpos, table, page_size, scale, causal, i,
     g = h // (hq // hkv)
     s = int(qseq[i])
     n = visible_count(lens, qseq, qpos, i, causal)
-    kk = _gather_tokens(k, np.asarray(table)[s], n, page_size)[:, g, :]
-    vv = _gather_tokens(v, np.asarray(table)[s], n, page_size)[:, g, :]
+    lo = window_start(n, window)
+    kk = _gather_tokens(k, np.asarray(table)[s], n, page_size)[lo:, g, :]
+    vv = _gather_tokens(v, np.asarray(table)[s], n, page_size)[lo:, g, :]
     qv = _f64(q[i, h])
     x = scale * (kk @ qv)
     o, l = _softmax_pv(x[None, :], vv)
@@ -290,7 +307,7 @@ def mla_one(q_abs, q_pos, latent, k_pos, lens, qseq, qpos, table, page_size,
 
 
 __all__ = [
-    "visible_count", "paged_attention", "paged_mla", "split_ranges",
+    "visible_count", "window_start", "paged_attention", "paged_mla", "split_ranges",
     "merge_partials", "paged_attention_split", "paged_mla_split",
     "attention_one", "mla_one",
 ]
