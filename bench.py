@@ -223,6 +223,41 @@ def append_measure(torch, pkv, workloads, steps: int):
             "workload": f"append of the {wl.queries} queries of: {wl.name}"}
 
 
+def window_measure(torch, pkv, workloads, steps: int, window: int = 1024):
+    """Sliding-window decode GB/s: the packed-decode workload with each query
+    limited to its last ``window`` keys, balanced schedule; bytes = the K/V
+    rows inside the windows, each read once."""
+    wl = workloads.config(2)
+    dev = {k: v.to("cuda") for k, v in wl.tensors.items()}
+    stream = torch.cuda.current_stream()
+    plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
+    hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
+    out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
+    ws = pkv.Workspace(wl.queries, hq, dv, 0)
+
+    def step():
+        pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws,
+                      out=out, window=window)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    plan.timing(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    n, ms = plan.timing_read("rows")
+    plan.timing(False)
+    es = torch.empty((), dtype=wl.dtype).element_size()
+    nbytes = int(np.minimum(wl.visible(), window).sum()) * hkv * (d + dv) * es
+    avg_us = ms / max(1, n) * 1e3
+    gbs = nbytes / (avg_us * 1e-6) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "split-KV decode, window",
+            "window": window, "avg_launch_us": round(avg_us, 2), "launches": n,
+            "bytes_per_launch": nbytes, "workload": f"{wl.name}, window {window}, balanced"}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -328,6 +363,7 @@ def main():
     if not args.no_prefill and wl.kind == "attention":
         line["prefill"] = prefill_measure(torch, pkv, workloads, args.prefill_steps)
         line["append"] = append_measure(torch, pkv, workloads, args.prefill_steps)
+        line["window"] = window_measure(torch, pkv, workloads, args.prefill_steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

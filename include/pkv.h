@@ -250,6 +250,21 @@ pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q,
                          uint32_t value_dim, float scale, int causal,
                          pkv_workspace *ws, void *stream);
 
+/* Attention with a sliding window (the `window` field of the libmir-cuda
+ * decode-attention geometry; the page shows the field, not its use): query
+ * i sees only the last `window` of its visible keys, positions
+ * [max(0, n - window), n) with n as in pkv_attention; window 0 is
+ * pkv_attention.  With a window every query runs on the row kernels (decode
+ * rows and chunk queries alike; the chunked-prefill tile kernel has no
+ * window), with split, balanced or no workspace.  Arguments and errors as
+ * pkv_attention. */
+pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype,
+                                const void *q, const void *k, const void *v,
+                                void *out, uint32_t q_heads, uint32_t kv_heads,
+                                uint32_t head_dim, uint32_t value_dim,
+                                float scale, int causal, uint32_t window,
+                                pkv_workspace *ws, void *stream);
+
 /* MLA (`DevicePlan::mla` doc): one shared latent head is both key and value;
  * a position part only adds to the score:
  *   x_t = scale * (<q_abs[i,h,:], latent_t> + <q_pos[i,h,:], k_pos_t>)

@@ -275,8 +275,11 @@ def _dtype_code(*ts) -> int:
     return _DTYPES[dt]
 
 
-def attention(plan: Plan, q, k, v, scale: float, causal: bool = True, workspace=None, out=None):
-    """Paged MHA/GQA attention; returns ``out`` [Q, Hq, Dv]."""
+def attention(plan: Plan, q, k, v, scale: float, causal: bool = True, workspace=None, out=None,
+              window: int = 0):
+    """Paged MHA/GQA attention; returns ``out`` [Q, Hq, Dv].  ``window`` > 0:
+    each query sees only the last ``window`` of its visible keys
+    (pkv_attention_window)."""
     if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
         raise PKVError("EINVAL", "q must be 3-D and the caches 4-D")
     qn, hq, d = q.shape
@@ -290,10 +293,18 @@ def attention(plan: Plan, q, k, v, scale: float, causal: bool = True, workspace=
     elif tuple(out.shape) != (qn, hq, dv):
         raise PKVError("ESHAPE", "head counts, head dims or tensor shapes do not fit together")
     code = _dtype_code(q, k, v, out)
-    check(lib().pkv_attention(plan.handle, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              out.data_ptr(), hq, hkv, d, dv, float(scale), int(bool(causal)),
-                              workspace.handle if workspace is not None else None,
-                              ctypes.c_void_p(plan.stream)))
+    ws = workspace.handle if workspace is not None else None
+    if window:
+        if not 0 < int(window) <= 0xFFFFFFFF:
+            raise PKVError("ERANGE", "window outside u32")
+        check(lib().pkv_attention_window(plan.handle, code, q.data_ptr(), k.data_ptr(),
+                                         v.data_ptr(), out.data_ptr(), hq, hkv, d, dv,
+                                         float(scale), int(bool(causal)), int(window), ws,
+                                         ctypes.c_void_p(plan.stream)))
+    else:
+        check(lib().pkv_attention(plan.handle, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  out.data_ptr(), hq, hkv, d, dv, float(scale),
+                                  int(bool(causal)), ws, ctypes.c_void_p(plan.stream)))
     return out
 
 

@@ -239,6 +239,7 @@ pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_wo
     ma.splits = ra.splits;
     ma.pages_per_split = ra.pages_per_split;
     ma.causal = ra.causal;
+    ma.window = ra.window;
     ma.ws_o = ra.ws_o;
     ma.ws_lse = ra.ws_lse;
     ma.out = ra.out;
@@ -573,7 +574,15 @@ uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads, uint32_t kv_
 
 pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, const void *k,
                          const void *v, void *out, uint32_t hq, uint32_t hkv, uint32_t d,
-                         uint32_t dv, float scale, int causal, pkv_workspace *ws, void *stream_) {
+                         uint32_t dv, float scale, int causal, pkv_workspace *ws, void *stream) {
+  return pkv_attention_window(plan, dtype, q, k, v, out, hq, hkv, d, dv, scale, causal, 0u, ws,
+                              stream);
+}
+
+pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype, const void *q,
+                                const void *k, const void *v, void *out, uint32_t hq,
+                                uint32_t hkv, uint32_t d, uint32_t dv, float scale, int causal,
+                                uint32_t window, pkv_workspace *ws, void *stream_) {
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (!plan) return fail(PKV_EINVAL, "null plan");
@@ -608,6 +617,7 @@ pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, c
   ra.dv = dv;
   ra.pdim = 0;
   ra.causal = causal ? 1 : 0;
+  ra.window = window;
   ra.scale_log2 = scale * kLog2e;
   ra.q = q;
   ra.k = k;
@@ -640,7 +650,8 @@ pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, c
   ta.v_page = ra.v_page;
   ta.v_tok = ra.v_tok;
   ta.out = out;
-  const bool use_tiles = L.T > 0 && tiles_supported(ta, dtype);
+  // the tile kernel has no window: with one, every query runs as a row
+  const bool use_tiles = L.T > 0 && window == 0 && tiles_supported(ta, dtype);
   ra.qlist = use_tiles ? plan->dev + L.rows : nullptr;
   ra.n_queries = use_tiles ? L.R : L.Q;
 

@@ -69,6 +69,7 @@ template <bool PAGE_UNIFORM>
 struct TileMap {
   const uint32_t *table;
   uint32_t t_lo, t_hi, first, step, ps, ps_shift, n_pages_pool;
+  uint32_t lo;         // first visible key (sliding window); rows before it are masked
   uint32_t lane_page;  // page of tile (base + lane)
   uint32_t base;       // first tile held in lane_page
 
@@ -100,7 +101,8 @@ __device__ __forceinline__ void load_tile(TileRegs<D> &t, const RowArgs &a, Tile
     const uint32_t page = __builtin_amdgcn_readlane(map.lane_page, k - map.base);
     const uint32_t rows = map.t_hi - t0 < 16u ? map.t_hi - t0 : 16u;
     const bool page_ok = page < map.n_pages_pool;  // never read outside the pool
-    t.valid16 = page_ok ? (1u << rows) - 1u : 0u;
+    const uint32_t before = map.lo > t0 ? map.lo - t0 : 0u;  // rows before the window
+    t.valid16 = page_ok && before < 16u ? ((1u << rows) - 1u) & ~((1u << before) - 1u) : 0u;
     const uint32_t slot0 = t0 & (map.ps - 1);
 #pragma unroll
     for (int n = 0; n < TR::KS; ++n) {
@@ -117,7 +119,7 @@ __device__ __forceinline__ void load_tile(TileRegs<D> &t, const RowArgs &a, Tile
     for (int n = 0; n < TR::KS; ++n) {
       const uint32_t r = TR::RPI * n + lane / TR::CPR;
       const uint32_t tok = t0 + r;
-      bool ok = tok < map.t_hi;
+      bool ok = tok >= map.lo && tok < map.t_hi;
       const uint32_t lp = map.ps_shift != 32u ? tok >> map.ps_shift : tok / map.ps;
       const uint32_t slot = tok - lp * map.ps;
       const uint32_t page = ok ? map.table[lp] : 0u;
@@ -281,6 +283,7 @@ __device__ __forceinline__ void init_map(TileMap<PU> &map, const RowArgs &a, uin
   const bool pow2 = (ps & (ps - 1)) == 0;
   map.ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 32u;
   map.n_pages_pool = a.plan.N;
+  map.lo = 0;
 }
 
 template <class DT, int D, bool PU>
@@ -308,11 +311,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
   const uint32_t i = a.qlist ? a.qlist[qi] : qi;
   uint32_t seq;
   const uint32_t n = visible_keys(a.plan, i, a.causal, &seq);
+  const uint32_t lo = window_lo(n, a.window);
   const uint32_t ps = a.plan.ps;
   const uint64_t span = uint64_t(a.pages_per_split) * ps;
   const uint64_t lo64 = uint64_t(part) * span;
-  if (a.splits > 1 && lo64 >= n) return;  // empty part: the merge skips it
-  const uint32_t t_lo = uint32_t(lo64 < n ? lo64 : n);
+  // empty part (past the keys, or wholly before the window): the merge skips it
+  if (a.splits > 1 && (lo64 >= n || lo64 + span <= lo)) return;
+  // tiles stay on the 16-key grid (one page each when PU); rows before the
+  // window are masked
+  const uint32_t lo_grid = PU ? lo & ~15u : lo;
+  uint32_t t_lo = uint32_t(lo64 < n ? lo64 : n);
+  if (t_lo < lo_grid) t_lo = lo_grid;
   const uint32_t t_hi = uint32_t(lo64 + span < n ? lo64 + span : n);
   const uint32_t h0 = kvh * grp + sub * kHeads;               // first q head of the block
   const uint32_t nh = grp - sub * kHeads < kHeads ? grp - sub * kHeads : kHeads;
@@ -327,6 +336,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
   unsigned char *vt = lds + wv * L::kTileBytes;  // this wave's V tile
   TileMap<PU> map;
   init_map<PU>(map, a, seq, t_lo, t_hi, wv, 4u);
+  map.lo = lo;
   const uint32_t first = t_lo + wv * 16u;
   const uint32_t n_tiles = first < t_hi ? (t_hi - first + 63u) / 64u : 0u;
   stream_tiles<DT, D, PU>(st, map, n_tiles, a, kbase, vbase, qb, vt, a.scale_log2, lane);
@@ -390,11 +400,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
 // its query began in an earlier range, else slot 2w + 1 (its query goes on
 // into the next range).  A second, small kernel merges the cut pieces.
 
-// Tiles of 16 keys of row query r.
+// Tiles of 16 keys of row query r, on the 16-key grid from the tile that
+// holds its first visible key (the window's start).
 __device__ __forceinline__ uint32_t row_tiles(const RowArgs &a, uint32_t r) {
   const uint32_t i = a.qlist ? a.qlist[r] : r;
   uint32_t seq;
-  return ceil_div_u(visible_keys(a.plan, i, a.causal, &seq), 16u);
+  const uint32_t n = visible_keys(a.plan, i, a.causal, &seq);
+  return ceil_div_u(n, 16u) - window_lo(n, a.window) / 16u;
 }
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t lane) {
@@ -506,14 +518,17 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
     uint32_t seq;
     const uint32_t n = __builtin_amdgcn_readfirstlane(visible_keys(a.plan, i, a.causal, &seq));
     seq = __builtin_amdgcn_readfirstlane(seq);
-    const uint32_t t_hi = tt1 * 16u < n ? tt1 * 16u : n;
+    const uint32_t lo = window_lo(n, a.window);
+    const uint32_t tb = lo / 16u;  // tile tt of the query is grid tile tb + tt
+    const uint32_t t_hi = (tb + tt1) * 16u < n ? (tb + tt1) * 16u : n;
 
     uint4 qb[KS];
     load_q<DT, D>(qb, a, i, h0, nh, lane);
     WaveState<D> st;
     reset_state<D>(st);
     TileMap<PU> map;
-    init_map<PU>(map, a, seq, tt0 * 16u, t_hi, 0u, 1u);
+    init_map<PU>(map, a, seq, (tb + tt0) * 16u, t_hi, 0u, 1u);
+    map.lo = lo;
     stream_tiles<DT, D, PU>(st, map, tt1 - tt0, a, kbase, vbase, qb, vt, a.scale_log2, lane);
 
     const float lsum = rows4_sum(st.lsum);

@@ -110,4 +110,10 @@ __device__ __forceinline__ uint32_t visible_keys(const PlanView &p, uint32_t i, 
 
 __device__ __forceinline__ uint32_t ceil_div_u(uint32_t a, uint32_t b) { return a / b + (a % b != 0); }
 
+// First visible key under a sliding window: the last `window` of the visible
+// keys [0, n) stay, [n - window, n); window 0 keeps them all.
+__device__ __forceinline__ uint32_t window_lo(uint32_t n, uint32_t window) {
+  return window != 0u && n > window ? n - window : 0u;
+}
+
 }  // namespace pkv

@@ -25,6 +25,7 @@ struct RowArgs {
   uint32_t hq, hkv, d, dv, pdim;  // pdim: MLA position dim, 0 for attention
   uint32_t splits, pages_per_split;
   int causal;
+  uint32_t window;   // > 0: only the last `window` visible keys (0 = all)
   float scale_log2;  // scale * log2(e): scores are kept in base 2
   const void *q, *k, *v;     // MLA: k = v = latent
   const void *qp, *kp;       // MLA position parts (null for attention)
@@ -48,6 +49,7 @@ struct MergeArgs {
   uint32_t n_queries;
   uint32_t hq, hkv, dv, splits, pages_per_split;
   int causal;
+  uint32_t window;
   const float *ws_o, *ws_lse;
   void *out;
   const uint32_t *bal_rec;  // balanced schedule (bal_waves > 0), as in RowArgs

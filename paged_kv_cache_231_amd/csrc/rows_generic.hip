@@ -34,8 +34,10 @@ __global__ __launch_bounds__(64) void rows_generic_kernel(RowArgs a) {
   uint32_t seq;
   const uint32_t n = visible_keys(a.plan, i, a.causal, &seq);
   const uint64_t span = uint64_t(a.pages_per_split) * a.plan.ps;
-  const uint64_t t0 = uint64_t(part) * span;
-  const uint64_t t1 = t0 + span < n ? t0 + span : uint64_t(n);
+  const uint64_t lo = window_lo(n, a.window);
+  const uint64_t p0 = uint64_t(part) * span;
+  const uint64_t t0 = p0 > lo ? p0 : lo;
+  const uint64_t t1 = p0 + span < n ? p0 + span : uint64_t(n);
   if (a.splits > 1 && t0 >= t1) return;  // empty part: the merge skips it
 
   const uint32_t g = h / (a.hq / a.hkv);
@@ -135,7 +137,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const uint32_t used_pages = ceil_div_u(n, a.plan.ps);
   uint32_t parts = ceil_div_u(used_pages, a.pages_per_split);
   if (parts > a.splits) parts = a.splits;
-  const uint64_t base = uint64_t(i) * a.splits;
+  // parts wholly before the window are empty: skip them
+  const uint32_t first = window_lo(n, a.window) / a.plan.ps / a.pages_per_split;
+  parts = parts > first ? parts - first : 0u;
+  const uint64_t base = uint64_t(i) * a.splits + first;
 
   const float lse = tid < parts ? a.ws_lse[(base + tid) * a.hq + h] : -INFINITY;
   float mx = wave_max(fmaxf(lse, kNoMax));
