@@ -13,10 +13,12 @@ Modules
   plan       an independent encoder/decoder of the u32 plan words (spec v1)
   append     the cache append: write targets, validate_writes, the copy-on-
              write report (``DevicePlan::append_with_report``)
+  fp8        attention over an FP8 E4M3 byte cache with per-cache scales
 
 Pins: every function here is checked by the ``-m "not gpu"`` tests in
-``tests/test_oracle_pins.py``, ``tests/test_oracle_plan.py`` and
-``tests/test_oracle_append.py`` against
+``tests/test_oracle_pins.py``, ``tests/test_oracle_plan.py``,
+``tests/test_oracle_append.py``, ``tests/test_oracle_window.py`` and
+``tests/test_oracle_fp8.py`` against
 closed forms, brute force, a library routine (torch SDPA in float64) and
 hand-derived golden word lists; none is "parity unpinned".
 """
@@ -34,6 +36,7 @@ from .reference import (  # noqa: F401
     mla_one,
 )
 from .plan import encode_plan, decode_plan, PlanError  # noqa: F401
+from .fp8 import e4m3_decode, paged_attention_fp8, attention_one_fp8  # noqa: F401
 from .append import (  # noqa: F401
     WriteConflict,
     write_targets,
