@@ -258,6 +258,42 @@ def window_measure(torch, pkv, workloads, steps: int, window: int = 1024):
             "bytes_per_launch": nbytes, "workload": f"{wl.name}, window {window}, balanced"}
 
 
+def fp8_measure(torch, pkv, workloads, steps: int, k_scale: float = 0.05, v_scale: float = 0.04):
+    """Decode over an FP8 E4M3 cache: the packed-decode workload with its K/V
+    quantised to one byte per element, balanced schedule; bytes = the visible
+    cache bytes (1 per element), each read once."""
+    wl = workloads.config(2)
+    k8, v8 = workloads.fp8_caches(wl, k_scale, v_scale)
+    k8, v8 = k8.to("cuda"), v8.to("cuda")
+    q = wl.tensors["q"].to("cuda")
+    stream = torch.cuda.current_stream()
+    plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
+    hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
+    out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
+    ws = pkv.Workspace(wl.queries, hq, dv, 0)
+
+    def step():
+        pkv.attention_fp8(plan, q, k8, v8, wl.scale, k_scale, v_scale, wl.causal, workspace=ws,
+                          out=out)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    plan.timing(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    n, ms = plan.timing_read("rows")
+    plan.timing(False)
+    nbytes = int(wl.visible().sum()) * hkv * (d + dv)
+    avg_us = ms / max(1, n) * 1e3
+    gbs = nbytes / (avg_us * 1e-6) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "split-KV decode, FP8 E4M3 cache",
+            "avg_launch_us": round(avg_us, 2), "launches": n, "bytes_per_launch": nbytes,
+            "workload": f"{wl.name}, K/V as FP8 E4M3 bytes, balanced"}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -364,6 +400,7 @@ def main():
         line["prefill"] = prefill_measure(torch, pkv, workloads, args.prefill_steps)
         line["append"] = append_measure(torch, pkv, workloads, args.prefill_steps)
         line["window"] = window_measure(torch, pkv, workloads, args.prefill_steps)
+        line["fp8"] = fp8_measure(torch, pkv, workloads, args.prefill_steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

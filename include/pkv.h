@@ -265,6 +265,27 @@ pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype,
                                 float scale, int causal, uint32_t window,
                                 pkv_workspace *ws, void *stream);
 
+/* Attention over an 8-bit KV cache (the libmir-cuda graph page keeps K and
+ * V as byte buffers, `DeviceBuffer<u8>`, next to bf16 queries and outputs;
+ * the encoding is not shown).  Each cache element is one OCP FP8 E4M3 byte
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+ * infinity, S.1111.111 = NaN), scaled by one f32 per cache:
+ *   key = e4m3(k byte) * k_scale, value = e4m3(v byte) * v_scale
+ * and the result is that of pkv_attention_window on those keys and values.
+ *   q [Q, q_heads, head_dim] and out [Q, q_heads, value_dim]: F16 or BF16
+ *   k [N, ps, kv_heads, head_dim], v [N, ps, kv_heads, value_dim]: bytes
+ * head_dim == value_dim in {64, 128, 256}; q, k, v 16-byte aligned.  Every
+ * query runs on the decode MFMA kernels (which widen the bytes exactly to
+ * the query type in LDS), with split, balanced or no workspace.  Errors: as
+ * pkv_attention; PKV_EINVAL for F32 queries, scales not finite and > 0 or
+ * misaligned tensors; PKV_ESHAPE for other head dims. */
+pkv_status pkv_attention_fp8(const pkv_plan *plan, pkv_dtype dtype,
+                             const void *q, const void *k, const void *v,
+                             void *out, uint32_t q_heads, uint32_t kv_heads,
+                             uint32_t head_dim, uint32_t value_dim, float scale,
+                             float k_scale, float v_scale, int causal,
+                             uint32_t window, pkv_workspace *ws, void *stream);
+
 /* MLA (`DevicePlan::mla` doc): one shared latent head is both key and value;
  * a position part only adds to the score:
  *   x_t = scale * (<q_abs[i,h,:], latent_t> + <q_pos[i,h,:], k_pos_t>)

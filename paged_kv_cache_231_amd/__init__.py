@@ -27,7 +27,7 @@ import torch
 
 from ._lib import LIB_PATH, AppendReport, PKVError, STATUS, check, lib  # noqa: F401
 
-__all__ = ["Plan", "Workspace", "attention", "mla", "append", "encode_plan", "validate_plan",
+__all__ = ["Plan", "Workspace", "attention", "attention_fp8", "mla", "append", "encode_plan", "validate_plan",
            "validate_writes", "suggest_splits", "PKVError", "LIB_PATH", "lib", "HEADER_WORDS",
            "MAX_SPLITS"]
 
@@ -305,6 +305,37 @@ def attention(plan: Plan, q, k, v, scale: float, causal: bool = True, workspace=
         check(lib().pkv_attention(plan.handle, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   out.data_ptr(), hq, hkv, d, dv, float(scale),
                                   int(bool(causal)), ws, ctypes.c_void_p(plan.stream)))
+    return out
+
+
+def attention_fp8(plan: Plan, q, k8, v8, scale: float, k_scale: float, v_scale: float,
+                  causal: bool = True, workspace=None, out=None, window: int = 0):
+    """Attention over an FP8 E4M3 cache (pkv_attention_fp8): k8 / v8 are
+    uint8 tensors [N, ps, Hkv, D] of E4M3 codes, keys = decode * k_scale,
+    values = decode * v_scale; q and out F16 or BF16.  Returns ``out``."""
+    if q.dim() != 3 or k8.dim() != 4 or v8.dim() != 4:
+        raise PKVError("EINVAL", "q must be 3-D and the caches 4-D")
+    if k8.dtype != torch.uint8 or v8.dtype != torch.uint8:
+        raise PKVError("EINVAL", "FP8 caches are uint8 tensors of E4M3 codes")
+    qn, hq, d = q.shape
+    n, ps, hkv, dk = k8.shape
+    dv = v8.shape[3]
+    if qn != plan.queries or n != plan.pages or ps != plan.page_size or dk != d \
+            or tuple(v8.shape[:3]) != (n, ps, hkv):
+        raise PKVError("ESHAPE", "head counts, head dims or tensor shapes do not fit together")
+    if out is None:
+        out = torch.empty((qn, hq, dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (qn, hq, dv):
+        raise PKVError("ESHAPE", "head counts, head dims or tensor shapes do not fit together")
+    code = _dtype_code(q, out)
+    for t in (k8, v8):
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise PKVError("EINVAL", "operands must be contiguous device tensors of one float dtype on one device")
+    check(lib().pkv_attention_fp8(plan.handle, code, q.data_ptr(), k8.data_ptr(), v8.data_ptr(),
+                                  out.data_ptr(), hq, hkv, d, dv, float(scale), float(k_scale),
+                                  float(v_scale), int(bool(causal)), int(window),
+                                  workspace.handle if workspace is not None else None,
+                                  ctypes.c_void_p(plan.stream)))
     return out
 
 

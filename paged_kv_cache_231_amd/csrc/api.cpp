@@ -143,7 +143,10 @@ class Timed {
 
 // Waves per CU of a balanced launch: one per SIMD.  Fewer concurrent page
 // streams keep more DRAM rows open; 8 or 12 waves per CU measured slower.
+// An FP8 cache moves half the bytes per tile, so it keeps two waves per SIMD
+// to have as many bytes in flight.
 constexpr uint32_t kBalancedWavesPerCu = 4;
+constexpr uint32_t kBalancedWavesPerCuFp8 = 8;
 
 // Resident waves per CU of the balanced kernel, cached per (dtype, d, page
 // uniformity); 0 for shapes it does not take.
@@ -172,7 +175,8 @@ uint32_t balanced_waves(const RowArgs &ra, pkv_dtype dt, const pkv_workspace *ws
   const uint64_t segq = uint64_t(ra.hkv) * ((grp + 15) / 16);
   const uint64_t max_tiles = (uint64_t(ra.plan.W) * ra.plan.ps + 15) / 16;
   if (uint64_t(ra.n_queries) * max_tiles >= (1ull << 31)) return 0;
-  const uint64_t per_cu = std::min<uint64_t>(kBalancedWavesPerCu, bal_waves_per_cu(ra.d, ra.plan.ps, dt));
+  const uint64_t per_cu = std::min<uint64_t>(ra.kv_fp8 ? kBalancedWavesPerCuFp8 : kBalancedWavesPerCu,
+                                             bal_waves_per_cu(ra.d, ra.plan.ps, dt));
   uint64_t w = std::min<uint64_t>(ws->max_waves, per_cu * ws->cus);
   w -= w % 4;
   if (segq > w) return 0;  // not one group of segq waves
@@ -216,6 +220,8 @@ pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_wo
     if (rows_mfma_blocks(ra) * 256u > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
     Timed t(plan, PKV_KERNEL_ROWS, st);
     e = launch_rows_mfma(ra, dt, st);
+  } else if (ra.kv_fp8) {
+    return fail(PKV_ESHAPE, "an FP8 cache needs head_dim == value_dim in {64, 128, 256}");
   } else if (rows_fast_supported(ra, dt)) {
     if (uint64_t(ra.n_queries) * ra.hq * ra.splits * 256u > kU32Max)
       return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
@@ -444,7 +450,7 @@ pkv_status pkv_workspace_create_balanced(uint32_t queries, uint32_t heads, uint3
   for (pkv_dtype dt : {PKV_F16, PKV_BF16})
     for (uint32_t ps : {16u, 3u})
       per_cu = std::max<uint32_t>(per_cu, uint32_t(bal_waves_per_cu(dv, ps, dt)));
-  per_cu = std::min(per_cu, kBalancedWavesPerCu);
+  per_cu = std::min(per_cu, std::max(kBalancedWavesPerCu, kBalancedWavesPerCuFp8));
   const uint64_t waves = uint64_t(per_cu) * uint32_t(cus);
   const uint64_t rows = 2 * waves * 16;  // two 16-head slots per wave
   const uint64_t bytes = rows * (uint64_t(dv) + 1) * sizeof(float) + (2 * uint64_t(queries) + 1) * 4;
@@ -572,18 +578,15 @@ uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads, uint32_t kv_
   return best_s;
 }
 
-pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, const void *k,
-                         const void *v, void *out, uint32_t hq, uint32_t hkv, uint32_t d,
-                         uint32_t dv, float scale, int causal, pkv_workspace *ws, void *stream) {
-  return pkv_attention_window(plan, dtype, q, k, v, out, hq, hkv, d, dv, scale, causal, 0u, ws,
-                              stream);
-}
+}  // extern "C"
 
-pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype, const void *q,
-                                const void *k, const void *v, void *out, uint32_t hq,
-                                uint32_t hkv, uint32_t d, uint32_t dv, float scale, int causal,
-                                uint32_t window, pkv_workspace *ws, void *stream_) {
-  clear_error();
+namespace pkv {
+namespace {
+
+pkv_status attention_impl(const pkv_plan *plan, pkv_dtype dtype, bool fp8, const void *q,
+                          const void *k, const void *v, void *out, uint32_t hq, uint32_t hkv,
+                          uint32_t d, uint32_t dv, float scale, float k_scale, float v_scale,
+                          int causal, uint32_t window, pkv_workspace *ws, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (!plan) return fail(PKV_EINVAL, "null plan");
   if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
@@ -591,6 +594,16 @@ pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype, const voi
   if (hq == 0 || hkv == 0 || hq % hkv != 0 || d == 0 || dv == 0 || d > 1024 || dv > 1024)
     return fail(PKV_ESHAPE, "head counts, head dims or tensor shapes do not fit together");
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PKV_EINVAL, "scale must be finite and positive");
+  if (fp8) {
+    if (dtype == PKV_F32) return fail(PKV_EINVAL, "an FP8 cache needs F16 or BF16 queries");
+    if (d != dv || (d != 64 && d != 128 && d != 256))
+      return fail(PKV_ESHAPE, "an FP8 cache needs head_dim == value_dim in {64, 128, 256}");
+    if (!std::isfinite(k_scale) || k_scale <= 0.f || !std::isfinite(v_scale) || v_scale <= 0.f)
+      return fail(PKV_EINVAL, "FP8 cache scales must be finite and positive");
+    if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+          reinterpret_cast<uintptr_t>(v)) & 15u) != 0)
+      return fail(PKV_EINVAL, "an FP8 cache needs 16-byte aligned q, k and v");
+  }
   const PlanLayout &L = plan->L;
   if (!u32_elems({L.Q, hq, d}) || !u32_elems({L.N, L.ps, hkv, d}) || !u32_elems({L.N, L.ps, hkv, dv}) ||
       !u32_elems({L.Q, hq, dv}))
@@ -602,11 +615,11 @@ pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype, const voi
   if (L.Q == 0) return PKV_OK;
   const bool have_cache = uint64_t(L.N) * L.ps > 0;
   if (!q || !out || (have_cache && (!k || !v))) return fail(PKV_EINVAL, "null tensor pointer");
-  const uint64_t es = elem_size(dtype);
+  const uint64_t es = elem_size(dtype), ces = fp8 ? 1 : es;  // query / cache element bytes
   const uint64_t out_b = uint64_t(L.Q) * hq * dv * es;
   if (overlaps(out, out_b, q, uint64_t(L.Q) * hq * d * es) ||
-      overlaps(out, out_b, k, uint64_t(L.N) * L.ps * hkv * d * es) ||
-      overlaps(out, out_b, v, uint64_t(L.N) * L.ps * hkv * dv * es))
+      overlaps(out, out_b, k, uint64_t(L.N) * L.ps * hkv * d * ces) ||
+      overlaps(out, out_b, v, uint64_t(L.N) * L.ps * hkv * dv * ces))
     return fail(PKV_EINVAL, "output overlaps an input");
 
   RowArgs ra{};
@@ -618,7 +631,9 @@ pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype, const voi
   ra.pdim = 0;
   ra.causal = causal ? 1 : 0;
   ra.window = window;
-  ra.scale_log2 = scale * kLog2e;
+  ra.scale_log2 = scale * kLog2e * (fp8 ? k_scale : 1.f);
+  ra.kv_fp8 = fp8 ? 1u : 0u;
+  ra.v_scale = fp8 ? v_scale : 1.f;
   ra.q = q;
   ra.k = k;
   ra.v = v;
@@ -650,8 +665,9 @@ pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype, const voi
   ta.v_page = ra.v_page;
   ta.v_tok = ra.v_tok;
   ta.out = out;
-  // the tile kernel has no window: with one, every query runs as a row
-  const bool use_tiles = L.T > 0 && window == 0 && tiles_supported(ta, dtype);
+  // the tile kernel has no window and no FP8 cache: with either, every
+  // query runs as a row
+  const bool use_tiles = L.T > 0 && window == 0 && !fp8 && tiles_supported(ta, dtype);
   ra.qlist = use_tiles ? plan->dev + L.rows : nullptr;
   ra.n_queries = use_tiles ? L.R : L.Q;
 
@@ -665,6 +681,37 @@ pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype, const voi
     if (e != hipSuccess) return hip_fail(e);
   }
   return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" {
+
+pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q, const void *k,
+                         const void *v, void *out, uint32_t hq, uint32_t hkv, uint32_t d,
+                         uint32_t dv, float scale, int causal, pkv_workspace *ws, void *stream) {
+  clear_error();
+  return attention_impl(plan, dtype, false, q, k, v, out, hq, hkv, d, dv, scale, 1.f, 1.f, causal,
+                        0u, ws, stream);
+}
+
+pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype, const void *q,
+                                const void *k, const void *v, void *out, uint32_t hq,
+                                uint32_t hkv, uint32_t d, uint32_t dv, float scale, int causal,
+                                uint32_t window, pkv_workspace *ws, void *stream) {
+  clear_error();
+  return attention_impl(plan, dtype, false, q, k, v, out, hq, hkv, d, dv, scale, 1.f, 1.f, causal,
+                        window, ws, stream);
+}
+
+pkv_status pkv_attention_fp8(const pkv_plan *plan, pkv_dtype dtype, const void *q, const void *k,
+                             const void *v, void *out, uint32_t hq, uint32_t hkv, uint32_t d,
+                             uint32_t dv, float scale, float k_scale, float v_scale, int causal,
+                             uint32_t window, pkv_workspace *ws, void *stream) {
+  clear_error();
+  return attention_impl(plan, dtype, true, q, k, v, out, hq, hkv, d, dv, scale, k_scale, v_scale,
+                        causal, window, ws, stream);
 }
 
 pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k, const void *new_v,
@@ -775,6 +822,7 @@ pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs, con
   ra.d = rank;
   ra.dv = rank;
   ra.pdim = pos_dim;
+  ra.v_scale = 1.f;
   ra.causal = causal ? 1 : 0;
   ra.scale_log2 = scale * kLog2e;
   ra.q = q_abs;

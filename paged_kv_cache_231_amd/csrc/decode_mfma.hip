@@ -48,15 +48,35 @@ struct Lds {
 // K/V rows of one 16-token tile as loaded from the cache: each load
 // instruction covers RPI whole rows (CPR 16-byte chunks each, lane l taking
 // row RPI*n + l/CPR, chunk l%CPR), read with the streaming hint.  Whole-row
-// instructions keep HBM busy; the MFMA layouts are produced from LDS.
-template <int D>
+// instructions keep HBM busy; the MFMA layouts are produced from LDS.  F8:
+// the cache holds one FP8 E4M3 byte per element (half the chunks per row,
+// twice the rows per instruction); rows are widened to the query type when
+// staged.
+template <int D, bool F8>
 struct TileRegs {
-  static constexpr int KS = D / 32;    // loads per lane per tensor
-  static constexpr int CPR = D / 8;    // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR; // rows per load instruction
-  uint4 k[KS], v[KS];
+  static constexpr int EB = F8 ? 1 : 2;     // bytes per cache element
+  static constexpr int CPR = D * EB / 16;   // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;      // rows per load instruction
+  static constexpr int NL = 16 / RPI;       // loads per lane per tensor
+  uint4 k[NL], v[NL];
   uint32_t valid16;  // bit r: token r of the tile exists
 };
+
+// Two FP8 E4M3 codes (bytes 0, 1 or 2, 3 of x) widened exactly to the query
+// type (every E4M3 value is a bf16 and an f16 value); the hardware scale
+// operand is 1.
+template <class DT>
+__device__ __forceinline__ uint32_t widen_f8(uint32_t x, bool hi);
+template <>
+__device__ __forceinline__ uint32_t widen_f8<BF16>(uint32_t x, bool hi) {
+  return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true))
+            : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_f8<F16>(uint32_t x, bool hi) {
+  return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true))
+            : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
+}
 
 // Where the tokens of the wave's tiles live.  With PAGE_UNIFORM (page size a
 // power of two >= 16) every tile lies inside one page; the page numbers of
@@ -83,12 +103,12 @@ struct TileMap {
   }
 };
 
-template <class DT, int D, bool PU>
-__device__ __forceinline__ void load_tile(TileRegs<D> &t, const RowArgs &a, TileMap<PU> &map,
-                                          const typename DT::T *kbase,
-                                          const typename DT::T *vbase, uint32_t k,
+template <class DT, int D, bool PU, bool F8>
+__device__ __forceinline__ void load_tile(TileRegs<D, F8> &t, const RowArgs &a, TileMap<PU> &map,
+                                          const unsigned char *kbase,
+                                          const unsigned char *vbase, uint32_t k,
                                           uint32_t lane) {
-  using TR = TileRegs<D>;
+  using TR = TileRegs<D, F8>;
   const uint32_t t0 = map.tile_start(k);
   const uint32_t chunk = lane % TR::CPR;
   // A row past the end reads row 0 of page 0 (inside the pool whenever any
@@ -105,18 +125,18 @@ __device__ __forceinline__ void load_tile(TileRegs<D> &t, const RowArgs &a, Tile
     t.valid16 = page_ok && before < 16u ? ((1u << rows) - 1u) & ~((1u << before) - 1u) : 0u;
     const uint32_t slot0 = t0 & (map.ps - 1);
 #pragma unroll
-    for (int n = 0; n < TR::KS; ++n) {
+    for (int n = 0; n < TR::NL; ++n) {
       const uint32_t r = TR::RPI * n + lane / TR::CPR;
       const bool ok = page_ok && r < rows;
       const uint32_t ko = ok ? page * uint32_t(a.k_page) + (slot0 + r) * uint32_t(a.k_tok) : 0u;
       const uint32_t vo = ok ? page * uint32_t(a.v_page) + (slot0 + r) * uint32_t(a.v_tok) : 0u;
-      t.k[n] = load_stream16(kbase + ko + 8u * chunk);
-      t.v[n] = load_stream16(vbase + vo + 8u * chunk);
+      t.k[n] = load_stream16(kbase + uint64_t(ko) * TR::EB + 16u * chunk);
+      t.v[n] = load_stream16(vbase + uint64_t(vo) * TR::EB + 16u * chunk);
     }
   } else {
     uint32_t valid = 0;
 #pragma unroll
-    for (int n = 0; n < TR::KS; ++n) {
+    for (int n = 0; n < TR::NL; ++n) {
       const uint32_t r = TR::RPI * n + lane / TR::CPR;
       const uint32_t tok = t0 + r;
       bool ok = tok >= map.lo && tok < map.t_hi;
@@ -127,8 +147,8 @@ __device__ __forceinline__ void load_tile(TileRegs<D> &t, const RowArgs &a, Tile
       valid |= ok ? 1u << r : 0u;
       const uint32_t ko = ok ? page * uint32_t(a.k_page) + slot * uint32_t(a.k_tok) : 0u;
       const uint32_t vo = ok ? page * uint32_t(a.v_page) + slot * uint32_t(a.v_tok) : 0u;
-      t.k[n] = load_stream16(kbase + ko + 8u * chunk);
-      t.v[n] = load_stream16(vbase + vo + 8u * chunk);
+      t.k[n] = load_stream16(kbase + uint64_t(ko) * TR::EB + 16u * chunk);
+      t.v[n] = load_stream16(vbase + uint64_t(vo) * TR::EB + 16u * chunk);
     }
     // every lane knows the rows it loaded; OR them across the wave
     uint32_t all = valid;
@@ -146,26 +166,44 @@ struct WaveState {
   float m, lsum;
 };
 
-template <class DT, int D>
-__device__ __forceinline__ void attend_tile(WaveState<D> &st, const TileRegs<D> &t,
+template <class DT, int D, bool F8>
+__device__ __forceinline__ void attend_tile(WaveState<D> &st, const TileRegs<D, F8> &t,
                                             const uint4 *qb, unsigned char *vt, float sl2,
                                             uint32_t lane) {
   using M = Mfma<DT>;
   using L = Lds<D>;
   constexpr int KS = D / 32, DB = D / 16;
   const uint32_t c16 = lane & 15u, j = lane >> 4;
-  // stage the K and V rows (same byte layout as the cache rows); rows past
+  // stage the K and V rows in the query type (the cache rows' byte layout;
+  // FP8 rows widened, each 16-byte chunk of codes to two chunks); rows past
   // the end get zero V
-  using TR = TileRegs<D>;
+  using TR = TileRegs<D, F8>;
   unsigned char *kt = vt;
   unsigned char *vtile = vt + kTile * L::kRow;
 #pragma unroll
-  for (int n = 0; n < KS; ++n) {
+  for (int n = 0; n < TR::NL; ++n) {
     const uint32_t r = TR::RPI * n + lane / TR::CPR;
-    const uint32_t off = r * L::kRow + 16u * (lane % TR::CPR);
-    *reinterpret_cast<uint4 *>(kt + off) = t.k[n];
-    *reinterpret_cast<uint4 *>(vtile + off) =
-        ((t.valid16 >> r) & 1u) ? t.v[n] : make_uint4(0, 0, 0, 0);
+    const bool keep = (t.valid16 >> r) & 1u;
+    if constexpr (F8) {
+      const uint32_t off = r * L::kRow + 32u * (lane % TR::CPR);
+      const uint4 kw = t.k[n], vw = t.v[n];
+      *reinterpret_cast<uint4 *>(kt + off) =
+          make_uint4(widen_f8<DT>(kw.x, false), widen_f8<DT>(kw.x, true),
+                     widen_f8<DT>(kw.y, false), widen_f8<DT>(kw.y, true));
+      *reinterpret_cast<uint4 *>(kt + off + 16) =
+          make_uint4(widen_f8<DT>(kw.z, false), widen_f8<DT>(kw.z, true),
+                     widen_f8<DT>(kw.w, false), widen_f8<DT>(kw.w, true));
+      const uint4 v0 = make_uint4(widen_f8<DT>(vw.x, false), widen_f8<DT>(vw.x, true),
+                                  widen_f8<DT>(vw.y, false), widen_f8<DT>(vw.y, true));
+      const uint4 v1 = make_uint4(widen_f8<DT>(vw.z, false), widen_f8<DT>(vw.z, true),
+                                  widen_f8<DT>(vw.w, false), widen_f8<DT>(vw.w, true));
+      *reinterpret_cast<uint4 *>(vtile + off) = keep ? v0 : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(vtile + off + 16) = keep ? v1 : make_uint4(0, 0, 0, 0);
+    } else {
+      const uint32_t off = r * L::kRow + 16u * (lane % TR::CPR);
+      *reinterpret_cast<uint4 *>(kt + off) = t.k[n];
+      *reinterpret_cast<uint4 *>(vtile + off) = keep ? t.v[n] : make_uint4(0, 0, 0, 0);
+    }
   }
 
   // S^T = K . Q^T : A = K[token c16][chunk 4ks + j]; rows = tokens 4j+0..3,
@@ -235,37 +273,37 @@ __device__ __forceinline__ void reset_state(WaveState<D> &st) {
 // steady-state loop issues its loads unconditionally, so the wait before
 // each tile covers only that tile's loads; page numbers are refilled once
 // per 64 tiles, outside the loop.
-template <class DT, int D, bool PU>
+template <class DT, int D, bool PU, bool F8>
 __device__ __forceinline__ void stream_tiles(WaveState<D> &st, TileMap<PU> &map,
                                              uint32_t n_tiles, const RowArgs &a,
-                                             const typename DT::T *kbase,
-                                             const typename DT::T *vbase, const uint4 *qb,
+                                             const unsigned char *kbase,
+                                             const unsigned char *vbase, const uint4 *qb,
                                              unsigned char *vt, float sl2, uint32_t lane) {
-  TileRegs<D> ta, tb;
+  TileRegs<D, F8> ta, tb;
   for (uint32_t c0 = 0; c0 < n_tiles; c0 += 64) {
     const uint32_t cn = n_tiles - c0 < 64u ? n_tiles - c0 : 64u;
     map.fill(c0, lane);
     uint32_t k = 0;
     if (cn >= 4) {
-      load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0, lane);
-      load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + 1, lane);
+      load_tile<DT, D, PU, F8>(ta, a, map, kbase, vbase, c0, lane);
+      load_tile<DT, D, PU, F8>(tb, a, map, kbase, vbase, c0 + 1, lane);
       for (; k + 3 < cn; k += 2) {
-        attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
-        load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
-        attend_tile<DT, D>(st, tb, qb, vt, sl2, lane);
-        load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + k + 3, lane);
+        attend_tile<DT, D, F8>(st, ta, qb, vt, sl2, lane);
+        load_tile<DT, D, PU, F8>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
+        attend_tile<DT, D, F8>(st, tb, qb, vt, sl2, lane);
+        load_tile<DT, D, PU, F8>(tb, a, map, kbase, vbase, c0 + k + 3, lane);
       }
     } else {
-      load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0, lane);
-      if (cn > 1) load_tile<DT, D, PU>(tb, a, map, kbase, vbase, c0 + 1, lane);
+      load_tile<DT, D, PU, F8>(ta, a, map, kbase, vbase, c0, lane);
+      if (cn > 1) load_tile<DT, D, PU, F8>(tb, a, map, kbase, vbase, c0 + 1, lane);
     }
     // at most three tiles left: k in ta, k + 1 in tb
     if (k < cn) {
-      attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
-      if (k + 2 < cn) load_tile<DT, D, PU>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
+      attend_tile<DT, D, F8>(st, ta, qb, vt, sl2, lane);
+      if (k + 2 < cn) load_tile<DT, D, PU, F8>(ta, a, map, kbase, vbase, c0 + k + 2, lane);
     }
-    if (k + 1 < cn) attend_tile<DT, D>(st, tb, qb, vt, sl2, lane);
-    if (k + 2 < cn) attend_tile<DT, D>(st, ta, qb, vt, sl2, lane);
+    if (k + 1 < cn) attend_tile<DT, D, F8>(st, tb, qb, vt, sl2, lane);
+    if (k + 2 < cn) attend_tile<DT, D, F8>(st, ta, qb, vt, sl2, lane);
   }
 }
 
@@ -286,7 +324,7 @@ __device__ __forceinline__ void init_map(TileMap<PU> &map, const RowArgs &a, uin
   map.lo = 0;
 }
 
-template <class DT, int D, bool PU>
+template <class DT, int D, bool PU, bool F8>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
   using M = Mfma<DT>;
   constexpr int KS = D / 32;  // 32-wide K steps of q.k (also 16-byte chunks per lane per row)
@@ -331,15 +369,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
   WaveState<D> st;
   reset_state<D>(st);
 
-  const typename DT::T *kbase = static_cast<const typename DT::T *>(a.k) + uint64_t(kvh) * D;
-  const typename DT::T *vbase = static_cast<const typename DT::T *>(a.v) + uint64_t(kvh) * D;
+  constexpr uint32_t EB = F8 ? 1u : 2u;  // bytes per cache element
+  const unsigned char *kbase = static_cast<const unsigned char *>(a.k) + uint64_t(kvh) * D * EB;
+  const unsigned char *vbase = static_cast<const unsigned char *>(a.v) + uint64_t(kvh) * D * EB;
   unsigned char *vt = lds + wv * L::kTileBytes;  // this wave's V tile
   TileMap<PU> map;
   init_map<PU>(map, a, seq, t_lo, t_hi, wv, 4u);
   map.lo = lo;
   const uint32_t first = t_lo + wv * 16u;
   const uint32_t n_tiles = first < t_hi ? (t_hi - first + 63u) / 64u : 0u;
-  stream_tiles<DT, D, PU>(st, map, n_tiles, a, kbase, vbase, qb, vt, a.scale_log2, lane);
+  stream_tiles<DT, D, PU, F8>(st, map, n_tiles, a, kbase, vbase, qb, vt, a.scale_log2, lane);
 
   // per-head sum over the four lane groups (m is already uniform across them)
   const float lsum = rows4_sum(st.lsum);
@@ -369,7 +408,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
       num = fmaf(so[(w * kHeads + h) * L::kOStride + d], sc, num);
       den = fmaf(s_l[w][h], sc, den);
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const float inv = den > 0.f ? a.v_scale / den : 0.f;  // v_scale: FP8 value cache
     if (a.splits == 1) {
       auto *out = static_cast<uint16_t *>(a.out) + (uint64_t(i) * a.hq + h0 + h) * D;
       out[d] = M::from_f(num * inv);
@@ -440,7 +479,7 @@ __device__ __forceinline__ void scan_chunk(Chunk &c, const RowArgs &a, uint32_t 
 // Launched with one block of four waves per CU (one wave per SIMD): fewer
 // concurrent page streams keep more DRAM rows open, and more waves per CU
 // or a third tile in flight per wave measured no faster.
-template <class DT, int D, bool PU>
+template <class DT, int D, bool PU, bool F8>
 __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
   using M = Mfma<DT>;
   constexpr int KS = D / 32;
@@ -500,8 +539,9 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
   const uint32_t kvh = g / hgk, sub = g % hgk;
   const uint32_t h0 = kvh * grp + sub * kHeads;
   const uint32_t nh = grp - sub * kHeads < kHeads ? grp - sub * kHeads : kHeads;
-  const typename DT::T *kbase = static_cast<const typename DT::T *>(a.k) + uint64_t(kvh) * D;
-  const typename DT::T *vbase = static_cast<const typename DT::T *>(a.v) + uint64_t(kvh) * D;
+  constexpr uint32_t EB = F8 ? 1u : 2u;  // bytes per cache element
+  const unsigned char *kbase = static_cast<const unsigned char *>(a.k) + uint64_t(kvh) * D * EB;
+  const unsigned char *vbase = static_cast<const unsigned char *>(a.v) + uint64_t(kvh) * D * EB;
 
   while (t < t_end) {
     if (qi - ch.base >= 64u) scan_chunk(ch, a, ch.base + 64u, ch.end, lane);
@@ -529,10 +569,10 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
     TileMap<PU> map;
     init_map<PU>(map, a, seq, (tb + tt0) * 16u, t_hi, 0u, 1u);
     map.lo = lo;
-    stream_tiles<DT, D, PU>(st, map, tt1 - tt0, a, kbase, vbase, qb, vt, a.scale_log2, lane);
+    stream_tiles<DT, D, PU, F8>(st, map, tt1 - tt0, a, kbase, vbase, qb, vt, a.scale_log2, lane);
 
     const float lsum = rows4_sum(st.lsum);
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;  // v_scale: FP8 value cache
     if (tt0 == 0u && tt1 == ntq) {
       if (c16 < nh) {
         uint16_t *orow = static_cast<uint16_t *>(a.out) + (uint64_t(i) * a.hq + h0 + c16) * D;
@@ -631,23 +671,23 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
   for (uint32_t d = tid, e = 0; d < a.dv && e < 4; d += 256, ++e) out[d] = DT::from_f(acc[e] * inv);
 }
 
-template <class DT, bool PU>
+template <class DT, bool PU, bool F8>
 hipError_t launch_d(const RowArgs &a, dim3 grid, hipStream_t st) {
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<DT, 64, PU>), grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<DT, 128, PU>), grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((decode_mfma_kernel<DT, 256, PU>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((decode_mfma_kernel<DT, 64, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((decode_mfma_kernel<DT, 128, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((decode_mfma_kernel<DT, 256, PU, F8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
 }
 
-template <class DT, bool PU>
+template <class DT, bool PU, bool F8>
 hipError_t launch_bal_d(const RowArgs &a, dim3 grid, hipStream_t st) {
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((decode_balanced_kernel<DT, 64, PU>), grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_balanced_kernel<DT, 128, PU>), grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((decode_balanced_kernel<DT, 256, PU>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((decode_balanced_kernel<DT, 64, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((decode_balanced_kernel<DT, 128, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((decode_balanced_kernel<DT, 256, PU, F8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
@@ -657,9 +697,9 @@ template <class DT, bool PU>
 int bal_blocks_per_cu(uint32_t d) {
   int blocks = 0;
   hipError_t e = hipErrorNotSupported;
-  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 64, PU>, 256, 0);
-  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 128, PU>, 256, 0);
-  if (d == 256) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 256, PU>, 256, 0);
+  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 64, PU, false>, 256, 0);
+  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 128, PU, false>, 256, 0);
+  if (d == 256) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<DT, 256, PU, false>, 256, 0);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
@@ -680,7 +720,7 @@ int rows_mfma_blocks_per_cu(const RowArgs &a, pkv_dtype dt) {
   int blocks = 0;
   hipError_t e = hipErrorNotSupported;
 #define PKV_OCC(DT, D, PU)                                                                  \
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma_kernel<DT, D, PU>, \
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma_kernel<DT, D, PU, false>, \
                                                    256, 0)
   if (dt == PKV_BF16) {
     if (a.d == 64) { if (pu) PKV_OCC(BF16, 64, true); else PKV_OCC(BF16, 64, false); }
@@ -708,8 +748,12 @@ hipError_t launch_rows_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
   // page size a power of two >= 16: every 16-token tile lies in one page
   const uint32_t ps = a.plan.ps;
   const bool pu = (ps & (ps - 1)) == 0 && ps >= 16u;
-  if (dt == PKV_BF16) return pu ? launch_d<BF16, true>(a, grid, st) : launch_d<BF16, false>(a, grid, st);
-  return pu ? launch_d<F16, true>(a, grid, st) : launch_d<F16, false>(a, grid, st);
+  if (a.kv_fp8) {
+    if (dt == PKV_BF16) return pu ? launch_d<BF16, true, true>(a, grid, st) : launch_d<BF16, false, true>(a, grid, st);
+    return pu ? launch_d<F16, true, true>(a, grid, st) : launch_d<F16, false, true>(a, grid, st);
+  }
+  if (dt == PKV_BF16) return pu ? launch_d<BF16, true, false>(a, grid, st) : launch_d<BF16, false, false>(a, grid, st);
+  return pu ? launch_d<F16, true, false>(a, grid, st) : launch_d<F16, false, false>(a, grid, st);
 }
 
 int balanced_waves_per_cu(uint32_t d, uint32_t ps, pkv_dtype dt) {
@@ -725,8 +769,12 @@ hipError_t launch_rows_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st) 
   const dim3 grid(a.bal_waves / kWaves);
   const uint32_t ps = a.plan.ps;
   const bool pu = (ps & (ps - 1)) == 0 && ps >= 16u;
-  if (dt == PKV_BF16) return pu ? launch_bal_d<BF16, true>(a, grid, st) : launch_bal_d<BF16, false>(a, grid, st);
-  return pu ? launch_bal_d<F16, true>(a, grid, st) : launch_bal_d<F16, false>(a, grid, st);
+  if (a.kv_fp8) {
+    if (dt == PKV_BF16) return pu ? launch_bal_d<BF16, true, true>(a, grid, st) : launch_bal_d<BF16, false, true>(a, grid, st);
+    return pu ? launch_bal_d<F16, true, true>(a, grid, st) : launch_bal_d<F16, false, true>(a, grid, st);
+  }
+  if (dt == PKV_BF16) return pu ? launch_bal_d<BF16, true, false>(a, grid, st) : launch_bal_d<BF16, false, false>(a, grid, st);
+  return pu ? launch_bal_d<F16, true, false>(a, grid, st) : launch_bal_d<F16, false, false>(a, grid, st);
 }
 
 hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, hipStream_t st) {

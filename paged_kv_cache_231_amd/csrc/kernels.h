@@ -26,7 +26,9 @@ struct RowArgs {
   uint32_t splits, pages_per_split;
   int causal;
   uint32_t window;   // > 0: only the last `window` visible keys (0 = all)
-  float scale_log2;  // scale * log2(e): scores are kept in base 2
+  float scale_log2;  // scale * log2(e) (* k_scale for an FP8 key cache): base-2 scores
+  uint32_t kv_fp8;   // K and V hold FP8 E4M3 bytes (decode MFMA kernels only)
+  float v_scale;     // output factor: the FP8 value cache's scale, else 1
   const void *q, *k, *v;     // MLA: k = v = latent
   const void *qp, *kp;       // MLA position parts (null for attention)
   uint64_t k_page, k_tok;    // k: page stride, token stride

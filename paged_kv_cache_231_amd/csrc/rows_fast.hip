@@ -285,7 +285,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 bool rows_fast_supported(const RowArgs &a, pkv_dtype dt) {
-  if (a.pdim != 0 || a.d != a.dv || a.window != 0) return false;  // no window here
+  if (a.pdim != 0 || a.d != a.dv || a.window != 0 || a.kv_fp8) return false;  // neither here
   if (a.d != 64 && a.d != 128 && a.d != 256) return false;
   if (dt != PKV_F32 && dt != PKV_F16 && dt != PKV_BF16) return false;
   if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v)) return false;

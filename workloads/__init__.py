@@ -175,6 +175,16 @@ def build_mla(name, seed, dtype, lens, queries, h, r, p, page_size, pool=None,
                     info=dict(h=h, r=r, p=p))
 
 
+def fp8_caches(wl: Workload, k_scale: float, v_scale: float):
+    """The workload's K and V as FP8 E4M3 byte codes (uint8 tensors):
+    round(k / k_scale), round(v / v_scale) to the nearest E4M3 value (torch's
+    float8_e4m3fn cast; NaN poison stays NaN).  Holds no attention
+    arithmetic: the caches are inputs."""
+    k = (wl.tensors["k"].float() / k_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    v = (wl.tensors["v"].float() / v_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return k.contiguous(), v.contiguous()
+
+
 def decode_queries(lens):
     """One query per sequence at its last position (packed decode)."""
     return [(s, int(L) - 1) for s, L in enumerate(lens)]
