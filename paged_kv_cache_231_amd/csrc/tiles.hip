@@ -301,8 +301,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     }
     block_sync_lds();
   };
-  // S^T of key tile kt for both 16-row halves and both N-tiles (four
-  // independent MFMA chains)
+  // S^T of key tile kt for both 16-row halves and both N-tiles: eight
+  // independent MFMA chains (even and odd k-steps apart), sixteen per SIMD
+  // with two waves, which keeps the 16x16x32 pipe full
   auto scores = [&](uint32_t kt, f32x4_t (&sc)[2][2]) {
     const unsigned char *kt_lds = lds + (kt % kStages) * L::kStage;
     uint4 ka[2][KS];
@@ -314,16 +315,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
         ka[mb][ks] = *reinterpret_cast<const uint4 *>(kt_lds + r * L::kRowB +
                                                       16u * ((4u * ks + j) ^ L::swz(r)));
     }
+    f32x4_t acc[2][2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sc[mb][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[mb][nt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sc[mb][nt] = M::qk(ka[mb][ks], qb[nt][ks], sc[mb][nt]);
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mb][nt][ks & 1] = M::qk(ka[mb][ks], qb[nt][ks], acc[mb][nt][ks & 1]);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) sc[mb][nt] = acc[mb][nt][0] + acc[mb][nt][1];
   };
 
   // Software pipeline: the scores of tile kt+1 are issued before the
@@ -367,6 +376,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     // with tile kt's softmax arithmetic.  After the last tile the scores
     // read a ring stage whose contents are not used (in bounds).
     f32x4_t s_next[2][2];
+    __builtin_amdgcn_s_setprio(1);
     scores(kt + 1, s_next);
     // online softmax (base 2); the max is taken on raw scores (scale > 0),
     // and each probability is exp2(score * scale_log2 - m) with one FMA
@@ -416,6 +426,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // O^T += V^T . P^T over the 32 keys: K slots 8j .. 8j+3 are key rows
     // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16
 #pragma unroll
