@@ -734,6 +734,7 @@ pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k, 
   st = validate_writes(plan->host.data(), L);
   if (st != PKV_OK) return st;
   if (L.Q == 0) return PKV_OK;  // a no-op append copies nothing
+  if (L.Q > 0x7FFFFFFFu) return fail(PKV_ERANGE, "more than 2^31 - 1 queries to append");
   if (!new_k || !new_v || !k || !v) return fail(PKV_EINVAL, "null tensor pointer");
   const uint64_t es = elem_size(dtype);
   const uint64_t kb = uint64_t(hkv) * d * es, vb = uint64_t(hkv) * dv * es;  // one slot / query
