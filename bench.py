@@ -26,6 +26,11 @@ The JSON line also carries:
                 workload (8 chunks x 512 queries + 120 decode rows): useful
                 FLOPs of the chunk queries / tile-kernel time, against the
                 dense bf16 MFMA peak.
+  append, window, fp8
+                the cache append, sliding-window decode and FP8-cache decode
+                legs (per-kernel HIP-event durations).
+  decode_step   one captured graph of append + attention on the packed
+                decode workload: replay and eager times per step.
   cpu_baseline  the float64 oracle timed on the host cores over a bounded
                 sample of the same workload, in GB/s.
 """
@@ -294,6 +299,54 @@ def fp8_measure(torch, pkv, workloads, steps: int, k_scale: float = 0.05, v_scal
             "workload": f"{wl.name}, K/V as FP8 E4M3 bytes, balanced"}
 
 
+def decode_step_measure(torch, pkv, workloads, steps: int):
+    """A captured decode step on the packed-decode workload: one graph holds
+    the append of every sequence's new K/V row at its own position and the
+    attention over the grown caches (balanced schedule).  Reported: the
+    replay time per step, the same calls launched eagerly, and the step's
+    bytes (K/V rows read by the attention, plus the append's reads and
+    writes) per replay time against the HBM peak."""
+    wl = workloads.config(2)
+    dev = {k: v.to("cuda") for k, v in wl.tensors.items()}
+    hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=s)
+        ws = pkv.Workspace(wl.queries, hq, dv, 0, stream=s)
+        nk = torch.randn(wl.queries, hkv, d, device="cuda").to(wl.dtype)
+        nv = torch.randn(wl.queries, hkv, dv, device="cuda").to(wl.dtype)
+        out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
+
+        def step():
+            pkv.append(plan, nk, nv, dev["k"], dev["v"])
+            pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws,
+                          out=out)
+
+        def timed(run):
+            for _ in range(3):
+                run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(steps):
+                run()
+            e1.record(s)
+            s.synchronize()
+            return e0.elapsed_time(e1) / steps * 1e3
+
+        eager_us = timed(step)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        graph_us = timed(g.replay)
+    nbytes = workloads.attention_bytes(wl) + 2 * (nk.numel() + nv.numel()) * nk.element_size()
+    gbs = nbytes / (graph_us * 1e-6) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel": "captured decode step: cache append + split-KV decode + merge",
+            "graph_us": round(graph_us, 2), "eager_us": round(eager_us, 2),
+            "bytes_per_step": nbytes, "workload": f"{wl.name}, one new token per sequence"}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -401,6 +454,7 @@ def main():
         line["append"] = append_measure(torch, pkv, workloads, args.prefill_steps)
         line["window"] = window_measure(torch, pkv, workloads, args.prefill_steps)
         line["fp8"] = fp8_measure(torch, pkv, workloads, args.prefill_steps)
+        line["decode_step"] = decode_step_measure(torch, pkv, workloads, args.prefill_steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -174,16 +174,20 @@ pkv_status pkv_workspace_create(uint32_t queries, uint32_t heads, uint32_t dv,
  * contiguous ranges, one per group of waves that attend the same keys for
  * the KV heads (and 16-head groups) of the call, so every wave streams the
  * same number of tiles whatever the length mix, and the heads of a page are
- * read side by side.  The f32 partials of the pieces a range boundary cuts
- * (two 16-head slots per wave) are merged by a second kernel.  Memory:
- * 2 * waves * 16 * (dv + 1) f32 + (2 * queries + 1) u32, waves = CUs *
- * resident waves per CU (about 17 MB at dv = 128 on 256 CUs).  Calls whose
- * rows the MFMA decode kernel does not take (f32, head dims other than
- * 64/128/256 or head_dim != value_dim, pkv_mla, 2^31 or more tile
- * positions, more KV heads x 16-head groups than waves) run unsplit with
- * it.  Same sharing rules as a split workspace: calls that overlap on one
- * workspace race.  Errors: PKV_EINVAL (a zero dimension, null out),
- * PKV_ERANGE (above PKV_WORKSPACE_LIMIT_BYTES), PKV_EHIP. */
+ * read side by side.  pkv_mla with it does the same with 32-token tiles and
+ * one block per CU as the unit (one range per group of 64-head-group
+ * blocks).  The f32 partials of the pieces a range boundary cuts (two slots
+ * per unit, one row per head of the unit) are merged by a second kernel.
+ * Memory: rows * (dv + 1) f32 + (2 * queries + 1) u32 with rows = max(2 *
+ * waves * 16, 2 * CUs * 64), waves = CUs * resident waves per CU of the
+ * decode kernel for dv (about 34 MB at dv = 128, 67 MB at dv = 512 on 256
+ * CUs).  Calls that the MFMA decode or MLA kernels do not take (f32, head
+ * dims other than 64/128/256 or head_dim != value_dim, MLA shapes other
+ * than rank 512 with position dim 64, 2^31 or more tile positions, more
+ * units per group than the launch has) run unsplit with it.  Same sharing
+ * rules as a split workspace: calls that overlap on one workspace race.
+ * Errors: PKV_EINVAL (a zero dimension, null out), PKV_ERANGE (above
+ * PKV_WORKSPACE_LIMIT_BYTES), PKV_EHIP. */
 pkv_status pkv_workspace_create_balanced(uint32_t queries, uint32_t heads,
                                          uint32_t dv, void *stream,
                                          pkv_workspace **out);
@@ -218,7 +222,7 @@ pkv_status pkv_tune_splits(const pkv_plan *plan, pkv_dtype dtype, const void *q,
                            uint32_t value_dim, float scale, int causal,
                            uint32_t reps, void *stream, uint32_t *splits);
 
-/* The same for pkv_mla (split counts only). */
+/* The same for pkv_mla (split counts, then the balanced schedule as 0). */
 pkv_status pkv_tune_splits_mla(const pkv_plan *plan, pkv_dtype dtype,
                                const void *q_abs, const void *q_pos,
                                const void *latent, const void *k_pos, void *out,

@@ -184,7 +184,8 @@ class Workspace:
     """f32 split partials for ``splits`` parts; reusable across plans with the
     same queries, heads and value dim on the same stream.  ``splits=0`` makes
     a balanced workspace (pkv_workspace_create_balanced): the row queries'
-    tiles are cut into equal ranges, one per resident wave."""
+    tiles are cut into equal ranges, one per resident decode wave (attention)
+    or per group of 64-head-group blocks, one block per CU (MLA)."""
 
     def __init__(self, queries: int, heads: int, dv: int, splits: int, stream=None):
         self.stream = _stream_handle(stream)
@@ -249,7 +250,8 @@ def tune_splits(plan: Plan, q, k, v, scale: float, causal: bool = True, out=None
 
 def tune_splits_mla(plan: Plan, q_abs, q_pos, latent, k_pos, scale: float, causal: bool = True,
                     out=None, reps: int = 5) -> int:
-    """Fastest split count for this MLA call (pkv_tune_splits_mla)."""
+    """Fastest split count for this MLA call (pkv_tune_splits_mla); 0 means
+    the balanced schedule."""
     qn, h, r = q_abs.shape
     p = q_pos.shape[2]
     if out is None:

@@ -39,9 +39,11 @@ struct pkv_workspace {
   uint32_t queries = 0, heads = 0, dv = 0, splits = 0;  // splits 0: balanced
   float *buf = nullptr;
   size_t bytes = 0;
-  // balanced schedule: up to max_waves wave ranges (two 16-row slots each),
-  // then {first tile, tiles} per query and the total
+  // balanced schedule: slot_rows f32 rows of dv (two slots per unit: 16 rows
+  // per decode wave, up to max_waves; 64 per MLA block, one block per CU),
+  // their lse, then {first tile, tiles} per query and the total
   uint32_t max_waves = 0, cus = 0;
+  uint64_t slot_rows = 0;
   float *slot_lse = nullptr;
   uint32_t *rec = nullptr;
 };
@@ -183,6 +185,36 @@ uint32_t balanced_waves(const RowArgs &ra, pkv_dtype dt, const pkv_workspace *ws
   return uint32_t(w);
 }
 
+// Blocks of a balanced MLA launch, or 0 when the call cannot use the
+// balanced schedule (then it runs unsplit).
+uint32_t mla_balanced(const RowArgs &ra, pkv_dtype dt, const pkv_workspace *ws) {
+  if (!ws || ws->splits != 0 || ws->slot_rows == 0 || ra.pdim == 0) return 0;
+  if (!mla_mfma_supported(ra, dt)) return 0;
+  // every tile number and k * (tiles per group) must stay below 2^31
+  const uint64_t max_tiles = (uint64_t(ra.plan.W) * ra.plan.ps + 31) / 32;
+  if (uint64_t(ra.n_queries) * max_tiles >= (1ull << 31)) return 0;
+  return mla_balanced_blocks(ra, ws->cus, ws->slot_rows);
+}
+
+MergeArgs balanced_merge_args(const RowArgs &ra) {
+  MergeArgs ma{};
+  ma.plan = ra.plan;
+  ma.qlist = ra.qlist;
+  ma.n_queries = ra.n_queries;
+  ma.hq = ra.hq;
+  ma.hkv = ra.hkv;
+  ma.dv = ra.dv;
+  ma.splits = 1;
+  ma.pages_per_split = ra.pages_per_split;
+  ma.causal = ra.causal;
+  ma.ws_o = ra.ws_o;
+  ma.ws_lse = ra.ws_lse;
+  ma.out = ra.out;
+  ma.bal_rec = ra.bal_rec;
+  ma.bal_waves = ra.bal_waves;
+  return ma;
+}
+
 // Launches the row kernel (and the merge when split) over `qlist`.
 pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_workspace *ws,
                     hipStream_t st) {
@@ -194,23 +226,18 @@ pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_wo
       e = launch_rows_balanced(ra, dt, st);
     }
     if (e != hipSuccess) return hip_fail(e);
-    MergeArgs ma{};
-    ma.plan = ra.plan;
-    ma.qlist = ra.qlist;
-    ma.n_queries = ra.n_queries;
-    ma.hq = ra.hq;
-    ma.hkv = ra.hkv;
-    ma.dv = ra.dv;
-    ma.splits = 1;
-    ma.pages_per_split = ra.pages_per_split;
-    ma.causal = ra.causal;
-    ma.ws_o = ra.ws_o;
-    ma.ws_lse = ra.ws_lse;
-    ma.out = ra.out;
-    ma.bal_rec = ra.bal_rec;
-    ma.bal_waves = ra.bal_waves;
     Timed t(plan, PKV_KERNEL_MERGE, st);
-    return hip_fail(launch_merge_balanced(ma, dt, st));
+    return hip_fail(launch_merge_balanced(balanced_merge_args(ra), dt, 16, st));
+  }
+  ra.bal_waves = mla_balanced(ra, dt, ws);
+  if (ra.bal_waves) {
+    {
+      Timed t(plan, PKV_KERNEL_MLA, st);
+      e = launch_mla_balanced(ra, dt, st);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    Timed t(plan, PKV_KERNEL_MERGE, st);
+    return hip_fail(launch_merge_balanced(balanced_merge_args(ra), dt, kMlaBlockHeads, st));
   }
   if (ra.pdim != 0 && mla_mfma_supported(ra, dt)) {
     if (mla_mfma_blocks(ra) > kU32Max) return fail(PKV_ERANGE, "launch grid exceeds the x-dimension limit");
@@ -452,7 +479,8 @@ pkv_status pkv_workspace_create_balanced(uint32_t queries, uint32_t heads, uint3
       per_cu = std::max<uint32_t>(per_cu, uint32_t(bal_waves_per_cu(dv, ps, dt)));
   per_cu = std::min(per_cu, std::max(kBalancedWavesPerCu, kBalancedWavesPerCuFp8));
   const uint64_t waves = uint64_t(per_cu) * uint32_t(cus);
-  const uint64_t rows = 2 * waves * 16;  // two 16-head slots per wave
+  // two 16-head slots per decode wave; two 64-head slots per MLA block
+  const uint64_t rows = std::max<uint64_t>(2 * waves * 16, 2 * uint64_t(cus) * kMlaBlockHeads);
   const uint64_t bytes = rows * (uint64_t(dv) + 1) * sizeof(float) + (2 * uint64_t(queries) + 1) * 4;
   if (bytes > PKV_WORKSPACE_LIMIT_BYTES) return fail(PKV_ERANGE, "workspace above PKV_WORKSPACE_LIMIT_BYTES");
   auto *w = new pkv_workspace;
@@ -464,6 +492,7 @@ pkv_status pkv_workspace_create_balanced(uint32_t queries, uint32_t heads, uint3
   w->splits = 0;
   w->max_waves = uint32_t(waves);
   w->cus = uint32_t(cus);
+  w->slot_rows = rows;
   w->bytes = size_t(bytes);
   if (hipMalloc(&w->buf, w->bytes) != hipSuccess) {
     delete w;
@@ -946,7 +975,7 @@ pkv_status pkv_tune_splits_mla(const pkv_plan *plan, pkv_dtype dtype, const void
                                int causal, uint32_t reps, void *stream, uint32_t *splits) {
   clear_error();
   if (!plan || !splits) return fail(PKV_EINVAL, "null argument");
-  return tune_splits(plan, heads, rank, reps, static_cast<hipStream_t>(stream), false,
+  return tune_splits(plan, heads, rank, reps, static_cast<hipStream_t>(stream), true,
                      [&](pkv_workspace *ws) {
                        return pkv_mla(plan, dtype, q_abs, q_pos, latent, k_pos, out, heads, rank,
                                       pos_dim, scale, causal, ws, stream);

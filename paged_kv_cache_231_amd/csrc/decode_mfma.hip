@@ -25,6 +25,7 @@
 // Only the C layout fixes meaning; the K-slot order just has to agree
 // between A and B, and it does because both are filled with one mapping.
 
+#include "balanced.h"
 #include "mfma_common.h"
 
 namespace pkv {
@@ -421,60 +422,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Balanced schedule.  With the block-per-part grid above, the work of a CU
-// is whatever lengths its resident blocks happen to draw, and the kernel
-// lasts as long as the busiest CU.  Here the row queries' 16-key tiles are
-// numbered query after query (one number per tile position, shared by the
-// query's segq = KV heads x 16-head groups segments) and cut into equal
-// contiguous ranges, one per group of segq consecutive waves; wave g of a
-// group attends segment g over its group's range.  Every wave so streams the
-// same number of tiles, and the segq waves that read the same cache pages
-// (one KV head each) run side by side, which keeps DRAM rows open for all
-// heads of a page.  Each wave finds its range from a prefix of the tile
-// counts it computes itself; wave 0 also stores, per row query, its first
-// tile and tile count for the merge.  A range is a list of pieces, one per
-// query it touches.  A piece that is a whole query writes the output
-// directly.  A piece cut by a range boundary writes f32 partials (normalised
-// o and lse) to a slot: slot 2w when it is the first piece of wave w and
-// its query began in an earlier range, else slot 2w + 1 (its query goes on
-// into the next range).  A second, small kernel merges the cut pieces.
-
-// Tiles of 16 keys of row query r, on the 16-key grid from the tile that
-// holds its first visible key (the window's start).
-__device__ __forceinline__ uint32_t row_tiles(const RowArgs &a, uint32_t r) {
-  const uint32_t i = a.qlist ? a.qlist[r] : r;
-  uint32_t seq;
-  const uint32_t n = visible_keys(a.plan, i, a.causal, &seq);
-  return ceil_div_u(n, 16u) - window_lo(n, a.window) / 16u;
-}
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= uint32_t(o)) x += y;
-  }
-  return x;
-}
-
-// Tile prefix over 64 consecutive row queries base .. base + 63: lane l
-// holds v = tiles of query base + l (0 past the end) and excl = first tile
-// of that query; end = first tile after the chunk.
-struct Chunk {
-  uint32_t base, end;
-  uint32_t v, excl;
-};
-
-__device__ __forceinline__ void scan_chunk(Chunk &c, const RowArgs &a, uint32_t base,
-                                           uint32_t carry, uint32_t lane) {
-  const uint32_t r = base + lane;
-  const uint32_t v = r < a.n_queries ? row_tiles(a, r) : 0u;
-  const uint32_t x = wave_incl_scan(v, lane);
-  c.base = base;
-  c.v = v;
-  c.excl = carry + x - v;
-  c.end = carry + __builtin_amdgcn_readlane(x, 63);
-}
+// Balanced schedule (balanced.h) with waves as units.  With the block-per-part
+// grid above, the work of a CU is whatever lengths its resident blocks happen
+// to draw, and the kernel lasts as long as the busiest CU.  Here the row
+// queries' 16-key tiles are cut into equal ranges, one per group of segq =
+// KV heads x 16-head groups consecutive waves; wave g of a group attends
+// segment g over its group's range, so the segq waves that read the same
+// cache pages (one KV head each) run side by side, which keeps DRAM rows open
+// for all heads of a page.
 
 // Launched with one block of four waves per CU (one wave per SIMD): fewer
 // concurrent page streams keep more DRAM rows open, and more waves per CU
@@ -497,43 +452,8 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
   const uint32_t w = blockIdx.x * kWaves + wv;
   const uint32_t grp_k = w / segq, g = w % segq;
   if (grp_k >= groups) return;
-  const uint32_t R = a.n_queries;
-
-  // Total tiles T and the super-chunk of row queries holding this group's
-  // first tile: chunks of 64 queries (coalesced loads, one wave sum each);
-  // lane l adds up chunks l*m .. l*m + m - 1.
-  const uint32_t nch = (R + 63u) / 64u;
-  const uint32_t m = (nch + 63u) / 64u;
-  uint32_t s = 0, carry = 0;
-  for (uint32_t c = 0; c < nch; ++c) {
-    const uint32_t r = c * 64u + lane;
-    const uint32_t v = r < R ? row_tiles(a, r) : 0u;
-    const uint32_t x = wave_incl_scan(v, lane);
-    const uint32_t tot = __builtin_amdgcn_readlane(x, 63);
-    if (c / m == lane) s += tot;
-    if (w == 0u && r < R) {  // {first tile, tiles} of every row query, for the merge
-      a.bal_rec[2u * r] = carry + x - v;
-      a.bal_rec[2u * r + 1u] = v;
-    }
-    carry += tot;
-  }
-  const uint32_t sx = wave_incl_scan(s, lane);
-  const uint32_t T = __builtin_amdgcn_readlane(sx, 63);
-  if (w == 0u && lane == 0u) a.bal_rec[2u * R] = T;
-  const uint32_t tpg = T / groups + (T % groups != 0u);
-  // tpg * groups < T + groups <= 2^31 + groups: no overflow (checked by the host)
-  uint32_t t = grp_k * tpg;
-  if (t >= T) return;
-  const uint32_t t_w0 = t;
-  const uint32_t t_end = T - t < tpg ? T : t + tpg;
-
-  // super-chunk lane: the last one starting at or before t (its sum is > 0)
-  const uint64_t sel = __ballot(sx - s <= t);
-  const uint32_t lb = 63u - uint32_t(__builtin_clzll(sel));
-  Chunk ch;
-  scan_chunk(ch, a, lb * m * 64u, __builtin_amdgcn_readlane(sx - s, lb), lane);
-  while (ch.end <= t) scan_chunk(ch, a, ch.base + 64u, ch.end, lane);
-  uint32_t qi = ch.base + 63u - uint32_t(__builtin_clzll(__ballot(ch.excl <= t)));
+  bal::Range rg;
+  if (!bal::find_range<16>(rg, a, groups, grp_k, w == 0u, lane)) return;
 
   unsigned char *vt = lds + wv * L::kTileBytes;
   const uint32_t kvh = g / hgk, sub = g % hgk;
@@ -543,18 +463,10 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
   const unsigned char *kbase = static_cast<const unsigned char *>(a.k) + uint64_t(kvh) * D * EB;
   const unsigned char *vbase = static_cast<const unsigned char *>(a.v) + uint64_t(kvh) * D * EB;
 
-  while (t < t_end) {
-    if (qi - ch.base >= 64u) scan_chunk(ch, a, ch.base + 64u, ch.end, lane);
-    const uint32_t li = qi - ch.base;
-    const uint32_t c0 = __builtin_amdgcn_readlane(ch.excl, li);
-    const uint32_t ntq = __builtin_amdgcn_readlane(ch.v, li);  // tiles of this query
-    if (c0 + ntq <= t) {  // a query with no tiles
-      ++qi;
-      continue;
-    }
-    const uint32_t tt0 = t - c0;
-    const uint32_t tt1 = ntq - tt0 < t_end - t ? ntq : tt0 + (t_end - t);
-    const uint32_t i = __builtin_amdgcn_readfirstlane(a.qlist ? a.qlist[qi] : qi);
+  bal::Piece pc;
+  while (bal::next_piece<16>(rg, a, lane, pc)) {
+    const uint32_t tt0 = pc.tt0, tt1 = pc.tt1;
+    const uint32_t i = __builtin_amdgcn_readfirstlane(a.qlist ? a.qlist[pc.qi] : pc.qi);
     uint32_t seq;
     const uint32_t n = __builtin_amdgcn_readfirstlane(visible_keys(a.plan, i, a.causal, &seq));
     seq = __builtin_amdgcn_readfirstlane(seq);
@@ -573,7 +485,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
 
     const float lsum = rows4_sum(st.lsum);
     const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;  // v_scale: FP8 value cache
-    if (tt0 == 0u && tt1 == ntq) {
+    if (tt0 == 0u && tt1 == pc.ntq) {
       if (c16 < nh) {
         uint16_t *orow = static_cast<uint16_t *>(a.out) + (uint64_t(i) * a.hq + h0 + c16) * D;
 #pragma unroll
@@ -585,7 +497,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
         }
       }
     } else {
-      const uint32_t slot = (t == t_w0 && tt0 > 0u) ? 2u * w : 2u * w + 1u;
+      const uint32_t slot = bal::piece_slot(pc, w);
       if (c16 < nh) {
         const uint64_t row = uint64_t(slot) * kHeads + c16;
         float *wo = a.ws_o + row * D;
@@ -594,16 +506,16 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
         if (j == 0) a.ws_lse[row] = st.m + fast_log2(lsum);
       }
     }
-    t += tt1 - tt0;
-    if (tt1 == ntq) ++qi;
   }
 }
 
 // Merge of the cut pieces of one (query, head): out = sum_p 2^(lse_p - M)
 // o_p / sum_p 2^(lse_p - M), M = max_p lse_p, over the slots of that head's
-// waves in the groups k0..k1 the query spans.  Queries inside one range
-// were written by the wave-range kernel; queries with no tiles get zeros.
-template <class DT>
+// units in the groups k0..k1 the query spans.  A unit owns UH heads of one
+// KV head (16 for the decode waves, 64 for the MLA blocks); its slots hold
+// UH rows.  Queries inside one range were written by the range kernel;
+// queries with no tiles get zeros.
+template <class DT, uint32_t UH>
 __global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
   using T = typename DT::T;
   __shared__ float s_w[256];
@@ -612,9 +524,9 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
   const uint32_t h = blockIdx.x % a.hq;
   const uint32_t qi = blockIdx.x / a.hq;
   const uint32_t grp = a.hq / a.hkv;
-  const uint32_t hgk = (grp + kHeads - 1) / kHeads;
+  const uint32_t hgk = (grp + UH - 1) / UH;
   const uint32_t segq = a.hkv * hgk;
-  const uint32_t g = (h / grp) * hgk + (h % grp) / kHeads, hl = (h % grp) % kHeads;
+  const uint32_t g = (h / grp) * hgk + (h % grp) / UH, hl = (h % grp) % UH;
   const uint32_t c0 = a.bal_rec[2u * qi], ntq = a.bal_rec[2u * qi + 1u];
   const uint32_t total_tiles = a.bal_rec[2u * a.n_queries];
   const uint32_t i = a.qlist ? a.qlist[qi] : qi;
@@ -628,11 +540,11 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
   const uint32_t k0 = c0 / tpg, k1 = (c0 + ntq - 1u) / tpg;
   if (k0 == k1) return;  // whole query in one range: already written
   const uint32_t np = k1 - k0 + 1u;
-  // piece p: wave (k0 + p) segq + g; slot 2w + 1 for p = 0, else 2w
+  // piece p: unit u = (k0 + p) segq + g; slot 2u + 1 for p = 0, else 2u
   auto row_of = [&](uint32_t p) -> uint64_t {
-    const uint32_t w = (k0 + p) * segq + g;
-    const uint32_t slot = p == 0u ? 2u * w + 1u : 2u * w;
-    return uint64_t(slot) * kHeads + hl;
+    const uint32_t u = (k0 + p) * segq + g;
+    const uint32_t slot = p == 0u ? 2u * u + 1u : 2u * u;
+    return uint64_t(slot) * UH + hl;
   };
 
   float mx = kNoMax;
@@ -777,13 +689,22 @@ hipError_t launch_rows_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st) 
   return pu ? launch_bal_d<F16, true, false>(a, grid, st) : launch_bal_d<F16, false, false>(a, grid, st);
 }
 
-hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, hipStream_t st) {
+hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, uint32_t unit_heads,
+                                 hipStream_t st) {
   const uint64_t blocks = uint64_t(a.n_queries) * a.hq;
   if (blocks == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(blocks));
+  if (unit_heads != uint32_t(kHeads) && unit_heads != kMlaBlockHeads) return hipErrorInvalidValue;
+  const bool mla = unit_heads == kMlaBlockHeads;
   switch (dt) {
-    case PKV_F16: hipLaunchKernelGGL(merge_balanced_kernel<F16>, grid, dim3(256), 0, st, a); break;
-    case PKV_BF16: hipLaunchKernelGGL(merge_balanced_kernel<BF16>, grid, dim3(256), 0, st, a); break;
+    case PKV_F16:
+      if (mla) hipLaunchKernelGGL((merge_balanced_kernel<F16, kMlaBlockHeads>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((merge_balanced_kernel<F16, kHeads>), grid, dim3(256), 0, st, a);
+      break;
+    case PKV_BF16:
+      if (mla) hipLaunchKernelGGL((merge_balanced_kernel<BF16, kMlaBlockHeads>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((merge_balanced_kernel<BF16, kHeads>), grid, dim3(256), 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -36,11 +36,12 @@ struct RowArgs {
   uint64_t kp_page, kp_tok;
   void *out;                 // [Q, hq, dv] in the input dtype
   float *ws_o, *ws_lse;      // [Q, splits, hq, dv], [Q, splits, hq] (splits > 1)
-  // Balanced schedule (bal_waves > 0): the row queries' tile positions are
-  // cut into equal ranges, one per group of segq waves (segq = KV heads x
-  // 16-head groups); pieces cut by a range boundary go to ws_o/ws_lse slots
-  // (2 per wave, 16 head rows each).  bal_rec[2r], bal_rec[2r + 1]: first
-  // tile and tile count of row query r; bal_rec[2 n_queries]: total tiles.
+  // Balanced schedule (bal_waves > 0 units): the row queries' tile
+  // positions are cut into equal ranges, one per group of segq units (decode:
+  // waves, segq = KV heads x 16-head groups; MLA: blocks, segq = 64-head
+  // groups); pieces cut by a range boundary go to ws_o/ws_lse slots (2 per
+  // unit, one row per head of the unit).  bal_rec[2r], bal_rec[2r + 1]:
+  // first tile and tile count of row query r; bal_rec[2 n_queries]: total.
   uint32_t *bal_rec;
   uint32_t bal_waves;
 };
@@ -95,16 +96,25 @@ int rows_mfma_blocks_per_cu(const RowArgs &a, pkv_dtype dt);
 hipError_t launch_rows_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 // Balanced MFMA decode: the wave-range kernel, then the merge of the pieces
 // cut by range boundaries.  balanced_waves_per_cu: resident waves per CU of
-// the wave-range kernel.
+// the wave-range kernel.  The merge takes the heads per unit: 16 for the
+// decode waves, kMlaBlockHeads for the MLA blocks.
 int balanced_waves_per_cu(uint32_t d, uint32_t ps, pkv_dtype dt);
 hipError_t launch_rows_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st);
-hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, hipStream_t st);
+hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, uint32_t unit_heads,
+                                 hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, pkv_dtype dt, hipStream_t st);
 // MLA on MFMA (F16/BF16, rank 512, position dim 64): one block per
-// (query, 128-head group, split part).
+// (query, 64-head group, split part); balanced: one block per CU, each
+// (range, 64-head group), bal_waves = the block count.
+constexpr uint32_t kMlaBlockHeads = 64;
 bool mla_mfma_supported(const RowArgs &a, pkv_dtype dt);
 uint64_t mla_mfma_blocks(const RowArgs &a);
 hipError_t launch_mla_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st);
+// Blocks of a balanced MLA launch on `cus` compute units with slot rows
+// for `slot_rows` (two kMlaBlockHeads-row slots per block): whole groups of
+// 8 x head-group blocks, 0 when none fits.
+uint32_t mla_balanced_blocks(const RowArgs &a, uint32_t cus, uint64_t slot_rows);
+hipError_t launch_mla_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st);
 bool tiles_supported(const TileArgs &a, pkv_dtype dt);
 hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st);
 

@@ -6,15 +6,19 @@
 // output are dense contractions over the latent:
 //   S^T[tokens x heads] = latent . q_abs^T + k_pos . q_pos^T   (576-deep)
 //   O^T[rank x heads]  += latent^T . P^T                        (token-deep)
-// A block owns one (query, split part, 64-head group); its four waves (one
+// A block owns one (query, split part, 64-head group) in the split grid, or
+// one equal range of the queries' 32-token tiles and a 64-head group in the
+// balanced grid (pieces of several queries in turn); its four waves (one
 // per SIMD) own 16 heads each, with the 512 x 16 f32 output tile in VGPRs
 // and the loop-invariant query operands in AGPRs (MFMA reads them there).
 // Latent and k_pos rows travel HBM -> LDS directly into a four-stage ring
 // (three 32-token tiles ahead); the latent is read from LDS as the A operand
 // of q.k and, transposed, as the A operand of the value product (16x16x32
 // with 32 tokens per step).  The online softmax is kept in base 2 with lazy
-// rescaling.  Split parts write f32 partials that the merge kernel combines.
+// rescaling.  Split parts, and balanced pieces cut by a range boundary,
+// write f32 partials that a merge kernel combines.
 
+#include "balanced.h"
 #include "mfma_common.h"
 
 namespace pkv {
@@ -23,6 +27,7 @@ namespace {
 
 constexpr int kWaves = 4;          // one wave per SIMD
 constexpr int kHeadsPerBlock = kWaves * 16;
+static_assert(kHeadsPerBlock == int(kMlaBlockHeads), "slot rows per block of the balanced merge");
 constexpr int kTT = 32;            // tokens per tile (two 16-row M-tiles)
 constexpr int kStages = 4;         // LDS ring stages
 constexpr int kTableCache = 1024;  // block-table entries cached in LDS
@@ -92,9 +97,16 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// One piece of work for the whole block: query i (sequence seq), tokens
+// [t_lo, t_hi), this wave's 16 heads from h0.  The result goes to the output
+// rows of the query (direct) or, normalised with its base-2 lse, to f32
+// rows row0 + c16 of ws_o / ws_lse.  Every wave of the block calls it with
+// the same query and tokens; it starts by rewriting the table cache and the
+// ring, so a caller running pieces back to back passes a block barrier
+// first.
 template <class DT, int R, int P>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mla_kernel(RowArgs a, uint32_t head_groups) {
+__device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t seq, uint32_t t_lo,
+                                          uint32_t t_hi, uint32_t h0, bool direct, uint64_t row0) {
   using M = Mfma<DT>;
   using L = MLds<R, P>;
   using T = typename DT::T;
@@ -108,27 +120,7 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t c16 = lane & 15u, j = lane >> 4;
-  // Blocks are dispatched round-robin over the eight XCDs.  The head groups
-  // of one (query, part) read the same cache rows, so they get consecutive
-  // logical numbers on one XCD (the second read then hits that XCD's L2);
-  // logical order is part-major (the first parts of every query start first).
-  const uint32_t bid = blockIdx.x, span8 = 8u * head_groups;
-  const uint32_t logical = (bid / span8) * span8 + (bid % 8u) * head_groups + (bid % span8) / 8u;
-  const uint32_t per_part = a.n_queries * head_groups;
-  if (logical >= per_part * a.splits) return;
-  const uint32_t part = logical / per_part;
-  const uint32_t rest = logical % per_part;
-  const uint32_t hgi = rest % head_groups;
-  const uint32_t qi = rest / head_groups;
-  const uint32_t i = a.qlist ? a.qlist[qi] : qi;
-  uint32_t seq;
-  const uint32_t n = visible_keys(a.plan, i, a.causal, &seq);
   const uint32_t ps = a.plan.ps;
-  const uint64_t span = uint64_t(a.pages_per_split) * ps;
-  const uint64_t lo64 = uint64_t(part) * span;
-  if (a.splits > 1 && lo64 >= n) return;  // empty part: the merge skips it
-  const uint32_t t_lo = uint32_t(lo64 < n ? lo64 : n);
-  const uint32_t t_hi = uint32_t(lo64 + span < n ? lo64 + span : n);
   const bool pow2 = (ps & (ps - 1)) == 0;
   const uint32_t ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 0u;
   auto page_of = [&](uint32_t tok) { return pow2 ? tok >> ps_shift : tok / ps; };
@@ -149,7 +141,6 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
 
   // this wave's heads: column c16 -> head h0 + c16; columns of heads past hq
   // compute on head 0's query and are not stored
-  const uint32_t h0 = hgi * kHeadsPerBlock + wv * 16u;
   uint4 qa[KS], qp[KP];
   {
     const uint32_t h = h0 + c16;
@@ -367,7 +358,7 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
   const uint32_t h = h0 + c16;
   if (h >= a.hq) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (a.splits == 1) {
+  if (direct) {
     T *out = static_cast<T *>(a.out) + (uint64_t(i) * a.hq + h) * R;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -377,11 +368,75 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
       *reinterpret_cast<uint2 *>(out + 16 * b + 4 * j) = w;
     }
   } else {
-    const uint64_t r = (uint64_t(i) * a.splits + part) * a.hq + h;
+    const uint64_t r = row0 + c16;
     float *wo = a.ws_o + r * R;
 #pragma unroll
     for (int b = 0; b < DB; ++b) *reinterpret_cast<f32x4_t *>(wo + 16 * b + 4 * j) = o[b] * inv;
     if (j == 0) a.ws_lse[r] = m + fast_log2(l_tot);
+  }
+}
+
+// Split grid: one block per (query, split part, 64-head group).
+template <class DT, int R, int P>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_kernel(RowArgs a, uint32_t head_groups) {
+  // Blocks are dispatched round-robin over the eight XCDs.  The head groups
+  // of one (query, part) read the same cache rows, so they get consecutive
+  // logical numbers on one XCD (the second read then hits that XCD's L2);
+  // logical order is part-major (the first parts of every query start first).
+  const uint32_t bid = blockIdx.x, span8 = 8u * head_groups;
+  const uint32_t logical = (bid / span8) * span8 + (bid % 8u) * head_groups + (bid % span8) / 8u;
+  const uint32_t per_part = a.n_queries * head_groups;
+  if (logical >= per_part * a.splits) return;
+  const uint32_t part = logical / per_part;
+  const uint32_t rest = logical % per_part;
+  const uint32_t hgi = rest % head_groups;
+  const uint32_t qi = rest / head_groups;
+  const uint32_t i = a.qlist ? a.qlist[qi] : qi;
+  uint32_t seq;
+  const uint32_t n = visible_keys(a.plan, i, a.causal, &seq);
+  const uint64_t span = uint64_t(a.pages_per_split) * a.plan.ps;
+  const uint64_t lo64 = uint64_t(part) * span;
+  if (a.splits > 1 && lo64 >= n) return;  // empty part: the merge skips it
+  const uint32_t t_lo = uint32_t(lo64 < n ? lo64 : n);
+  const uint32_t t_hi = uint32_t(lo64 + span < n ? lo64 + span : n);
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t h0 = hgi * kHeadsPerBlock + wv * 16u;
+  mla_piece<DT, R, P>(a, i, seq, t_lo, t_hi, h0, a.splits == 1,
+                      (uint64_t(i) * a.splits + part) * a.hq + h0);
+}
+
+// Balanced grid (balanced.h) with blocks as units: block u of the launch
+// attends 64-head group g = u % head_groups over range u / head_groups, so
+// every block streams the same number of 32-token tiles whatever the length
+// mix.  The head groups of one range are numbered onto one XCD and run side
+// by side, so the second read of each latent tile hits that XCD's L2.
+template <class DT, int R, int P>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_balanced_kernel(RowArgs a, uint32_t head_groups) {
+  const uint32_t bid = blockIdx.x, span8 = 8u * head_groups;
+  const uint32_t u = (bid / span8) * span8 + (bid % 8u) * head_groups + (bid % span8) / 8u;
+  const uint32_t groups = a.bal_waves / head_groups;
+  const uint32_t grp_k = u / head_groups, g = u % head_groups;
+  if (grp_k >= groups) return;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  bal::Range rg;
+  if (!bal::find_range<kTT>(rg, a, groups, grp_k, u == 0u && wv == 0u, lane)) return;
+  const uint32_t h0 = g * kHeadsPerBlock + wv * 16u;
+  bal::Piece pc;
+  while (bal::next_piece<kTT>(rg, a, lane, pc)) {
+    const uint32_t i = __builtin_amdgcn_readfirstlane(a.qlist ? a.qlist[pc.qi] : pc.qi);
+    uint32_t seq;
+    const uint32_t n = __builtin_amdgcn_readfirstlane(visible_keys(a.plan, i, a.causal, &seq));
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    const uint32_t t_lo = pc.tt0 * kTT;
+    const uint32_t t_hi = pc.tt1 * kTT < n ? pc.tt1 * kTT : n;
+    const bool whole = pc.tt0 == 0u && pc.tt1 == pc.ntq;
+    const uint32_t slot = bal::piece_slot(pc, u);
+    __syncthreads();  // the previous piece's ring and table cache are free
+    mla_piece<DT, R, P>(a, i, seq, t_lo, t_hi, h0, whole,
+                        uint64_t(slot) * kHeadsPerBlock + wv * 16u);
   }
 }
 
@@ -402,6 +457,25 @@ uint64_t mla_mfma_blocks(const RowArgs &a) {
   const uint64_t hg = (a.hq + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const uint64_t n = uint64_t(a.n_queries) * hg * a.splits;
   return (n + 8 * hg - 1) / (8 * hg) * (8 * hg);
+}
+
+uint32_t mla_balanced_blocks(const RowArgs &a, uint32_t cus, uint64_t slot_rows) {
+  const uint64_t hg = (a.hq + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  uint64_t b = slot_rows / (2 * kHeadsPerBlock);
+  if (cus < b) b = cus;
+  b -= b % (8 * hg);
+  return uint32_t(b);
+}
+
+hipError_t launch_mla_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
+  const uint32_t hg = (a.hq + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  if (a.bal_waves == 0 || a.bal_waves % (8 * hg) != 0) return hipErrorInvalidValue;
+  const dim3 grid(a.bal_waves);
+  if (dt == PKV_BF16)
+    hipLaunchKernelGGL((mla_balanced_kernel<BF16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+  else
+    hipLaunchKernelGGL((mla_balanced_kernel<F16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+  return hipGetLastError();
 }
 
 hipError_t launch_mla_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st) {

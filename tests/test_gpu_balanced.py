@@ -70,17 +70,17 @@ def test_balanced_mixed_prefill_and_decode():
 
 
 def test_balanced_workspace_falls_back_to_unsplit():
-    """Calls the balanced kernel does not take (f32, head dim 48, MLA) run
-    unsplit with a balanced workspace and stay correct."""
+    """Calls the balanced kernels do not take (f32, head dim 48, MLA of rank
+    64) run unsplit with a balanced workspace and stay correct."""
     lens = [40, 300, 7]
     wl = _wl(torch.float32, 8, 2, 128, 16, lens, seed=1400)
     assert_close(run(wl, splits=0), expected(wl), torch.float32, "f32 balanced ws")
     wl = build_attention("bal", 1401, torch.bfloat16, lens, decode_queries(lens), 6, 3, 48, 48, 16,
                          poison=True)
     assert_close(run(wl, splits=0), expected(wl), torch.bfloat16, "d=48 balanced ws")
-    mw = build_mla("bal", 1402, torch.bfloat16, lens, decode_queries(lens), 128, 512, 64, 64,
+    mw = build_mla("bal", 1402, torch.bfloat16, lens, decode_queries(lens), 16, 64, 16, 16,
                    poison=True)
-    assert_close(run(mw, splits=0), expected(mw), torch.bfloat16, "mla balanced ws")
+    assert_close(run(mw, splits=0), expected(mw), torch.bfloat16, "mla rank 64 balanced ws")
 
 
 def test_balanced_launches_and_reuse():

@@ -1,0 +1,132 @@
+"""GPU parity of the balanced MLA schedule (pkv_mla with a balanced
+workspace): the queries' 32-token tiles cut into equal ranges, one per group
+of 64-head-group blocks (one block per CU), with the pieces cut by range
+boundaries merged on the device.  Tiny inputs leave most blocks without
+tiles; one long sequence among short ones is cut into a piece per range;
+larger inputs give several pieces per block.  Tolerance 1.5e-2 for
+f16/bf16; unused cache slots are NaN."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_231_amd as pkv
+from workloads import build_mla, config, decode_queries
+from tests._gpu import assert_close, expected, expected_rows, make_plan, run, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _mla(dtype, h, ps, lens, seed, queries=None, causal=True):
+    q = queries if queries is not None else decode_queries(lens)
+    need = sum(-(-L // ps) for L in lens)
+    return build_mla("mlabal", seed, dtype, lens, q, h, 512, 64, ps, pool=need + 3, causal=causal,
+                     poison=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("h,ps", [(128, 64), (16, 16), (40, 5), (256, 1)])
+def test_mla_balanced_shapes(dtype, h, ps):
+    """Ragged head groups (16, 40: one partial 64-head group; 256: four),
+    page sizes 1/5/16/64, lengths inside, on and across a 32-token tile,
+    and two queries that are not at their sequence's end."""
+    lens = [1, 31, 32, 33, 300, 1000]
+    queries = decode_queries(lens) + [(4, 17), (5, 500)]
+    wl = _mla(dtype, h, ps, lens, 2000 + h + ps, queries)
+    assert_close(run(wl, splits=0), expected(wl), dtype, f"mla balanced h={h} ps={ps}")
+
+
+def test_mla_balanced_more_ranges_than_tiles():
+    """Two tiles in all: every other block's range is empty, and the two
+    queries are whole pieces written without the merge."""
+    wl = _mla(torch.bfloat16, 128, 64, [1, 40], 2100)
+    assert_close(run(wl, splits=0), expected(wl), torch.bfloat16, "mla balanced, 2 tiles")
+
+
+def test_mla_balanced_one_long_query_across_every_range():
+    """A 30000-token sequence beside short ones: its tiles fill nearly every
+    range, so the merge combines about one piece per block group."""
+    wl = _mla(torch.bfloat16, 128, 64, [30000, 5, 40, 1], 2200)
+    assert_close(run(wl, splits=0), expected(wl), torch.bfloat16, "mla balanced long")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_mla_balanced_many_pieces(causal):
+    """Forty sequences of 300..12000 tokens: ranges that start and end
+    inside queries and queries wholly inside one range."""
+    rng = np.random.default_rng(23)
+    lens = [int(x) for x in rng.integers(300, 12000, size=40)]
+    wl = _mla(torch.bfloat16, 128, 64, lens, 2300, causal=causal)
+    assert_close(run(wl, splits=0), expected(wl), torch.bfloat16, "mla balanced many")
+
+
+def test_mla_balanced_launches_and_reuse():
+    """One MLA kernel and one merge per call; repeated calls on one workspace
+    stay correct; the unbalanced path is unchanged."""
+    wl = _mla(torch.bfloat16, 128, 64, [3000, 77, 1000], 2400)
+    dev = to_dev(wl)
+    plan = make_plan(wl)
+    ws = pkv.Workspace(wl.queries, 128, 512, 0)
+    want = expected(wl)
+    plan.timing(True)
+    for _ in range(3):
+        out = pkv.mla(plan, dev["q_abs"], dev["q_pos"], dev["latent"], dev["k_pos"], wl.scale,
+                      wl.causal, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out.double().cpu().numpy(), want, torch.bfloat16, "mla balanced repeat")
+    assert plan.timing_read("mla")[0] == 3
+    assert plan.timing_read("merge")[0] == 3
+    plan.timing(False)
+    assert_close(run(wl, splits=3, plan=plan, dev=dev), want, torch.bfloat16, "mla split 3")
+
+
+def test_mla_balanced_graph_capture_replays_with_new_lengths():
+    """Captured once; lengths change through the plan words between replays,
+    so the tile prefix, the block ranges and the cut pieces all move; every
+    replay equals an eager call bit for bit and the oracle within
+    tolerance."""
+    lens = [5000, 90, 300, 2500, 16]
+    wl = _mla(torch.bfloat16, 128, 64, lens, 2500)
+    dev = to_dev(wl)
+    s = torch.cuda.Stream()
+    args = (dev["q_abs"], dev["q_pos"], dev["latent"], dev["k_pos"], wl.scale, True)
+    with torch.cuda.stream(s):
+        plan = make_plan(wl, stream=s)
+        ws = pkv.Workspace(wl.queries, 128, 512, 0, stream=s)
+        out = torch.empty(wl.queries, 128, 512, dtype=torch.bfloat16, device="cuda")
+        eager = torch.empty_like(out)
+        pkv.mla(plan, *args, workspace=ws, out=out)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            pkv.mla(plan, *args, workspace=ws, out=out)
+        rng = np.random.default_rng(11)
+        for step in range(4):
+            new_lens = np.array([int(rng.integers(1, L + 1)) for L in lens])
+            plan.rebind(new_lens, wl.qseq, new_lens - 1, wl.table)
+            g.replay()
+            s.synchronize()
+            got = out.double().cpu().numpy()
+            pkv.mla(plan, *args, workspace=ws, out=eager)
+            s.synchronize()
+            _ = (dev["q_abs"] * 2).sum().item()
+            np.testing.assert_array_equal(got, eager.double().cpu().numpy())
+            wl.lens, wl.qpos = new_lens, new_lens - 1
+            assert_close(got, expected(wl), wl.dtype, f"mla balanced replay {step}")
+
+
+def test_mla_balanced_full_size_sampled():
+    """The MLA benchmark workload at full size (128 sequences of
+    1024..32768 tokens, 128 heads) with a balanced workspace, on sampled
+    (query, head) rows against the oracle."""
+    wl = config(5)
+    dev = to_dev(wl)
+    plan = make_plan(wl)
+    rng = np.random.default_rng(105)
+    idx = sorted(set(int(x) for x in rng.integers(0, wl.queries, size=10)) | {0, wl.queries - 1})
+    pairs = [(i, int(rng.integers(0, wl.info["h"]))) for i in idx]
+    want = expected_rows(wl, pairs)
+    got = run(wl, splits=0, plan=plan, dev=dev)
+    sel = np.stack([got[i, h] for i, h in pairs])
+    assert_close(sel, want, wl.dtype, "config 5 balanced")
+    assert np.isfinite(got).all()
