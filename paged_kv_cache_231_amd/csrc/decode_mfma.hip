@@ -514,15 +514,21 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
 // units in the groups k0..k1 the query spans.  A unit owns UH heads of one
 // KV head (16 for the decode waves, 64 for the MLA blocks); its slots hold
 // UH rows.  Queries inside one range were written by the range kernel;
-// queries with no tiles get zeros.
+// queries with no tiles get zeros.  One wave per (query, head), four per
+// block; lane l owns value elements 4l + 256e .. +3 (dv a multiple of 4, at
+// most 1024).  Pieces are taken eight at a time with their lse and partial
+// rows loaded together (one round of loads after the range record for up to
+// eight pieces), combined online: the running sum is rescaled when a batch
+// raises the max.
 template <class DT, uint32_t UH>
 __global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
   using T = typename DT::T;
-  __shared__ float s_w[256];
-  __shared__ float s_red[8];
-  const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
-  const uint32_t h = blockIdx.x % a.hq;
-  const uint32_t qi = blockIdx.x / a.hq;
+  constexpr uint32_t kBatch = 8;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint64_t pair = uint64_t(blockIdx.x) * 4u + wv;
+  if (pair >= uint64_t(a.n_queries) * a.hq) return;
+  const uint32_t qi = uint32_t(pair / a.hq), h = uint32_t(pair % a.hq);
   const uint32_t grp = a.hq / a.hkv;
   const uint32_t hgk = (grp + UH - 1) / UH;
   const uint32_t segq = a.hkv * hgk;
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
   const uint32_t i = a.qlist ? a.qlist[qi] : qi;
   T *out = static_cast<T *>(a.out) + (uint64_t(i) * a.hq + h) * a.dv;
   if (ntq == 0u) {
-    for (uint32_t d = tid; d < a.dv; d += 256) out[d] = DT::from_f(0.f);
+    for (uint32_t d = lane; d < a.dv; d += 64) out[d] = DT::from_f(0.f);
     return;
   }
   const uint32_t groups = a.bal_waves / segq;
@@ -546,41 +552,56 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
     const uint32_t slot = p == 0u ? 2u * u + 1u : 2u * u;
     return uint64_t(slot) * UH + hl;
   };
-
-  float mx = kNoMax;
-  for (uint32_t p = tid; p < np; p += 256) mx = fmaxf(mx, a.ws_lse[row_of(p)]);
-  mx = wave_max(mx);
-  if (lane == 0) s_red[wv] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  float ws = 0.f;
-  for (uint32_t p = tid; p < np; p += 256) ws += fast_exp2(a.ws_lse[row_of(p)] - mx);
-  ws = wave_sum(ws);
-  if (lane == 0) s_red[4 + wv] = ws;
-  __syncthreads();
-  const float total = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
-  const float inv = total > 0.f ? 1.f / total : 0.f;
-
-  // value elements d = tid, tid + 256, ... (dv <= 1024); pieces in chunks of
-  // 256 weights
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (uint32_t p0 = 0; p0 < np; p0 += 256) {
-    const uint32_t pc = np - p0 < 256u ? np - p0 : 256u;
-    __syncthreads();  // the previous chunk's weights are no longer read
-    s_w[tid] = tid < pc ? fast_exp2(a.ws_lse[row_of(p0 + tid)] - mx) : 0.f;
-    __syncthreads();
-    for (uint32_t d = tid, e = 0; d < a.dv && e < 4; d += 256, ++e) {
-      float x0 = 0.f, x1 = 0.f;
-      uint32_t p = 0;
-      for (; p + 2 <= pc; p += 2) {
-        x0 = fmaf(s_w[p], a.ws_o[row_of(p0 + p) * a.dv + d], x0);
-        x1 = fmaf(s_w[p + 1], a.ws_o[row_of(p0 + p + 1) * a.dv + d], x1);
+  const uint32_t ne = (a.dv + 255u) / 256u;  // float4 groups per lane
+  f32x4_t acc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mx = kNoMax, den = 0.f;
+  for (uint32_t p0 = 0; p0 < np; p0 += kBatch) {
+    const uint32_t pc = np - p0 < kBatch ? np - p0 : kBatch;
+    float lse[kBatch];
+    f32x4_t ov[kBatch][4];
+#pragma unroll
+    for (uint32_t b = 0; b < kBatch; ++b) {
+      lse[b] = kNoMax;
+      if (b < pc) {
+        const uint64_t r = row_of(p0 + b);
+        lse[b] = a.ws_lse[r];
+#pragma unroll
+        for (uint32_t e = 0; e < 4; ++e) {
+          const uint32_t d = 4u * lane + 256u * e;
+          if (e < ne && d < a.dv) ov[b][e] = *reinterpret_cast<const f32x4_t *>(a.ws_o + r * a.dv + d);
+        }
       }
-      if (p < pc) x0 = fmaf(s_w[p], a.ws_o[row_of(p0 + p) * a.dv + d], x0);
-      acc[e] += x0 + x1;
+    }
+    float bm = mx;
+#pragma unroll
+    for (uint32_t b = 0; b < kBatch; ++b) bm = fmaxf(bm, lse[b]);
+    const float sc = fast_exp2(mx - bm);
+    den *= sc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= sc;
+#pragma unroll
+    for (uint32_t b = 0; b < kBatch; ++b) {
+      if (b < pc) {
+        const float w = fast_exp2(lse[b] - bm);
+        den += w;
+#pragma unroll
+        for (uint32_t e = 0; e < 4; ++e)
+          if (e < ne && 4u * lane + 256u * e < a.dv) acc[e] += w * ov[b][e];
+      }
+    }
+    mx = bm;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (uint32_t e = 0; e < 4; ++e) {
+    const uint32_t d = 4u * lane + 256u * e;
+    if (e < ne && d < a.dv) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) out[d + c] = DT::from_f(acc[e][c] * inv);
     }
   }
-  for (uint32_t d = tid, e = 0; d < a.dv && e < 4; d += 256, ++e) out[d] = DT::from_f(acc[e] * inv);
 }
 
 template <class DT, bool PU, bool F8>
@@ -691,8 +712,11 @@ hipError_t launch_rows_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st) 
 
 hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, uint32_t unit_heads,
                                  hipStream_t st) {
-  const uint64_t blocks = uint64_t(a.n_queries) * a.hq;
-  if (blocks == 0) return hipSuccess;
+  const uint64_t pairs = uint64_t(a.n_queries) * a.hq;  // one wave each, four per block
+  if (pairs == 0) return hipSuccess;
+  if (a.dv % 4 != 0 || a.dv > 1024) return hipErrorInvalidValue;
+  const uint64_t blocks = (pairs + 3) / 4;
+  if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<uint32_t>(blocks));
   if (unit_heads != uint32_t(kHeads) && unit_heads != kMlaBlockHeads) return hipErrorInvalidValue;
   const bool mla = unit_heads == kMlaBlockHeads;
