@@ -16,12 +16,16 @@ algorithmic K/V bytes of a step (every visible token row of every KV head
 read once) divided by the wall time per step.
 
 The JSON line also carries:
-  roofline      the dominant kernel (the split decode kernel) against the
-                8 TB/s HBM peak; its duration is measured live with HIP events
-                that the library records around that kernel on its stream
-                (pkv_plan_timing).  `traffic` is the HBM bytes per launch from
-                the committed rocprofv3 counter summary when it was taken on
-                the current kernel source, else null.
+  roofline      the dominant kernel (the decode kernel) against the 8 TB/s
+                HBM peak; its duration is measured live over the timed steps
+                with HIP events that the kernel's own dispatch records on its
+                stream (pkv_plan_timing_select; only that kernel is timed
+                there).  `traffic` is the HBM bytes per launch from the
+                committed rocprofv3 counter summary when it was taken on the
+                current kernel source, else null.
+  kernel_breakdown
+                every kernel of a step (decode, merge), timed the same way
+                over a few more steps after the timed region.
   prefill       the chunked-prefill tile kernel on the mixed prefill + decode
                 workload (8 chunks x 512 queries + 120 decode rows): useful
                 FLOPs of the chunk queries / tile-kernel time, against the
@@ -403,26 +407,37 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    plan.timing(True)
+    # Inside the timed steps only the dominant kernel records its events (a
+    # timed launch costs a few microseconds of dispatch overhead).
+    plan.timing(True, kernels=(main_kernel,))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    n_main, ms_main = plan.timing_read(main_kernel)
+    plan.timing(False)
+    if n_main == 0:
+        sys.exit(f"the {main_kernel} kernel did not run in the timed steps")
+    ms_per_step = wall * 1e3 / args.steps
+    avg_main_us = round(ms_main / n_main * 1e3, 2)
+
+    # Per-kernel breakdown from a few more steps after the timed region, with
+    # every kernel timed.
+    plan.timing(True)
+    for _ in range(min(args.steps, 10)):
+        step()
+    torch.cuda.synchronize()
     kernels = {}
     for name in ("rows", "tiles", "mla", "merge"):
         n, ms = plan.timing_read(name)
         if n:
             kernels[name] = {"launches": n, "avg_us": round(ms / n * 1e3, 2)}
     plan.timing(False)
-    ms_per_step = wall * 1e3 / args.steps
 
     nbytes = workloads.attention_bytes(wl)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    if main_kernel not in kernels:  # e.g. a workload whose queries all went to tiles
-        main_kernel = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    avg_main_us = kernels[main_kernel]["avg_us"]
     achieved = nbytes / (avg_main_us * 1e-6) / 1e9
     traffic = traffic_from_summary() if args.workload == 2 and main_kernel == "rows" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -447,7 +462,7 @@ def main():
                    "splits": "balanced" if splits == 0 else splits,
                    "kv_bytes_per_step": nbytes, "parallelism": "single GPU"},
         "roofline": roofline,
-        "kernels": kernels,
+        "kernel_breakdown": kernels,
     }
     if not args.no_prefill and wl.kind == "attention":
         line["prefill"] = prefill_measure(torch, pkv, workloads, args.prefill_steps)

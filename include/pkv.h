@@ -338,14 +338,16 @@ pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k,
 
 /* ------------------------------------------------------------- timing
  * Per-kernel timing, for benchmarks.  While enabled on a plan, every
- * pkv_attention / pkv_mla / pkv_append call with that plan records a pair
- * of HIP events around each kernel it launches, on the call's stream, so a
- * kernel's duration is measured on the stream it runs on.  Kernels: the
- * per-query row kernel (decode rows, split parts), the chunked-prefill tile
- * kernel, the MLA kernel, the split merge, and the cache append.  Enabling
- * clears earlier records.  Not for use while the stream is being captured into a graph (the event
- * records would be captured too).  Errors: PKV_EINVAL (null plan, unknown
- * kernel, null output), PKV_EHIP (event creation or query failure). */
+ * pkv_attention / pkv_mla / pkv_append call with that plan has each kernel
+ * it launches record a pair of HIP events at the kernel's own start and end
+ * (hipExtLaunchKernel's event arguments: the timestamps belong to the
+ * dispatch, on the call's stream, and add no packets between kernels).
+ * Kernels: the per-query row kernel (decode rows, split parts, balanced
+ * ranges), the chunked-prefill tile kernel, the MLA kernel, the merges
+ * (split and balanced), and the cache append.  Enabling clears earlier
+ * records.  Calls on a stream that is being captured into a graph are not
+ * timed.  Errors: PKV_EINVAL (null plan, unknown kernel, null output),
+ * PKV_EHIP (event creation or query failure). */
 typedef enum {
   PKV_KERNEL_ROWS = 0,
   PKV_KERNEL_TILES = 1,
@@ -355,6 +357,14 @@ typedef enum {
 } pkv_kernel;
 
 pkv_status pkv_plan_timing(pkv_plan *plan, int enable);
+
+/* Timing limited to the kernels whose bit (1u << pkv_kernel) is set in
+ * kernel_mask; 0 turns timing off, and pkv_plan_timing(plan, 1) is the mask
+ * of every kernel.  A timed launch costs a few microseconds of dispatch
+ * overhead, so a benchmark times only the kernel it reports.  Enabling
+ * clears earlier records.  Errors: PKV_EINVAL (null plan, bits beyond
+ * PKV_KERNEL_APPEND). */
+pkv_status pkv_plan_timing_select(pkv_plan *plan, uint32_t kernel_mask);
 
 /* Number of recorded launches of `kernel` and their summed duration in
  * milliseconds (waits for the recorded events to complete). */

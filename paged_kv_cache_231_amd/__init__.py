@@ -156,10 +156,15 @@ class Plan:
 
     KERNELS = {"rows": 0, "tiles": 1, "mla": 2, "merge": 3, "append": 4}
 
-    def timing(self, enable: bool = True) -> None:
-        """Record HIP events around every kernel launched with this plan
-        (pkv_plan_timing); enabling clears earlier records."""
-        check(lib().pkv_plan_timing(self.handle, 1 if enable else 0))
+    def timing(self, enable: bool = True, kernels=None) -> None:
+        """Record HIP events at the start and end of every kernel launched
+        with this plan (pkv_plan_timing), or only of the named ``kernels``
+        (pkv_plan_timing_select); enabling clears earlier records."""
+        if kernels is None:
+            check(lib().pkv_plan_timing(self.handle, 1 if enable else 0))
+        else:
+            mask = sum(1 << self.KERNELS[k] for k in set(kernels)) if enable else 0
+            check(lib().pkv_plan_timing_select(self.handle, mask))
 
     def timing_read(self, kernel: str):
         """(launches, summed milliseconds) of one kernel since timing was enabled."""

@@ -59,6 +59,7 @@ SIGNATURES = {
     "pkv_append": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _u32, _u32, _u32,
                         ctypes.POINTER(AppendReport), _p]),
     "pkv_plan_timing": (_i, [_p, _i]),
+    "pkv_plan_timing_select": (_i, [_p, _u32]),
     "pkv_plan_timing_read": (_i, [_p, _i, ctypes.POINTER(_u32), ctypes.POINTER(ctypes.c_double)]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),

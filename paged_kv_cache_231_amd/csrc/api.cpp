@@ -28,7 +28,7 @@ struct pkv_plan {
     int kernel;
     hipEvent_t start, stop;
   };
-  bool timing = false;
+  uint32_t timing = 0;  // mask of timed kernels (1 << pkv_kernel)
   mutable std::vector<Rec> recs;
   mutable std::vector<hipEvent_t> spare;
 };
@@ -117,20 +117,37 @@ hipEvent_t take_event(const pkv_plan *plan) {
   return hipEventCreate(&e) == hipSuccess ? e : nullptr;
 }
 
-// Brackets one kernel launch with HIP events when the plan's timing is on.
+}  // namespace
+LaunchEvents &launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+namespace {
+
+// Times the kernel launched inside its scope when the plan's timing is on:
+// the launch records a pair of HIP events at the kernel's own start and end
+// (launch_k).  A scope that launches nothing records nothing; a stream being
+// captured into a graph is not timed.
 class Timed {
  public:
-  Timed(const pkv_plan *plan, pkv_kernel kernel, hipStream_t st) : plan_(plan), st_(st) {
-    if (!plan_->timing) return;
+  Timed(const pkv_plan *plan, pkv_kernel kernel, hipStream_t st) : plan_(plan) {
+    if (!(plan_->timing >> uint32_t(kernel) & 1u)) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
     rec_.kernel = int(kernel);
     rec_.start = take_event(plan_);
     rec_.stop = take_event(plan_);
-    if (rec_.start && rec_.stop && hipEventRecord(rec_.start, st_) == hipSuccess) on_ = true;
+    if (rec_.start && rec_.stop) {
+      launch_events() = LaunchEvents{rec_.start, rec_.stop, false};
+      on_ = true;
+    }
   }
   ~Timed() {
-    if (on_ && hipEventRecord(rec_.stop, st_) == hipSuccess) {
+    const bool used = on_ && launch_events().used;
+    launch_events() = LaunchEvents{};
+    if (used) {
       plan_->recs.push_back(rec_);
-    } else if (plan_->timing) {
+    } else {
       if (rec_.start) plan_->spare.push_back(rec_.start);
       if (rec_.stop) plan_->spare.push_back(rec_.stop);
     }
@@ -138,7 +155,6 @@ class Timed {
 
  private:
   const pkv_plan *plan_;
-  hipStream_t st_;
   pkv_plan::Rec rec_{};
   bool on_ = false;
 };
@@ -401,16 +417,21 @@ void pkv_plan_destroy(pkv_plan *plan) {
   delete plan;
 }
 
-pkv_status pkv_plan_timing(pkv_plan *plan, int enable) {
+pkv_status pkv_plan_timing_select(pkv_plan *plan, uint32_t kernel_mask) {
   clear_error();
   if (!plan) return fail(PKV_EINVAL, "null plan");
+  if (kernel_mask >> (uint32_t(PKV_KERNEL_APPEND) + 1u)) return fail(PKV_EINVAL, "unknown kernel in the mask");
   for (const auto &r : plan->recs) {
     plan->spare.push_back(r.start);
     plan->spare.push_back(r.stop);
   }
   plan->recs.clear();
-  plan->timing = enable != 0;
+  plan->timing = kernel_mask;
   return PKV_OK;
+}
+
+pkv_status pkv_plan_timing(pkv_plan *plan, int enable) {
+  return pkv_plan_timing_select(plan, enable ? (2u << uint32_t(PKV_KERNEL_APPEND)) - 1u : 0u);
 }
 
 pkv_status pkv_plan_timing_read(pkv_plan *plan, pkv_kernel kernel, uint32_t *launches,

@@ -73,11 +73,11 @@ hipError_t launch_append(AppendArgs a, uint64_t k_block_bytes, uint64_t v_block_
   if (per_q > 0xFFFFFFFFull || chunks > 65535) return hipErrorInvalidValue;
   const dim3 grid(a.n_queries, uint32_t(chunks));
   if (unit == 16)
-    hipLaunchKernelGGL(append_kernel<u32x4_t>, grid, dim3(256), 0, st, a);
+    launch_k(append_kernel<u32x4_t>, grid, dim3(256), 0, st, a);
   else if (unit == 4)
-    hipLaunchKernelGGL(append_kernel<uint32_t>, grid, dim3(256), 0, st, a);
+    launch_k(append_kernel<uint32_t>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(256), 0, st, a);
+    launch_k(append_kernel<uint16_t>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

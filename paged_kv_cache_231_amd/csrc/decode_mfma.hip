@@ -607,9 +607,9 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(MergeArgs a) {
 template <class DT, bool PU, bool F8>
 hipError_t launch_d(const RowArgs &a, dim3 grid, hipStream_t st) {
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<DT, 64, PU, F8>), grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_mfma_kernel<DT, 128, PU, F8>), grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((decode_mfma_kernel<DT, 256, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 64: launch_k((decode_mfma_kernel<DT, 64, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 128: launch_k((decode_mfma_kernel<DT, 128, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 256: launch_k((decode_mfma_kernel<DT, 256, PU, F8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
@@ -618,9 +618,9 @@ hipError_t launch_d(const RowArgs &a, dim3 grid, hipStream_t st) {
 template <class DT, bool PU, bool F8>
 hipError_t launch_bal_d(const RowArgs &a, dim3 grid, hipStream_t st) {
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((decode_balanced_kernel<DT, 64, PU, F8>), grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_balanced_kernel<DT, 128, PU, F8>), grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((decode_balanced_kernel<DT, 256, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 64: launch_k((decode_balanced_kernel<DT, 64, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 128: launch_k((decode_balanced_kernel<DT, 128, PU, F8>), grid, dim3(256), 0, st, a); break;
+    case 256: launch_k((decode_balanced_kernel<DT, 256, PU, F8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
@@ -722,12 +722,12 @@ hipError_t launch_merge_balanced(const MergeArgs &a, pkv_dtype dt, uint32_t unit
   const bool mla = unit_heads == kMlaBlockHeads;
   switch (dt) {
     case PKV_F16:
-      if (mla) hipLaunchKernelGGL((merge_balanced_kernel<F16, kMlaBlockHeads>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((merge_balanced_kernel<F16, kHeads>), grid, dim3(256), 0, st, a);
+      if (mla) launch_k((merge_balanced_kernel<F16, kMlaBlockHeads>), grid, dim3(256), 0, st, a);
+      else launch_k((merge_balanced_kernel<F16, kHeads>), grid, dim3(256), 0, st, a);
       break;
     case PKV_BF16:
-      if (mla) hipLaunchKernelGGL((merge_balanced_kernel<BF16, kMlaBlockHeads>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((merge_balanced_kernel<BF16, kHeads>), grid, dim3(256), 0, st, a);
+      if (mla) launch_k((merge_balanced_kernel<BF16, kMlaBlockHeads>), grid, dim3(256), 0, st, a);
+      else launch_k((merge_balanced_kernel<BF16, kHeads>), grid, dim3(256), 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }

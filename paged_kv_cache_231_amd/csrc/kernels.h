@@ -2,6 +2,7 @@
 // (api.cpp) and the HIP sources.  All strides are in elements.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -9,6 +10,28 @@
 #include "pkv.h"
 
 namespace pkv {
+
+// Per-kernel timing.  While the host dispatcher times a launch it sets this
+// thread's LaunchEvents; the next launch_k records the kernel's own start
+// and end in them (part of its dispatch, so no separate event packets sit
+// between kernels), marks them used and clears them.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+LaunchEvents &launch_events();  // this thread's (defined in api.cpp)
+
+// Every kernel of the library is launched through here.
+template <typename... Args, typename F = void (*)(Args...)>
+inline void launch_k(F kernel, const dim3 &grid, const dim3 &block, uint32_t shmem, hipStream_t st,
+                     Args... args) {
+  LaunchEvents &ev = launch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev.start, ev.stop, 0u, args...);
+  if (ev.start) {
+    ev.start = ev.stop = nullptr;
+    ev.used = true;
+  }
+}
 
 // Where a kernel finds the schedule inside the device plan words.
 struct PlanView {

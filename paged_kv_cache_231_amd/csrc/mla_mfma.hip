@@ -472,9 +472,9 @@ hipError_t launch_mla_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
   if (a.bal_waves == 0 || a.bal_waves % (8 * hg) != 0) return hipErrorInvalidValue;
   const dim3 grid(a.bal_waves);
   if (dt == PKV_BF16)
-    hipLaunchKernelGGL((mla_balanced_kernel<BF16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+    launch_k((mla_balanced_kernel<BF16, 512, 64>), grid, dim3(256), 0, st, a, hg);
   else
-    hipLaunchKernelGGL((mla_balanced_kernel<F16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+    launch_k((mla_balanced_kernel<F16, 512, 64>), grid, dim3(256), 0, st, a, hg);
   return hipGetLastError();
 }
 
@@ -484,9 +484,9 @@ hipError_t launch_mla_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(blocks));  // a multiple of 8 * hg
   if (dt == PKV_BF16)
-    hipLaunchKernelGGL((mla_kernel<BF16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+    launch_k((mla_kernel<BF16, 512, 64>), grid, dim3(256), 0, st, a, hg);
   else
-    hipLaunchKernelGGL((mla_kernel<F16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+    launch_k((mla_kernel<F16, 512, 64>), grid, dim3(256), 0, st, a, hg);
   return hipGetLastError();
 }
 

@@ -254,10 +254,10 @@ __global__ __launch_bounds__(256) void rows_fast_kernel(RowArgs a) {
 template <class DT, int D>
 hipError_t launch_gt(const RowArgs &a, int gt, dim3 grid, hipStream_t st) {
   switch (gt) {
-    case 1: hipLaunchKernelGGL((rows_fast_kernel<DT, D, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((rows_fast_kernel<DT, D, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((rows_fast_kernel<DT, D, 4>), grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((rows_fast_kernel<DT, D, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: launch_k((rows_fast_kernel<DT, D, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: launch_k((rows_fast_kernel<DT, D, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: launch_k((rows_fast_kernel<DT, D, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: launch_k((rows_fast_kernel<DT, D, 8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

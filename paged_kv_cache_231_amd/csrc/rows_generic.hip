@@ -181,9 +181,9 @@ hipError_t launch_rows_generic(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(blocks));
   switch (dt) {
-    case PKV_F32: hipLaunchKernelGGL(rows_generic_kernel<F32>, grid, dim3(64), 0, st, a); break;
-    case PKV_F16: hipLaunchKernelGGL(rows_generic_kernel<F16>, grid, dim3(64), 0, st, a); break;
-    case PKV_BF16: hipLaunchKernelGGL(rows_generic_kernel<BF16>, grid, dim3(64), 0, st, a); break;
+    case PKV_F32: launch_k(rows_generic_kernel<F32>, grid, dim3(64), 0, st, a); break;
+    case PKV_F16: launch_k(rows_generic_kernel<F16>, grid, dim3(64), 0, st, a); break;
+    case PKV_BF16: launch_k(rows_generic_kernel<BF16>, grid, dim3(64), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -194,9 +194,9 @@ hipError_t launch_merge(const MergeArgs &a, pkv_dtype dt, hipStream_t st) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(blocks));
   switch (dt) {
-    case PKV_F32: hipLaunchKernelGGL(merge_kernel<F32>, grid, dim3(256), 0, st, a); break;
-    case PKV_F16: hipLaunchKernelGGL(merge_kernel<F16>, grid, dim3(256), 0, st, a); break;
-    case PKV_BF16: hipLaunchKernelGGL(merge_kernel<BF16>, grid, dim3(256), 0, st, a); break;
+    case PKV_F32: launch_k(merge_kernel<F32>, grid, dim3(256), 0, st, a); break;
+    case PKV_F16: launch_k(merge_kernel<F16>, grid, dim3(256), 0, st, a); break;
+    case PKV_BF16: launch_k(merge_kernel<BF16>, grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -490,11 +490,11 @@ hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st) {
   const dim3 grid(static_cast<uint32_t>(blocks));
   const uint32_t ng = uint32_t(n_groups);
   if (dt == PKV_BF16) {
-    if (a.d == 64) hipLaunchKernelGGL((prefill_kernel<BF16, 64>), grid, dim3(256), 0, st, a, n_sub, ng);
-    else hipLaunchKernelGGL((prefill_kernel<BF16, 128>), grid, dim3(256), 0, st, a, n_sub, ng);
+    if (a.d == 64) launch_k((prefill_kernel<BF16, 64>), grid, dim3(256), 0, st, a, n_sub, ng);
+    else launch_k((prefill_kernel<BF16, 128>), grid, dim3(256), 0, st, a, n_sub, ng);
   } else {
-    if (a.d == 64) hipLaunchKernelGGL((prefill_kernel<F16, 64>), grid, dim3(256), 0, st, a, n_sub, ng);
-    else hipLaunchKernelGGL((prefill_kernel<F16, 128>), grid, dim3(256), 0, st, a, n_sub, ng);
+    if (a.d == 64) launch_k((prefill_kernel<F16, 64>), grid, dim3(256), 0, st, a, n_sub, ng);
+    else launch_k((prefill_kernel<F16, 128>), grid, dim3(256), 0, st, a, n_sub, ng);
   }
   return hipGetLastError();
 }

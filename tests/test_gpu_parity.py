@@ -117,6 +117,17 @@ def test_kernel_timing_records_each_launch():
     plan.timing(False)
     run(wl, plan=plan, dev=dev)
     assert plan.timing_read("rows") == (0, 0.0)
+    # pkv_plan_timing_select: only the selected kernel records; the events
+    # come from the kernel's own dispatch, so the time is positive
+    plan.timing(True, kernels=("rows",))
+    for _ in range(2):
+        run(wl, splits=3, plan=plan, dev=dev)
+    n_rows, ms_rows = plan.timing_read("rows")
+    assert n_rows == 2 and ms_rows > 0
+    assert plan.timing_read("merge") == (0, 0.0)
+    plan.timing(False)
+    with pytest.raises(pkv.PKVError):
+        pkv.check(pkv.lib().pkv_plan_timing_select(plan.handle, 1 << 5))
 
 
 def test_tune_splits_picks_a_candidate_and_leaves_the_result():
