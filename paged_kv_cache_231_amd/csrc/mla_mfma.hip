@@ -340,12 +340,27 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
     }
 
     // O^T += latent^T . P^T over 32 tokens: K slots 8j .. 8j+3 are rows
-    // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16.
+    // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16.  The two
+    // transposed reads of block b + kPvAhead are issued before the MFMA of
+    // block b and the order is fenced, so every MFMA finds its operand
+    // loaded (left to itself the compiler reads one block at a time and
+    // waits for each pair).
+    {
+      constexpr int kPvAhead = 4;
+      auto load_v = [&](int b) -> uint4 {
+        const unsigned char *p0 = st_lat + pv_off[b & 7] + 256 * (b >> 3);
+        const uint2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * L::kLatRow);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      uint4 va[kPvAhead + 1];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const unsigned char *p0 = st_lat + pv_off[b & 7] + 256 * (b >> 3);
-      const uint2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * L::kLatRow);
-      o[b] = M::qk(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[b]);
+      for (int b = 0; b < kPvAhead; ++b) va[b] = load_v(b);
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        if (b + kPvAhead < DB) va[(b + kPvAhead) % (kPvAhead + 1)] = load_v(b + kPvAhead);
+        o[b] = M::qk(va[b % (kPvAhead + 1)], pb, o[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (kt + kStages - 1 < n_tiles) {
       window_for(kt + kStages - 1);

@@ -428,14 +428,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
 
     __builtin_amdgcn_s_setprio(0);
     // O^T += V^T . P^T over the 32 keys: K slots 8j .. 8j+3 are key rows
-    // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16
+    // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16.  The reads of
+    // block b + kPvAhead are issued before the MFMAs of block b and the
+    // order is fenced, so the transposed-read latency hides behind the
+    // MFMAs in flight.
+    {
+      constexpr int kPvAhead = 3;
+      auto load_v = [&](int b) -> uint4 {
+        const unsigned char *p0 = vt_lds + pv_off[b];
+        const uint2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * L::kRowB);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      uint4 va[kPvAhead + 1];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const unsigned char *p0 = vt_lds + pv_off[b];
-      const uint2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * L::kRowB);
-      const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      o[0][b] = M::qk(va, pb[0], o[0][b]);
-      o[1][b] = M::qk(va, pb[1], o[1][b]);
+      for (int b = 0; b < kPvAhead && b < DB; ++b) va[b] = load_v(b);
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        if (b + kPvAhead < DB) va[(b + kPvAhead) % (kPvAhead + 1)] = load_v(b + kPvAhead);
+        o[0][b] = M::qk(va[b % (kPvAhead + 1)], pb[0], o[0][b]);
+        o[1][b] = M::qk(va[b % (kPvAhead + 1)], pb[1], o[1][b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     lacc[0] = M::qk(ones, pb[0], lacc[0]);
     lacc[1] = M::qk(ones, pb[1], lacc[1]);
