@@ -296,7 +296,10 @@ pkv_status pkv_attention_fp8(const pkv_plan *plan, pkv_dtype dtype,
  *   out[i,h,:] = softmax_t(x) . latent_t                 -> [Q, heads, rank]
  *   q_abs  [Q, heads, rank]      q_pos [Q, heads, pos_dim]
  *   latent [N, ps, 1, rank]      k_pos [N, ps, 1, pos_dim]
- * `scale` comes from the model's QK dimensions, not from rank.
+ * `scale` comes from the model's QK dimensions, not from rank.  Workspace:
+ * none (one pass per query), split (parts merged by log-sum-exp) or
+ * balanced (equal ranges of 32-token tiles per group of 64-head blocks, for
+ * F16/BF16 with rank 512 and pos_dim 64; other shapes run unsplit with it).
  * Errors: as pkv_attention; PKV_ESHAPE for rank outside 1..1024 or pos_dim
  * outside 1..256. */
 pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs,
