@@ -28,9 +28,9 @@ def _mla(dtype, h, ps, lens, seed, queries=None, causal=True):
 @pytest.mark.parametrize("h,ps", [(128, 64), (16, 16), (40, 5), (256, 1), (100, 64)])
 def test_mla_balanced_shapes(dtype, h, ps):
     """Ragged head groups (16, 40: one partial 64-head group; 100: a whole
-    and a partial one; 256: four),
-    page sizes 1/5/16/64, lengths inside, on and across a 32-token tile,
-    and two queries that are not at their sequence's end."""
+    and a partial one; 256: four), page sizes 1/5/16/64, lengths inside, on
+    and across a 32-token tile, and two queries that are not at their
+    sequence's end."""
     lens = [1, 31, 32, 33, 300, 1000]
     queries = decode_queries(lens) + [(4, 17), (5, 500)]
     wl = _mla(dtype, h, ps, lens, 2000 + h + ps, queries)
