@@ -65,18 +65,14 @@ __device__ __forceinline__ void block_sync_lds() {
 // (inline assembly: the compiler's wait insertion would otherwise drain the
 // ring before every LDS read; the ring's explicit waits order it).  The first
 // form takes a per-lane address, the second a uniform base plus a per-lane
-// 32-bit byte offset.
+// 32-bit byte offset.  The LDS base goes in through an M0 operand, so the
+// compiler itself sets M0 and knows what it holds.
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_base), "v"(src)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base) : "memory");
 }
 __device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_base), "v"(voff), "s"(base)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds_base)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

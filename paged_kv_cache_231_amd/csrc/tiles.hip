@@ -83,12 +83,10 @@ __device__ __forceinline__ void block_sync_lds() {
 // 16 bytes land at LDS byte address lds_base + 16 * l.  Written as inline
 // assembly so the compiler's wait insertion does not treat every later LDS
 // read as dependent on it: the ring's explicit vmcnt waits and barriers order
-// these loads against the reads.
+// these loads against the reads.  The LDS base is an M0 operand, so the
+// compiler sets M0 itself and knows what it holds.
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_base), "v"(src)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
