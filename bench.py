@@ -30,6 +30,10 @@ The JSON line also carries:
                 workload (8 chunks x 512 queries + 120 decode rows): useful
                 FLOPs of the chunk queries / tile-kernel time, against the
                 dense bf16 MFMA peak.
+With --workload 4 (that mixed workload as the step) the roofline is the tile
+kernel's FLOP rate against the MFMA peak and `value` is useful TFLOP/s per
+step; with --workload 5 (MLA) the roofline is HBM with the MFMA fraction
+beside it.
   append, window, fp8
                 the cache append, sliding-window decode and FP8-cache decode
                 legs (per-kernel HIP-event durations).
@@ -161,6 +165,20 @@ def cpu_baseline(wl, budget_s: float):
                       f"(float64 numpy, {elapsed:.1f} s, {done_bytes / 1e9:.3f} GB of cache rows)"}
 
 
+def tile_query_flops(plan, wl) -> int:
+    """Useful FLOPs of the queries the tile kernel owns: every query that is
+    not a decode row of the plan (plan words: header, lens, qseq, qpos, rows)."""
+    words = plan.words
+    R = int(words[7])
+    S, Q = int(words[3]), int(words[2])
+    rows_off = 16 + S + 2 * Q
+    in_rows = np.zeros(Q, dtype=bool)
+    in_rows[np.asarray(words[rows_off:rows_off + R], dtype=np.int64)] = True
+    vis = wl.visible().astype(np.int64)
+    hq, d, dv = wl.info["hq"], wl.info["d"], wl.info["dv"]
+    return int(vis[~in_rows].sum()) * hq * 2 * (d + dv)
+
+
 def prefill_measure(torch, pkv, workloads, steps: int):
     """Tile-kernel TFLOP/s on the mixed chunked-prefill workload."""
     wl = workloads.config(4)
@@ -185,16 +203,8 @@ def prefill_measure(torch, pkv, workloads, steps: int):
     n_t, ms_t = plan.timing_read("tiles")
     n_r, ms_r = plan.timing_read("rows")
     plan.timing(False)
-    # useful FLOPs of the queries the tile kernel owns (every query that is
-    # not a decode row of the plan)
-    words = plan.words
-    R, T = int(words[7]), int(words[8])
-    S, Q = int(words[3]), int(words[2])
-    rows_off = 16 + S + 2 * Q
-    in_rows = np.zeros(Q, dtype=bool)
-    in_rows[np.asarray(words[rows_off:rows_off + R], dtype=np.int64)] = True
-    vis = wl.visible().astype(np.int64)
-    flops = int(vis[~in_rows].sum()) * hq * 2 * (d + dv)
+    T = int(plan.words[8])
+    flops = tile_query_flops(plan, wl)
     avg_t = ms_t / max(1, n_t)
     tfs = flops / (avg_t * 1e-3) / 1e12
     return {"value": round(tfs, 1), "unit": "TFLOP/s", "peak": MFMA_BF16_PEAK_TFS,
@@ -437,18 +447,40 @@ def main():
     plan.timing(False)
 
     nbytes = workloads.attention_bytes(wl)
-    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    if main_kernel == "tiles":
+        # a step led by chunk queries, which re-read the same K/V rows: its
+        # rate is useful FLOPs per second
+        value, unit = workloads.attention_flops(wl) / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+    else:
+        value, unit = nbytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
     achieved = nbytes / (avg_main_us * 1e-6) / 1e9
     traffic = traffic_from_summary() if args.workload == 2 and main_kernel == "rows" else None
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": {"rows": "split-KV decode", "tiles": "chunked-prefill tiles",
-                           "mla": "MLA decode", "merge": "split merge"}[main_kernel],
-                "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": avg_main_us}
+    kernel_name = {"rows": "split-KV decode", "tiles": "chunked-prefill tiles",
+                   "mla": "MLA decode", "merge": "split merge"}[main_kernel]
+    if main_kernel == "tiles":
+        # the chunk queries' attention is a dense contraction: MFMA-bound
+        flops = tile_query_flops(plan, wl)
+        tfs = flops / (avg_main_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                    "traffic": None, "kernel": kernel_name,
+                    "algorithmic_flops_per_launch": flops, "avg_launch_us": avg_main_us}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": kernel_name,
+                    "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": avg_main_us}
+        if main_kernel == "mla":
+            # near the ridge point: the matrix-core fraction beside the HBM one
+            flops = workloads.attention_flops(wl)
+            tfs = flops / (avg_main_us * 1e-6) / 1e12
+            roofline.update({"mfma_achieved_tflops": round(tfs, 1),
+                             "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                             "algorithmic_flops_per_launch": flops})
     line = {
         "metric": "paged decode KV-read GB/s (% of HBM peak); chunked-prefill TFLOP/s (% MFMA)",
         "value": round(value, 1),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
