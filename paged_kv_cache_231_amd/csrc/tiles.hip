@@ -192,6 +192,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
 #pragma unroll
     for (int b = 0; b < DB; ++b) o[nt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m[2] = {kNoMax, kNoMax};
+  // a row's reference moves only when a raw score passes (m + kSlack) /
+  // scale_log2; kNoMax makes the first visible score do so
+  float thr[2] = {kNoMax, kNoMax};
   // Softmax denominators on the matrix core: one more 16-row output block
   // per N-tile whose A operand is all ones, so each of its rows accumulates
   // the sum of P over the keys for the lane's q-row (rescaled with O).
@@ -199,6 +202,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
   uint4 ones;
   ones.x = ones.y = ones.z = ones.w = M::pack2(1.f, 1.f);
   const float sl2 = a.scale_log2;
+  const float inv_sl2 = 1.f / sl2;
   const T *kbase = static_cast<const T *>(a.k) + uint64_t(kvh) * D;
   const T *vbase = static_cast<const T *>(a.v) + uint64_t(kvh) * D;
   __syncthreads();  // table cache ready (Q loads may still be in flight: fine)
@@ -376,28 +380,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     f32x4_t s_next[2][2];
     __builtin_amdgcn_s_setprio(1);
     scores(kt + 1, s_next);
-    // online softmax (base 2); the max is taken on raw scores (scale > 0),
-    // and each probability is exp2(score * scale_log2 - m) with one FMA
+    // online softmax (base 2): each probability is exp2(score * scale_log2
+    // - m) with one FMA, against the row's current reference m
     uint4 pb[2];
-    float alpha[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mt = vmax3(vmax3(x[nt][0][0], x[nt][0][1], x[nt][0][2]),
-                       vmax3(x[nt][0][3], x[nt][1][0], x[nt][1][1]),
-                       vmax3(x[nt][1][2], x[nt][1][3], -INFINITY));
-      mt = rows4_vmax(mt) * sl2;
-      // Lazy rescaling: the reference max only moves when a tile's max
-      // exceeds it by more than kSlack (base 2), so probabilities stay
-      // below 2^kSlack and most tiles skip rescaling O.  The result is the
-      // same softmax: numerator and denominator share the reference.
-      const float m_new = mt > m[nt] + kSlack ? mt : m[nt];
-      alpha[nt] = fast_exp2(m[nt] - m_new);
-      m[nt] = m_new;
+    auto probs = [&](int nt) {
       float p[2][4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[mb][e] = fast_exp2(__builtin_fmaf(x[nt][mb][e], sl2, -m_new));
+        for (int e = 0; e < 4; ++e) p[mb][e] = fast_exp2(__builtin_fmaf(x[nt][mb][e], sl2, -m[nt]));
       // P^T operand in the value reads' row order (see pv_off): pack even
       // and odd rows of each half, then one swap of lanes 32..63 of the even
       // pairs with lanes 0..31 of the odd pairs
@@ -406,7 +397,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
       const auto hi = __builtin_amdgcn_permlane32_swap(M::pack2(p[1][0], p[1][2]),
                                                        M::pack2(p[1][1], p[1][3]), false, false);
       pb[nt] = make_uint4(lo[0], lo[1], hi[0], hi[1]);
-    }
+    };
+    // this lane's largest raw score of each N-tile (8 of the row's 32 keys)
+    float lmax[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      lmax[nt] = vmax3(vmax3(x[nt][0][0], x[nt][0][1], x[nt][0][2]),
+                       vmax3(x[nt][0][3], x[nt][1][0], x[nt][1][1]),
+                       vmax(x[nt][1][2], x[nt][1][3]));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) probs(nt);
     // schedule of the block: the key-tile reads first, then one MFMA per
     // five VALU instructions
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
@@ -415,12 +415,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
-    if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+    // Lazy rescaling: the reference only moves when a row's max exceeds it
+    // by more than kSlack (base 2), so probabilities stay below 2^kSlack and
+    // most tiles take none of this.  The result is the same softmax:
+    // numerator and denominator share the reference.  A lane above its
+    // threshold means its row's max is too, so the row maxima are formed
+    // only here.
+    if (__any(lmax[0] > thr[0] || lmax[1] > thr[1])) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
+        const float mt = rows4_vmax(lmax[nt]) * sl2;
+        const float m_new = mt > m[nt] + kSlack ? mt : m[nt];
+        const float alpha = fast_exp2(m[nt] - m_new);
+        m[nt] = m_new;
+        thr[nt] = (m_new + kSlack) * inv_sl2;
 #pragma unroll
-        for (int b = 0; b < DB; ++b) o[nt][b] *= alpha[nt];
-        lacc[nt] *= alpha[nt];
+        for (int b = 0; b < DB; ++b) o[nt][b] *= alpha;
+        lacc[nt] *= alpha;
+        probs(nt);
       }
     }
 
