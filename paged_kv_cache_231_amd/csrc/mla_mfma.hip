@@ -293,47 +293,54 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) s[mt] = (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
 
-    // online softmax per head; lane (j, c16) holds tokens 16 mt + 4 j + e
+    // online softmax per head; lane (j, c16) holds tokens 16 mt + 4 j + e.
+    // Probabilities are exp2 of the scaled score minus the head's current
+    // reference m.  Lazy rescaling: the reference only moves when a head's
+    // max exceeds it by more than kSlack (base 2), so probabilities stay
+    // below 2^kSlack and most tiles skip what follows the threshold test.
+    // A lane above m + kSlack means its head's max is too, so the head
+    // maxima are formed only then.
     float x[2][4];
-    float mx = -INFINITY;
+    float lmx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool vis = t0 + 16u * mt + 4u * j + e < t_hi;
         x[mt][e] = vis ? s[mt][e] * sl2 : -INFINITY;
-        mx = fmaxf(mx, x[mt][e]);
+        lmx = fmaxf(lmx, x[mt][e]);
       }
-    mx = rows4_max(mx);
-    const float m_new = mx > m + kSlack ? mx : m;
-    const float alpha = fast_exp2(m - m_new);
-    const bool grow = m_new != m;
-    m = m_new;
     float p[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[mt][e] = fast_exp2(x[mt][e] - m_new);
-    lsum = lsum * alpha + (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-                           ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+    uint4 pb;
     // P^T operand in the value reads' row order: lane (j, c16) holds rows
     // 4j .. 4j+3 of each M-tile and needs rows pv_row(j, 0..3).  Pack the
     // even and odd rows separately; one swap of lanes 32..63 of the even
     // pairs with lanes 0..31 of the odd pairs delivers them: lanes of j = 0
     // get rows (0, 2) and (8, 10), j = 1 (4, 6) (12, 14), j = 2 (1, 3)
     // (9, 11), j = 3 (5, 7) (13, 15).
-    uint4 pb;
-    {
+    auto probs = [&]() {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[mt][e] = fast_exp2(x[mt][e] - m);
       const auto lo = __builtin_amdgcn_permlane32_swap(M::pack2(p[0][0], p[0][2]), M::pack2(p[0][1], p[0][3]),
                                                        false, false);
       const auto hi = __builtin_amdgcn_permlane32_swap(M::pack2(p[1][0], p[1][2]), M::pack2(p[1][1], p[1][3]),
                                                        false, false);
       pb = make_uint4(lo[0], lo[1], hi[0], hi[1]);
-    }
-    if (__any(grow)) {
+    };
+    probs();
+    if (__any(lmx > m + kSlack)) {
+      const float mx = rows4_max(lmx);
+      const float m_new = mx > m + kSlack ? mx : m;
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
 #pragma unroll
       for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      probs();
     }
+    lsum += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
 
     // O^T += latent^T . P^T over 32 tokens: K slots 8j .. 8j+3 are rows
     // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16.  The two
