@@ -159,8 +159,11 @@ __device__ __forceinline__ void load_tile(TileRegs<D, F8> &t, const RowArgs &a, 
   }
 }
 
-// Online-softmax state of one wave: running max m (base 2, uniform across
-// the four lane groups of a head), this lane's partial sum and O^T tiles.
+constexpr float kSlack = 8.0f;  // lazy-rescale threshold (log2 units)
+
+// Online-softmax state of one wave: the reference m (base 2, uniform across
+// the four lane groups of a head; within kSlack below the running max or
+// above it), this lane's partial sum and O^T tiles, both relative to m.
 template <int D>
 struct WaveState {
   f32x4_t o[D / 16];
@@ -216,26 +219,35 @@ __device__ __forceinline__ void attend_tile(WaveState<D> &st, const TileRegs<D, 
     s = M::qk(ka, qb[ks], s);
   }
 
+  // Online softmax against the head's reference st.m (base 2).  Lazy
+  // rescaling: the reference only moves when the head's max exceeds it by
+  // more than kSlack, so probabilities stay below 2^kSlack and most tiles
+  // skip the cross-lane max and the rescale.  A lane above st.m + kSlack
+  // means its head's max is too.  o, lsum and st.m share the reference, so
+  // the partial results (and lse = st.m + log2 lsum) are the same softmax.
   float x[4];
-  float mt = -INFINITY;
+  float lmx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const bool v = (t.valid16 >> (4 * j + e)) & 1u;
     x[e] = v ? s[e] * sl2 : -INFINITY;
-    mt = fmaxf(mt, x[e]);
+    lmx = fmaxf(lmx, x[e]);
   }
-  mt = rows4_max(mt);
-  const float m_new = fmaxf(st.m, mt);
-  const float alpha = fast_exp2(st.m - m_new);
-  st.m = m_new;
   float p[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) p[e] = fast_exp2(x[e] - m_new);
-  st.lsum = st.lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  if (__any(alpha != 1.f)) {
+  for (int e = 0; e < 4; ++e) p[e] = fast_exp2(x[e] - st.m);
+  if (__any(lmx > st.m + kSlack)) {
+    const float mt = rows4_max(lmx);
+    const float m_new = mt > st.m + kSlack ? mt : st.m;
+    const float alpha = fast_exp2(st.m - m_new);
+    st.m = m_new;
+    st.lsum *= alpha;
 #pragma unroll
     for (int b = 0; b < DB; ++b) st.o[b] *= alpha;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(x[e] - m_new);
   }
+  st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
   uint2 pb;
   pb.x = M::pack2(p[0], p[1]);
   pb.y = M::pack2(p[2], p[3]);
