@@ -6,8 +6,8 @@ data that happens almost only on a row's first tile, so these cases scale
 the key rows along each sequence: by a ramp (the reference moves on many
 later tiles) and by a spike at mid-sequence (one large jump).  The running
 outputs and denominators are then rescaled mid-stream in the prefill tile
-kernel, in the decode kernels (unsplit, split and balanced schedules) and
-in the MLA kernel (its position rows are scaled, not the latent, which is
+kernel (D = 128 and 64), in the decode kernels (unsplit, split and balanced
+schedules; bf16 and FP8 caches; a sliding window) and in the MLA kernel (its position rows are scaled, not the latent, which is
 also the value).  The scaled rows are rounded to the cache
 dtype on the CPU before either side reads them, so the oracle and the
 library see the same values.
@@ -104,3 +104,65 @@ def test_mla_moving_reference(shape, splits):
     factor = (lambda t, L: 1.0 + t / 16.0) if shape == "ramp" else (lambda t, L: 60.0 if t == L // 2 else 1.0)
     wl = _scale_rows(_quarter(wl, "latent"), "k_pos", factor)
     assert_close(run(wl, splits=splits), expected(wl), torch.bfloat16, f"mla {shape} splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 4, 0])
+def test_fp8_decode_moving_reference(splits):
+    """Decode over an FP8 E4M3 cache built from ramped keys (with key scale
+    1.5 the largest encodable key is 448 * 1.5 = 672, above the largest
+    ramped key of a few hundred; value scale 0.04); the oracle decodes the
+    same bytes."""
+    import oracle
+    import paged_kv_cache_231_amd as pkv
+    from workloads import fp8_caches
+
+    lens = [300, 1000, 2500, 17]
+    wl = build_attention("rescale", 3400, torch.bfloat16, lens, decode_queries(lens), 32, 8, 128, 128,
+                         16, poison=True)
+    wl = _scale_rows(_quarter(wl, "v"), "k", _ramp)
+    ks, vs = 1.5, 0.04
+    k8, v8 = fp8_caches(wl, ks, vs)
+    plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages)
+    ws = pkv.Workspace.for_splits(wl.queries, 32, 128, splits)
+    got = pkv.attention_fp8(plan, wl.tensors["q"].cuda(), k8.cuda(), v8.cuda(), wl.scale, ks, vs,
+                            wl.causal, workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.paged_attention_fp8(wl.tensors["q"], k8, v8, wl.lens, wl.qseq, wl.qpos, wl.table,
+                                      wl.page_size, wl.scale, wl.causal, ks, vs)[0]
+    assert_close(got.double().cpu().numpy(), want, torch.bfloat16, f"fp8 ramp splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [3, 0])
+def test_window_decode_moving_reference(splits):
+    """Sliding-window decode (window 1024) over ramped keys: the reference
+    first forms inside the window and then keeps moving."""
+    import oracle
+    import paged_kv_cache_231_amd as pkv
+
+    lens = [300, 1000, 2500, 5000]
+    wl = build_attention("rescale", 3500, torch.bfloat16, lens, decode_queries(lens), 32, 8, 128, 128,
+                         16, poison=True)
+    wl = _scale_rows(_quarter(wl, "v"), "k", _ramp)
+    plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages)
+    ws = pkv.Workspace.for_splits(wl.queries, 32, 128, splits)
+    t = wl.tensors
+    got = pkv.attention(plan, t["q"].cuda(), t["k"].cuda(), t["v"].cuda(), wl.scale, wl.causal, workspace=ws,
+                        window=1024)
+    torch.cuda.synchronize()
+    want = oracle.paged_attention(t["q"], t["k"], t["v"], wl.lens, wl.qseq, wl.qpos, wl.table,
+                                  wl.page_size, wl.scale, wl.causal, window=1024)[0]
+    assert_close(got.double().cpu().numpy(), want, torch.bfloat16, f"window ramp splits={splits}")
+
+
+def test_prefill_tiles_d64_moving_reference():
+    """The D=64 tile kernel (f16, three q heads per KV head) over ramped keys."""
+    chunks, dec = [(77, 300), (1000, 256)], [700]
+    lens = [p + c for p, c in chunks] + dec
+    queries = []
+    for s, (p, c) in enumerate(chunks):
+        queries += [(s, p + j) for j in range(c)]
+    queries += [(len(chunks) + j, L - 1) for j, L in enumerate(dec)]
+    wl = build_attention("rescale", 3600, torch.float16, lens, queries, 6, 2, 64, 64, 16, causal=True,
+                         poison=True)
+    wl = _scale_rows(_quarter(wl, "v"), "k", _ramp)
+    assert_close(run(wl), expected(wl), torch.float16, "prefill d=64 ramp")
