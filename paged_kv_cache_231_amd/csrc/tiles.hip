@@ -378,7 +378,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     // with tile kt's softmax arithmetic.  After the last tile the scores
     // read a ring stage whose contents are not used (in bounds).
     f32x4_t s_next[2][2];
-    __builtin_amdgcn_s_setprio(1);
     scores(kt + 1, s_next);
     // online softmax (base 2): each probability is exp2(score * scale_log2
     // - m) with one FMA, against the row's current reference m
@@ -436,7 +435,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
       }
     }
 
-    __builtin_amdgcn_s_setprio(0);
+    // The value product runs at a raised wave priority: the other wave of
+    // the SIMD (from another block) issues in its gaps, not the reverse.
+    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T . P^T over the 32 keys: K slots 8j .. 8j+3 are key rows
     // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16.  The reads of
     // block b + kPvAhead are issued before the MFMAs of block b and the
@@ -462,6 +463,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     }
     lacc[0] = M::qk(ones, pb[0], lacc[0]);
     lacc[1] = M::qk(ones, pb[1], lacc[1]);
+    __builtin_amdgcn_s_setprio(0);
     // refill the stage of tile kt-1 (every wave passed this iteration's
     // barrier, so none still reads it)
     if (kt + kStages - 1 < n_tiles) issue(kt + kStages - 1);
