@@ -211,8 +211,9 @@ uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads,
  * warm-up call, times each candidate with HIP events on `stream`, and
  * writes the fastest count to *splits (a count with more splits must be
  * more than 2% faster to win).  The balanced schedule is the last
- * candidate, reported as 0 (it too must be more than 2% faster than the
- * best count before it).  Uses temporary workspaces of its own;
+ * candidate, reported as 0; it wins when it measures faster than the best
+ * count before it (its workspace does not grow with the choice).  Uses
+ * temporary workspaces of its own;
  * `out` receives the attention result.  Synchronises the stream; not for
  * use under graph capture.  Errors: those of pkv_attention, PKV_EINVAL for
  * a null plan or splits, PKV_EHIP. */
