@@ -39,6 +39,12 @@ beside it.
                 legs (per-kernel HIP-event durations).
   decode_step   one captured graph of append + attention on the packed
                 decode workload: replay and eager times per step.
+  f32_decode, long_decode, mla
+                the f32 MHA decode (launch-bound), the long-context split
+                decode (4 x 131072) and the MLA decode workloads, each with
+                its tuned launch: dominant-kernel time (dispatch events),
+                merge time, whole-step time, HBM fraction, and for MLA the
+                MFMA fraction too.
   cpu_baseline  the float64 oracle timed on the host cores over a bounded
                 sample of the same workload, in GB/s.
 """
@@ -136,6 +142,7 @@ def cpu_baseline(wl, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
+    affinity = len(os.sched_getaffinity(0))
     t = wl.tensors
     done_bytes, nq = 0, 0
     order = np.argsort(wl.qseq, kind="stable")
@@ -159,8 +166,9 @@ def cpu_baseline(wl, budget_s: float):
         done_bytes += int(wl.visible()[i]) * row_bytes
         nq += 1
         elapsed = time.perf_counter() - start
-    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s",
+            "cores": int(min(threads, affinity)), "affinity_cores": int(affinity),
+            "blas_threads": int(threads), "kind": "oracle",
             "sample": f"{nq} single-query oracle calls cycling over the {wl.queries} queries "
                       f"(float64 numpy, {elapsed:.1f} s, {done_bytes / 1e9:.3f} GB of cache rows)"}
 
@@ -361,6 +369,78 @@ def decode_step_measure(torch, pkv, workloads, steps: int):
             "bytes_per_step": nbytes, "workload": f"{wl.name}, one new token per sequence"}
 
 
+def workload_leg(torch, pkv, workloads, n: int, steps: int):
+    """One more workload as its own leg: the tuned launch (split count or the
+    balanced schedule), the whole step timed with stream events, the
+    dominant kernel (decode rows, or MLA) with its own dispatch-recorded
+    events inside those steps, and the merge timed the same way after
+    them.  HBM fraction from the algorithmic bytes; MLA also reports its
+    FLOP rate against the MFMA peak."""
+    wl = workloads.config(n)
+    dev = {k: v.to("cuda") for k, v in wl.tensors.items()}
+    stream = torch.cuda.current_stream()
+    plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
+    if wl.kind == "attention":
+        hq, dv = wl.info["hq"], wl.info["dv"]
+        out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
+        splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
+        ws = pkv.Workspace.for_splits(wl.queries, hq, dv, splits)
+        main = "rows"
+
+        def step():
+            pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws,
+                          out=out)
+    else:
+        h, r = wl.info["h"], wl.info["r"]
+        out = torch.empty(wl.queries, h, r, dtype=wl.dtype, device="cuda")
+        splits = pkv.tune_splits_mla(plan, dev["q_abs"], dev["q_pos"], dev["latent"], dev["k_pos"],
+                                     wl.scale, wl.causal, out=out)
+        ws = pkv.Workspace.for_splits(wl.queries, h, r, splits)
+        main = "mla"
+
+        def step():
+            pkv.mla(plan, dev["q_abs"], dev["q_pos"], dev["latent"], dev["k_pos"], wl.scale,
+                    wl.causal, workspace=ws, out=out)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    plan.timing(True, kernels=(main,))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / steps * 1e3
+    n_m, ms_m = plan.timing_read(main)
+    plan.timing(True, kernels=("merge",))
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    n_g, ms_g = plan.timing_read("merge")
+    plan.timing(False)
+    kern_us = ms_m / max(1, n_m) * 1e3
+    nbytes = workloads.attention_bytes(wl)
+    gbs = nbytes / (kern_us * 1e-6) / 1e9
+    leg = {"value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+           "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "kernel": {"rows": "split-KV decode", "mla": "MLA decode"}[main],
+           "splits": "balanced" if splits == 0 else splits,
+           "avg_launch_us": round(kern_us, 2), "launches": n_m,
+           "merge_us": round(ms_g / n_g * 1e3, 2) if n_g else None,
+           "step_us": round(step_us, 2),
+           "step_gbs": round(nbytes / (step_us * 1e-6) / 1e9, 1),
+           "bytes_per_launch": nbytes, "workload": wl.name}
+    if main == "mla":
+        flops = workloads.attention_flops(wl)
+        tfs = flops / (kern_us * 1e-6) / 1e12
+        leg.update({"mfma_achieved_tflops": round(tfs, 1),
+                    "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                    "flops_per_launch": flops})
+    return leg
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -502,6 +582,10 @@ def main():
         line["window"] = window_measure(torch, pkv, workloads, args.prefill_steps)
         line["fp8"] = fp8_measure(torch, pkv, workloads, args.prefill_steps)
         line["decode_step"] = decode_step_measure(torch, pkv, workloads, args.prefill_steps)
+        # the other workloads, each as a leg of its own (never the one timed above)
+        for name, n in (("f32_decode", 1), ("long_decode", 3), ("mla", 5)):
+            if n != args.workload:
+                line[name] = workload_leg(torch, pkv, workloads, n, args.prefill_steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -131,8 +131,10 @@ pkv_status pkv_plan_create(const uint32_t *words, size_t n_words, void *stream,
  * ps, N, R, T) unchanged, so every launch grid and captured graph stays
  * valid; lengths, positions, rows, tiles and table entries may change.
  * `words` must stay unchanged until the copy has run (use pinned memory).
- * Errors: PKV_EINVAL (invalid words), PKV_ESHAPE (header changed),
- * PKV_EDEVICE (other stream/device), PKV_EHIP. */
+ * Not allowed while the plan's stream is being captured (a recorded copy
+ * would replay the capture-time words): rebind between replays.
+ * Errors: PKV_EINVAL (invalid words, stream under capture), PKV_ESHAPE
+ * (header changed), PKV_EDEVICE (other stream/device), PKV_EHIP. */
 pkv_status pkv_plan_rebind_async(pkv_plan *plan, const uint32_t *words,
                                  size_t n_words, void *stream);
 
@@ -140,7 +142,10 @@ pkv_status pkv_plan_rebind_async(pkv_plan *plan, const uint32_t *words,
  * the value travels inside the call, so no host buffer must outlive it
  * (boostr 0.1.0 `DeviceScalars::update` doc).  The plan with the new word
  * must validate (e.g. grow a length only after the table entry of a newly
- * used page is set).  Errors: PKV_EINVAL, PKV_EDEVICE, PKV_EHIP. */
+ * used page is set).  Not allowed while the plan's stream is being
+ * captured (a memset node would replay one value): set words between
+ * replays.  Errors: PKV_EINVAL (index, invalid plan, stream under capture),
+ * PKV_EDEVICE, PKV_EHIP. */
 pkv_status pkv_plan_set_word_async(pkv_plan *plan, size_t index, uint32_t value,
                                    void *stream);
 
@@ -211,8 +216,10 @@ uint32_t pkv_suggest_splits(const pkv_plan *plan, uint32_t q_heads,
  * warm-up call, times each candidate with HIP events on `stream`, and
  * writes the fastest count to *splits (a count with more splits must be
  * more than 2% faster to win).  The balanced schedule is the last
- * candidate, reported as 0; it wins when it measures faster than the best
- * count before it (its workspace does not grow with the choice).  Uses
+ * candidate, reported as 0; it is timed only when the call really runs the
+ * balanced kernels (a shape they do not take runs unsplit, which was timed
+ * already), and wins when it measures faster than the best count before it
+ * (its workspace does not grow with the choice).  Uses
  * temporary workspaces of its own;
  * `out` receives the attention result.  Synchronises the stream; not for
  * use under graph capture.  Errors: those of pkv_attention, PKV_EINVAL for

@@ -380,14 +380,14 @@ def append(plan: Plan, new_k, new_v, k, v, copy=False):
     the original unchanged.  Returns (k, v, report) with the caches written
     and the report as a dict."""
     if new_k.dim() != 3 or new_v.dim() != 3 or k.dim() != 4 or v.dim() != 4:
-        raise PKVError("EINVAL", "invalid cache append ranks")
+        raise PKVError("EINVAL", "append takes 3-D new rows and 4-D caches")
     copy_k, copy_v = (copy, copy) if isinstance(copy, bool) else (bool(copy[0]), bool(copy[1]))
     n, ps, hkv, d = k.shape
     dv = v.shape[3]
     if (n, ps) != (plan.pages, plan.page_size) or tuple(v.shape[:3]) != (n, ps, hkv) \
             or tuple(new_k.shape) != (plan.queries, hkv, d) \
             or tuple(new_v.shape) != (plan.queries, hkv, dv):
-        raise PKVError("ESHAPE", "incompatible cache append shapes")
+        raise PKVError("ESHAPE", "new rows and caches do not match the plan or each other")
     code = _dtype_code(new_k, new_v, k, v)
     kc = torch.empty_like(k) if copy_k and plan.queries else None
     vc = torch.empty_like(v) if copy_v and plan.queries else None

@@ -98,13 +98,19 @@ pkv_status check_workspace(const pkv_workspace *ws, const pkv_plan *plan, uint32
   if (!ws) return PKV_OK;
   if (ws->queries != plan->L.Q || ws->heads != heads || ws->dv != dv || ws->stream != stream ||
       ws->device != plan->device)
-    return fail(PKV_EWORKSPACE, "split workspace shape/device/stream mismatch");
+    return fail(PKV_EWORKSPACE, "workspace was made for other queries, heads, value dim, device or stream");
   return PKV_OK;
 }
 
 pkv_status hip_fail(hipError_t e) {
   if (e == hipSuccess) return PKV_OK;
   return fail(PKV_EHIP, "kernel launch failed");
+}
+
+// True while `st` is being captured into a graph (or when the query fails).
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
 }
 
 hipEvent_t take_event(const pkv_plan *plan) {
@@ -132,8 +138,7 @@ class Timed {
  public:
   Timed(const pkv_plan *plan, pkv_kernel kernel, hipStream_t st) : plan_(plan) {
     if (!(plan_->timing >> uint32_t(kernel) & 1u)) return;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+    if (capturing(st)) return;
     rec_.kernel = int(kernel);
     rec_.start = take_event(plan_);
     rec_.stop = take_event(plan_);
@@ -231,12 +236,17 @@ MergeArgs balanced_merge_args(const RowArgs &ra) {
   return ma;
 }
 
+// Set by run_rows when a call took the balanced schedule (the tuner times
+// the balanced candidate only when it really runs).
+thread_local bool t_ran_balanced = false;
+
 // Launches the row kernel (and the merge when split) over `qlist`.
 pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_workspace *ws,
                     hipStream_t st) {
   hipError_t e;
   ra.bal_waves = balanced_waves(ra, dt, ws);
   if (ra.bal_waves) {
+    t_ran_balanced = true;
     {
       Timed t(plan, PKV_KERNEL_ROWS, st);
       e = launch_rows_balanced(ra, dt, st);
@@ -247,6 +257,7 @@ pkv_status run_rows(const pkv_plan *plan, RowArgs ra, pkv_dtype dt, const pkv_wo
   }
   ra.bal_waves = mla_balanced(ra, dt, ws);
   if (ra.bal_waves) {
+    t_ran_balanced = true;
     {
       Timed t(plan, PKV_KERNEL_MLA, st);
       e = launch_mla_balanced(ra, dt, st);
@@ -363,6 +374,9 @@ pkv_status pkv_plan_rebind_async(pkv_plan *plan, const uint32_t *words, size_t n
   if (!plan) return fail(PKV_EINVAL, "null plan");
   pkv_status st = check_binding(plan, static_cast<hipStream_t>(stream));
   if (st != PKV_OK) return st;
+  // a copy recorded into a graph would replay the words of capture time
+  // while the host copy moved on; rebinding happens between replays
+  if (capturing(plan->stream)) return fail(PKV_EINVAL, "plan words cannot change while the stream is captured");
   PlanLayout L;
   st = validate_plan(words, n_words, &L);
   if (st != PKV_OK) return st;
@@ -382,6 +396,9 @@ pkv_status pkv_plan_set_word_async(pkv_plan *plan, size_t index, uint32_t value,
   if (st != PKV_OK) return st;
   if (index < PKV_PLAN_HEADER_WORDS || index >= plan->host.size())
     return fail(PKV_EINVAL, "word index outside the plan body");
+  // a memset node in a graph would replay one value forever; set words
+  // between replays
+  if (capturing(plan->stream)) return fail(PKV_EINVAL, "plan words cannot change while the stream is captured");
   const uint32_t old = plan->host[index];
   plan->host[index] = value;
   st = validate_plan(plan->host.data(), plan->host.size(), nullptr);
@@ -764,6 +781,7 @@ pkv_status pkv_attention_fp8(const pkv_plan *plan, pkv_dtype dtype, const void *
                         causal, window, ws, stream);
 }
 
+
 pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k, const void *new_v,
                       void *k, void *v, void *k_copy, void *v_copy, uint32_t hkv, uint32_t d,
                       uint32_t dv, pkv_append_report *report, void *stream_) {
@@ -774,7 +792,7 @@ pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k, 
   if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
     return fail(PKV_EINVAL, "paged operands must be F32, F16 or BF16");
   if (hkv == 0 || d == 0 || dv == 0 || d > 1024 || dv > 1024)
-    return fail(PKV_ESHAPE, "incompatible cache append shapes");
+    return fail(PKV_ESHAPE, "append needs nonzero head counts and head dims of at most 1024");
   const PlanLayout &L = plan->L;
   if (!u32_elems({L.Q, hkv, d}) || !u32_elems({L.Q, hkv, dv}) || !u32_elems({L.N, L.ps, hkv, d}) ||
       !u32_elems({L.N, L.ps, hkv, dv}))
@@ -949,9 +967,13 @@ pkv_status tune_splits(const pkv_plan *plan, uint32_t heads, uint32_t dv, uint32
   if (st == PKV_OK && try_balanced)
     st = pkv_workspace_create_balanced(L.Q, heads, dv, stream, &bw);
   if (st == PKV_OK && bw) {
+    t_ran_balanced = false;
     st = call(bw);
+    // a call the balanced schedule does not take runs unsplit with this
+    // workspace: that candidate was timed already
+    const bool applies = t_ran_balanced;
     float ms = 0.f;
-    if (st == PKV_OK) {
+    if (st == PKV_OK && applies) {
       if (hipEventRecord(e0, stream) != hipSuccess) st = fail(PKV_EHIP, "hipEventRecord failed");
       for (uint32_t r = 0; r < reps && st == PKV_OK; ++r) st = call(bw);
       if (st == PKV_OK && (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
@@ -960,7 +982,7 @@ pkv_status tune_splits(const pkv_plan *plan, uint32_t heads, uint32_t dv, uint32
     }
     // no margin here: the balanced workspace does not grow with the choice,
     // so it wins whenever it measures faster
-    if (st == PKV_OK && ms < best_ms) {
+    if (st == PKV_OK && applies && ms < best_ms) {
       best_ms = ms;
       *best_out = 0;
     }
