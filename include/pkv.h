@@ -298,6 +298,35 @@ pkv_status pkv_attention_fp8(const pkv_plan *plan, pkv_dtype dtype,
                              float k_scale, float v_scale, int causal,
                              uint32_t window, pkv_workspace *ws, void *stream);
 
+/* ------------------------------------------------------------- no-alloc
+ * For callers that cannot allocate device memory at call time (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pkv_attention with a balanced workspace, except that the workspace is a
+ * static device array of PKV_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU, held until the process ends.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the caller still owns
+ * q, k, v and out, laid out as for pkv_attention.  Resolving the array's
+ * address happens on the first call on a device (hipGetSymbolAddress).
+ * The array holds the balanced schedule's slot rows (2 x 16 rows of
+ * value_dim + 1 f32 per wave) after the per-query records ((2 Q + 1) u32);
+ * the wave count is capped by what fits (1024 waves at value_dim 128 on 256
+ * CUs, the same launch as a balanced workspace).  Nothing in it needs to
+ * start at zero; every call on one GPU shares that GPU's array and keeps
+ * the last call's contents, so calls that overlap on one GPU (two streams,
+ * two threads) race.  Shapes the balanced kernels do not take run unsplit,
+ * using no scratch.
+ * Errors: as pkv_attention; PKV_ERANGE when the queries' records and four
+ * waves' slots exceed the array, or when fewer waves fit than one group of
+ * the call (KV heads x ceil(G / 16)); PKV_EHIP when the array's address
+ * cannot be resolved. */
+#define PKV_NOALLOC_SCRATCH_BYTES (32ull << 20)
+
+pkv_status pkv_attention_noalloc(const pkv_plan *plan, pkv_dtype dtype,
+                                 const void *q, const void *k, const void *v,
+                                 void *out, uint32_t q_heads, uint32_t kv_heads,
+                                 uint32_t head_dim, uint32_t value_dim,
+                                 float scale, int causal, void *stream);
+
 /* MLA (`DevicePlan::mla` doc): one shared latent head is both key and value;
  * a position part only adds to the score:
  *   x_t = scale * (<q_abs[i,h,:], latent_t> + <q_pos[i,h,:], k_pos_t>)

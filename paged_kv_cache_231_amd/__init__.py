@@ -27,7 +27,7 @@ import torch
 
 from ._lib import LIB_PATH, AppendReport, PKVError, STATUS, check, lib  # noqa: F401
 
-__all__ = ["Plan", "Workspace", "attention", "attention_fp8", "mla", "append", "encode_plan", "validate_plan",
+__all__ = ["Plan", "Workspace", "attention", "attention_noalloc", "attention_fp8", "mla", "append", "encode_plan", "validate_plan",
            "validate_writes", "suggest_splits", "PKVError", "LIB_PATH", "lib", "HEADER_WORDS",
            "MAX_SPLITS"]
 
@@ -312,6 +312,30 @@ def attention(plan: Plan, q, k, v, scale: float, causal: bool = True, workspace=
         check(lib().pkv_attention(plan.handle, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   out.data_ptr(), hq, hkv, d, dv, float(scale),
                                   int(bool(causal)), ws, ctypes.c_void_p(plan.stream)))
+    return out
+
+
+def attention_noalloc(plan: Plan, q, k, v, scale: float, causal: bool = True, out=None):
+    """pkv_attention_noalloc: the balanced schedule with the library's static
+    per-GPU scratch array as its workspace (no device allocation in the
+    call; ``out`` must be given for that).  Calls that overlap on one GPU
+    race on the array."""
+    if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise PKVError("EINVAL", "q must be 3-D and the caches 4-D")
+    qn, hq, d = q.shape
+    n, ps, hkv, dk = k.shape
+    dv = v.shape[3]
+    if qn != plan.queries or n != plan.pages or ps != plan.page_size or dk != d \
+            or tuple(v.shape[:3]) != (n, ps, hkv):
+        raise PKVError("ESHAPE", "head counts, head dims or tensor shapes do not fit together")
+    if out is None:
+        out = torch.empty((qn, hq, dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (qn, hq, dv):
+        raise PKVError("ESHAPE", "head counts, head dims or tensor shapes do not fit together")
+    code = _dtype_code(q, k, v, out)
+    check(lib().pkv_attention_noalloc(plan.handle, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      out.data_ptr(), hq, hkv, d, dv, float(scale),
+                                      int(bool(causal)), ctypes.c_void_p(plan.stream)))
     return out
 
 

@@ -53,6 +53,7 @@ SIGNATURES = {
     "pkv_attention": (_i, [_p, _i, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _f, _i, _p, _p]),
     "pkv_attention_window": (_i, [_p, _i, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _f, _i, _u32,
                                   _p, _p]),
+    "pkv_attention_noalloc": (_i, [_p, _i, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _f, _i, _p]),
     "pkv_attention_fp8": (_i, [_p, _i, _p, _p, _p, _p, _u32, _u32, _u32, _u32, _f, _f, _f, _i,
                                _u32, _p, _p]),
     "pkv_mla": (_i, [_p, _i, _p, _p, _p, _p, _p, _u32, _u32, _u32, _f, _i, _p, _p]),

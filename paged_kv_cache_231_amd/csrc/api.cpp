@@ -12,6 +12,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -781,6 +782,93 @@ pkv_status pkv_attention_fp8(const pkv_plan *plan, pkv_dtype dtype, const void *
                         causal, window, ws, stream);
 }
 
+}  // extern "C"
+
+// Workspace of pkv_attention_noalloc: one array per GPU, in the library's
+// device code object (the loader places it; nothing is allocated at call
+// time).  Its name is only a host-side stand-in for the device array: host
+// code uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace pkv {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char *g_scratch[kMaxDevices] = {};
+int g_scratch_cus[kMaxDevices] = {};
+
+// Device address of this device's scratch array and its CU count, resolved
+// once per device with that device current; null on failure.
+unsigned char *scratch_of(int dev, int *cus) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    int n = 0;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return nullptr;
+    g_scratch[dev] = static_cast<unsigned char *>(p);
+    g_scratch_cus[dev] = n;
+  }
+  *cus = g_scratch_cus[dev];
+  return g_scratch[dev];
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" {
+
+pkv_status pkv_attention_noalloc(const pkv_plan *plan, pkv_dtype dtype, const void *q,
+                                 const void *k, const void *v, void *out, uint32_t hq,
+                                 uint32_t hkv, uint32_t d, uint32_t dv, float scale, int causal,
+                                 void *stream) {
+  clear_error();
+  if (!plan) return fail(PKV_EINVAL, "null plan");
+  if (hq == 0 || hkv == 0 || hq % hkv != 0 || d == 0 || dv == 0 || d > 1024 || dv > 1024)
+    return fail(PKV_ESHAPE, "head counts, head dims or tensor shapes do not fit together");
+  pkv_status st = check_binding(plan, static_cast<hipStream_t>(stream));
+  if (st != PKV_OK) return st;
+  int cus = 0;
+  unsigned char *base = scratch_of(plan->device, &cus);
+  if (!base) return fail(PKV_EHIP, "resolving the static scratch array failed");
+  // layout as a balanced workspace: slot rows of dv f32, their lse, then
+  // {first tile, tiles} per query and the total
+  const uint64_t rec_bytes = (2ull * plan->L.Q + 1) * 4;
+  const uint64_t row_bytes = (uint64_t(dv) + 1) * sizeof(float);
+  const uint64_t wave_bytes = 2ull * 16 * row_bytes;  // two 16-head slots per wave
+  if (rec_bytes + 4 * wave_bytes > PKV_NOALLOC_SCRATCH_BYTES)
+    return fail(PKV_ERANGE, "too many queries or too large a value dim for the static scratch");
+  uint64_t waves = (PKV_NOALLOC_SCRATCH_BYTES - rec_bytes) / wave_bytes;
+  uint32_t per_cu = 0;
+  for (pkv_dtype dt : {PKV_F16, PKV_BF16})
+    for (uint32_t ps : {16u, 3u})
+      per_cu = std::max<uint32_t>(per_cu, uint32_t(bal_waves_per_cu(dv, ps, dt)));
+  per_cu = std::min(per_cu, kBalancedWavesPerCu);
+  waves = std::min<uint64_t>(waves, uint64_t(std::max(per_cu, 1u)) * uint32_t(cus));
+  waves -= waves % 4;
+  const uint64_t segq = uint64_t(hkv) * ((hq / hkv + 15) / 16);
+  if (per_cu && segq > waves)
+    return fail(PKV_ERANGE, "the static scratch holds fewer waves than one group of this call");
+  pkv_workspace ws;  // a view of the scratch array; owns nothing
+  ws.device = plan->device;
+  ws.stream = static_cast<hipStream_t>(stream);
+  ws.queries = plan->L.Q;
+  ws.heads = hq;
+  ws.dv = dv;
+  ws.splits = 0;
+  ws.max_waves = uint32_t(waves);
+  ws.cus = uint32_t(cus);
+  ws.slot_rows = 2 * waves * 16;
+  ws.buf = reinterpret_cast<float *>(base);
+  ws.bytes = size_t(ws.slot_rows * row_bytes + rec_bytes);
+  ws.slot_lse = ws.buf + ws.slot_rows * dv;
+  ws.rec = reinterpret_cast<uint32_t *>(ws.slot_lse + ws.slot_rows);
+  return attention_impl(plan, dtype, false, q, k, v, out, hq, hkv, d, dv, scale, 1.f, 1.f, causal,
+                        0u, &ws, stream);
+}
 
 pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k, const void *new_v,
                       void *k, void *v, void *k_copy, void *v_copy, uint32_t hkv, uint32_t d,
