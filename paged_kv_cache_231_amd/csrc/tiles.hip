@@ -10,17 +10,21 @@
 //
 // A block owns 128 q-rows (a q-row is one (query, q head) pair; with G q
 // heads per KV head that is 128/G queries x G heads) of one tile and one KV
-// head; each of its four waves owns 32 q-rows as two MFMA N-tiles.  Keys are
-// walked in tiles of 32 rows.  K and V rows travel HBM -> LDS directly
-// (gfx950 global_load_lds, no registers on the way) into a ring of four
-// stages, three tiles ahead of the tile being computed, so the load latency
-// hides behind the MFMA work.  Each wave computes S^T = K . Q^T (tokens on
-// the M side), applies the absolute-position mask and an online softmax in
-// base 2, and accumulates O^T += V^T . P^T, with V^T read by transposed LDS
-// loads.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled by
-// row, which keeps both read patterns at most two-way banked.  The block
-// table of the sequence is cached in LDS.  Blocks that share a (tile, KV
-// head) are numbered so they land on one XCD and share its L2.
+// head; each of its four waves owns 32 q-rows, the N side of 32x32x16 MFMAs.
+// Keys are walked in tiles of 32 rows.  K and V rows travel HBM -> LDS
+// directly (gfx950 global_load_lds, no registers on the way) into a ring of
+// four stages, three tiles ahead of the tile being computed.  Each wave
+// computes S^T = K . Q^T (keys on the M side, so a lane holds 16 keys of one
+// q-row), applies the absolute-position mask and an online softmax in base
+// 2, and accumulates O^T += V^T . P^T with V^T from transposed LDS reads.
+// The M rows of the score product are a fixed permutation of the tile's key
+// rows, chosen so that a lane's 16 probabilities are, in order, its own
+// K-slots of the value product: P never moves between lanes.  Rows are
+// stored unpadded with their 16-byte chunks XOR-swizzled by row, which
+// keeps the score reads and the transposed value reads free of bank
+// conflicts.  The block table of the sequence is cached in LDS.  Blocks that
+// share a (tile, KV head) are numbered so they land on one XCD and share its
+// L2.
 
 #include "mfma_common.h"
 
@@ -33,7 +37,47 @@ constexpr int kRowsPerBlock = 128; // q-rows per block (32 per wave)
 constexpr int kTT = 32;            // key rows per tile
 constexpr int kStages = 4;         // LDS ring stages (3 tiles in flight)
 constexpr int kTableCache = 1024;  // block-table entries cached in LDS
-constexpr float kSlack = 8.0f;     // lazy-rescale threshold (log2 units)
+// A lane whose 16 probabilities of a tile sum above this (each is then at
+// most this) makes the wave move its softmax references to the row maxima.
+constexpr float kSumLimit = 256.f;
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+template <class DT>
+struct Mfma32;
+
+template <>
+struct Mfma32<BF16> {
+  // C(32 x 32) += A(32 x 16) . B(16 x 32), 8 elements per lane
+  static __device__ __forceinline__ f32x16_t mma(const uint4 &a, const uint4 &b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // c + both halves of a packed pair
+  static __device__ __forceinline__ float add_pair(uint32_t p, float c) {
+    const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p), one, c, false);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return BF16::pack2(lo, hi); }
+};
+
+template <>
+struct Mfma32<F16> {
+  static __device__ __forceinline__ f32x16_t mma(const uint4 &a, const uint4 &b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float add_pair(uint32_t p, float c) {
+    const f16x2_t one = {(_Float16)1.f, (_Float16)1.f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p), one, c, false);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const _Float16 a = _Float16(lo), b = _Float16(hi);
+    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+  }
+};
 
 template <int D>
 struct PLds {
@@ -44,12 +88,27 @@ struct PLds {
   static constexpr int kBytes = kStages * kStage;
   static constexpr int RPW = 1024 / kRowB;         // rows per wave load (64 lanes x 16 B)
   static constexpr int NI = kTT / (RPW * kPW);     // loads per wave per tensor per tile
-  // chunk c of row r sits in slot c ^ swz(r): rows sharing a 256-byte bank
-  // line get different XOR keys
+  // chunk c of row r sits in slot c ^ swz(r)
   static __device__ __forceinline__ uint32_t swz(uint32_t r) {
-    return D == 64 ? (r >> 1) & 7u : r & 15u;
+    return D == 64 ? (r >> 1) & 7u : ((r >> 1) & 7u) | ((r & 1u) << 3);
   }
 };
+
+// Key row (0..31 in the tile) behind M row m of the score product.  A lane
+// of the 32x32 result holds M rows 8i + 4h + e (i, e = 0..3, h = lane / 32);
+// the value product's K-slots of lane half h at step t are its results
+// i = 2t, 2t + 1 in order, so K-slot u of step t is M row 16t + 8(u >> 2) +
+// 4h + (u & 3).  This permutation makes the four rows one transposed read
+// fetches, and the rows 16 lanes read for the score product, fall in
+// distinct LDS banks under the swizzle above.
+__device__ __forceinline__ uint32_t key_of_mrow(uint32_t m) {
+  return (m & 1u) | ((m >> 1) & 1u) << 3 | ((m >> 2) & 1u) << 1 | ((m >> 3) & 1u) << 2 |
+         ((m >> 4) & 1u) << 4;
+}
+// The same for result element 4i + e of lane half 0 (half 1 adds 2).
+__host__ __device__ constexpr int key_of_elem(int i, int e) {
+  return (e & 1) + 8 * (e >> 1) + 4 * (i & 1) + 16 * (i >> 1);
+}
 
 // Float max without IEEE canonicalisation of the inputs (fmaxf quiets both
 // operands first): the running max is only a reference point, and a NaN
@@ -64,12 +123,16 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
-// max over the four 16-lane rows (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float rows4_vmax(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+// Sum and max of the values of lanes l and l ^ 32 (the swap leaves lane l
+// with one of the two in each result, so only symmetric combinations of
+// both results are the same in every lane).
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 
 // Compiler-level memory barriers around the raw hardware barrier: LDS loads
@@ -89,6 +152,12 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base) : "memory");
 }
 
+// The same with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) const char *)(p)));
@@ -105,13 +174,19 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+
 template <class DT, int D>
-__global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub,
-                                                      uint32_t n_groups) {
-  using M = Mfma<DT>;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
+    TileArgs a, uint32_t n_sub, uint32_t n_groups) {
+  using M = Mfma32<DT>;
   using L = PLds<D>;
   using T = typename DT::T;
-  constexpr int KS = D / 32, DB = D / 16;
+  constexpr int KS = D / 16;  // k-steps of the score product (8 values per lane half)
+  constexpr int MB = D / 32;  // 32-row blocks of value dims
   constexpr int kLoadsPerTile = 2 * L::NI;  // per thread: K and V
   __shared__ __align__(1024) unsigned char lds[L::kBytes];
   __shared__ uint32_t tcache[kTableCache];
@@ -131,7 +206,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t c16 = lane & 15u, j = lane >> 4;
+  const uint32_t c32 = lane & 31u, hf = lane >> 5;
   const PlanView &pv = a.plan;
   const uint32_t first = a.tiles[2 * tile], count = a.tiles[2 * tile + 1];
   const uint32_t grp = a.hq / a.hkv;
@@ -161,56 +236,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
     tcache[e] = (pg < pv.N ? pg : 0u) * page_elems;  // never read outside the pool
   }
 
-  // this wave's q-rows: N-tile nt, column c16 -> q-row 32*wv + 16*nt + c16
-  uint4 qb[2][KS];
-  uint32_t pos[2];
-  bool row_ok[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const uint32_t r = 32u * wv + 16u * nt + c16;
-    const uint32_t qq = r / grp, h = r % grp;
-    row_ok[nt] = r < qb_n * grp && q_lo + qq < q_hi;
-    pos[nt] = p0 + q_lo + qq;
+  // This lane's q-row (column c32 of the wave's N block) and its half of
+  // the head dims: K-slots of lane half hf at k-step ks are dims
+  // (D/2) hf + 8 ks .. +7, for the query operand and the key rows alike.
+  const uint32_t r = 32u * wv + c32;
+  const uint32_t qq = r / grp, hh = r % grp;
+  const bool row_ok = r < qb_n * grp && q_lo + qq < q_hi;
+  const uint32_t pos = p0 + q_lo + qq;
+  uint4 qb[KS];
+  {
     const T *qrow = static_cast<const T *>(a.q) +
-                    (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + h) * D;
+                    (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D + (D / 2) * hf;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qb[nt][ks] = row_ok[nt] ? *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j))
-                              : make_uint4(0, 0, 0, 0);
+      qb[ks] = row_ok ? *reinterpret_cast<const uint4 *>(qrow + 8 * ks) : make_uint4(0, 0, 0, 0);
   }
   // smallest position among the block's queries: key tiles wholly at or
   // below it need no causal mask
   const uint32_t pos_min = p0 + q_lo;
-  // last visible key of each q-row: position (causal) or the last key
-  uint32_t lim[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) lim[nt] = a.causal && pos[nt] < k_end - 1u ? pos[nt] : k_end - 1u;
+  // last visible key of the q-row: its position (causal) or the last key
+  const uint32_t lim = a.causal && pos < k_end - 1u ? pos : k_end - 1u;
 
-  f32x4_t o[2][DB];
+  f32x16_t o[MB];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int b = 0; b < MB; ++b)
 #pragma unroll
-    for (int b = 0; b < DB; ++b) o[nt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kNoMax, kNoMax};
-  // a row's reference moves only when a raw score passes (m + kSlack) /
-  // scale_log2; kNoMax makes the first visible score do so
-  float thr[2] = {kNoMax, kNoMax};
-  // Softmax denominators on the matrix core: one more 16-row output block
-  // per N-tile whose A operand is all ones, so each of its rows accumulates
-  // the sum of P over the keys for the lane's q-row (rescaled with O).
-  f32x4_t lacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  uint4 ones;
-  ones.x = ones.y = ones.z = ones.w = M::pack2(1.f, 1.f);
+    for (int x = 0; x < 16; ++x) o[b][x] = 0.f;
+  float m = kNoMax;  // the row's softmax reference (base 2, scaled)
+  float lsum = 0.f;  // this lane's share of the row's denominator
   const float sl2 = a.scale_log2;
-  const float inv_sl2 = 1.f / sl2;
   const T *kbase = static_cast<const T *>(a.k) + uint64_t(kvh) * D;
   const T *vbase = static_cast<const T *>(a.v) + uint64_t(kvh) * D;
   __syncthreads();  // table cache ready (Q loads may still be in flight: fine)
 
-  // DMA of key tile kt into its ring stage: wave wv, load n covers rows
-  // RPW*(NI*wv + n) .. +RPW-1; lane -> row r0 + lane / CPR, slot lane % CPR,
-  // which holds chunk slot ^ swz(row) of the cache row.  Rows past the end
-  // read row 0 of page 0 (inside the pool) and are zeroed before use.
   // Per-lane parts of the DMA addresses: load n of a wave covers rows
   // r0(n) .. r0(n)+RPW-1, lane -> row r0(n) + lane / CPR and slot lane % CPR,
   // which holds chunk slot ^ swz(row) of the cache row.  For a power-of-two
@@ -221,275 +279,307 @@ __global__ __launch_bounds__(256) void prefill_kernel(TileArgs a, uint32_t n_sub
   uint32_t lane_off[L::NI];
 #pragma unroll
   for (int n = 0; n < L::NI; ++n) {
-    const uint32_t r = L::RPW * (L::NI * wv + n) + lane / L::CPR;
-    const uint32_t chunk = (lane % L::CPR) ^ L::swz(r);
-    lane_off[n] = (pow2 ? (r & (ps - 1u)) * tok_elems : 0u) + 8u * chunk;
+    const uint32_t rr = L::RPW * (L::NI * wv + n) + lane / L::CPR;
+    const uint32_t chunk = (lane % L::CPR) ^ L::swz(rr);
+    lane_off[n] = (pow2 ? (rr & (ps - 1u)) * tok_elems : 0u) + 8u * chunk;
   }
-  // DMA of key tile kt into its ring stage.  Rows past the end read row 0 of
-  // page 0 (inside the pool) and are zeroed before use.
-  auto issue = [&](uint32_t kt) {
-    unsigned char *stage = lds + (kt % kStages) * L::kStage;
+  // DMA of key tile kt into its ring stage, in two parts: `lookup` finds
+  // the element offset of each lane's cache row (block-table entries from
+  // the LDS cache, read one pipeline step before the loads are issued, so
+  // their latency hides behind that step), `issue` starts the loads.  Rows
+  // past the end read the sequence's token 0, which every query sees: its
+  // key's scores are masked out there and its probability is 0, so the
+  // product adds 0 x that value row, as it must (a value that is not finite
+  // there makes every output non-finite anyway).
+  auto lookup = [&](uint32_t kt, uint32_t (&off)[L::NI]) {
     const uint32_t tok0 = kt * kTT;
     const uint32_t tile_off = pow2 ? (tok0 & (ps - 1u)) * tok_elems : 0u;
 #pragma unroll
     for (int n = 0; n < L::NI; ++n) {
-      const uint32_t r0 = L::RPW * (L::NI * wv + n);
-      const uint32_t r = r0 + lane / L::CPR;
-      const uint32_t tok = tok0 + r;
+      const uint32_t rr = L::RPW * (L::NI * wv + n) + lane / L::CPR;
+      const uint32_t tok = tok0 + rr;
       const bool ok = tok < k_end;
-      uint32_t off;
       if (pow2) {
         const uint32_t lp = ok ? tok >> ps_shift : 0u;  // entry 0 exists whenever a tile does
         const uint32_t pbase = lp < uint32_t(kTableCache)
                                    ? tcache[lp]
                                    : (table[lp] < pv.N ? table[lp] : 0u) * page_elems;
-        off = ok ? pbase + tile_off + lane_off[n] : lane_off[n] - (r & (ps - 1u)) * tok_elems;
+        off[n] = ok ? pbase + tile_off + lane_off[n] : pbase + lane_off[n] - (rr & (ps - 1u)) * tok_elems;
       } else {
         const uint32_t lp = ok ? tok / ps : 0u;
         const uint32_t slot = ok ? tok - lp * ps : 0u;
-        const uint32_t pbase = !ok ? 0u
-                               : lp < uint32_t(kTableCache)
+        const uint32_t pbase = lp < uint32_t(kTableCache)
                                    ? tcache[lp]
                                    : (table[lp] < pv.N ? table[lp] : 0u) * page_elems;
-        off = pbase + slot * tok_elems + lane_off[n];
+        off[n] = pbase + slot * tok_elems + lane_off[n];
       }
+    }
+  };
+  // Fast path (power-of-two pages of at least 8 tokens, tiles wholly before
+  // the end): the 8 rows a wave loads of a tile are consecutive tokens of
+  // one page, so their address is one uniform base (a scalar table read,
+  // issued one pipeline step before the loads) plus a per-lane offset fixed
+  // for the whole kernel.
+  const bool fast_dma = pow2 && ps >= 8u;
+  constexpr uint32_t kWaveRows = uint32_t(L::RPW * L::NI);  // rows per wave per tile
+  uint32_t vo[L::NI];
+#pragma unroll
+  for (int n = 0; n < L::NI; ++n) {
+    const uint32_t rr = L::RPW * (L::NI * wv + n) + lane / L::CPR;
+    const uint32_t chunk = (lane % L::CPR) ^ L::swz(rr);
+    vo[n] = ((rr - kWaveRows * wv) * tok_elems + 8u * chunk) * uint32_t(sizeof(T));
+  }
+  // (the plan words do not change while a kernel runs: read through the
+  // constant address space, the entry is a scalar load)
+  const __attribute__((address_space(4))) uint32_t *ctable =
+      (const __attribute__((address_space(4))) uint32_t *)table;
+  auto wave_base = [&](uint32_t kt) -> uint32_t {
+    const uint32_t tw = __builtin_amdgcn_readfirstlane(kt * kTT + kWaveRows * wv);
+    const uint32_t pg = ctable[tw >> ps_shift];
+    return (pg < pv.N ? pg : 0u) * page_elems + (tw & (ps - 1u)) * tok_elems;
+  };
+  auto issue_fast = [&](uint32_t kt, uint32_t wb) {
+    unsigned char *stage = lds + (kt % kStages) * L::kStage;
+    const T *kb = kbase + wb, *vb = vbase + wb;
+#pragma unroll
+    for (int n = 0; n < L::NI; ++n) {
+      const uint32_t r0 = L::RPW * (L::NI * wv + n);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + r0 * L::kRowB));
-      dma16(kbase + off, dst);
-      dma16(vbase + off, dst + uint32_t(L::kTile));
+      dma16s(vo[n], kb, dst);
+      dma16s(vo[n], vb, dst + uint32_t(L::kTile));
+    }
+  };
+  auto fast_tile = [&](uint32_t kt) { return fast_dma && (kt + 1) * kTT <= k_end; };
+
+  auto issue = [&](uint32_t kt, const uint32_t (&off)[L::NI]) {
+    unsigned char *stage = lds + (kt % kStages) * L::kStage;
+#pragma unroll
+    for (int n = 0; n < L::NI; ++n) {
+      const uint32_t r0 = L::RPW * (L::NI * wv + n);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + r0 * L::kRowB));
+      dma16(kbase + off[n], dst);
+      dma16(vbase + off[n], dst + uint32_t(L::kTile));
     }
   };
 
-  // Transposed value reads: lane (j, c16) supplies key row pv_row(j,
-  // c16 >> 2) (+16 for the second read), value dims 16b + 4 (c16 & 3) .. +3.
-  // pv_row(j, e) = 4 (j & 1) + (j >> 1) + 2 (e & 1) + 8 (e >> 1) puts rows
-  // 0,2,..,14 on lanes 0..31 and the odd rows on lanes 32..63, so the eight
-  // rows one LDS cycle serves land in distinct 32-byte slot pairs.
-  uint32_t pv_off[DB];
+  // LDS byte offsets (within a stage) of this lane's operand reads.
+  // Score product, k-step ks: key row key_of_mrow(c32), chunk (CPR/2) hf + ks.
+  uint32_t k_off[KS];
   {
-    const uint32_t e4 = c16 >> 2, q4 = c16 & 3u;
-    const uint32_t pr = 4u * (j & 1u) + (j >> 1) + 2u * (e4 & 1u) + 8u * (e4 >> 1);
+    const uint32_t kr = key_of_mrow(c32);
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
-      pv_off[b] = pr * L::kRowB + 8u * (q4 & 1u) + 16u * ((2u * b + (q4 >> 1)) ^ L::swz(pr));
+    for (int ks = 0; ks < KS; ++ks)
+      k_off[ks] = kr * L::kRowB + 16u * ((uint32_t(L::CPR / 2) * hf + ks) ^ L::swz(kr));
+  }
+  // Value product, value block mb, step t, read rr (K-slots 4rr .. 4rr+3):
+  // in each 16-lane group, lane 4e + q addresses key row
+  // key_of_mrow(16t + 8rr + 4hf + e) and value dims 32mb + 16g + 4q .. +3
+  // (g = lane / 16 mod 2); the transposed read hands lane i of the group
+  // value dim 32mb + 16g + i of those four rows.  Step t only adds 16 rows.
+  uint32_t v_off[MB][2];
+  {
+    const uint32_t g = (lane >> 4) & 1u, e = (lane >> 2) & 3u, q4 = lane & 3u;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const uint32_t kr = key_of_mrow(8u * rr + 4u * hf + e);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint32_t dv = 32u * mb + 16u * g + 4u * q4;
+        v_off[mb][rr] = uint32_t(L::kTile) + kr * L::kRowB + 16u * ((dv / 8u) ^ L::swz(kr)) + 2u * (dv % 8u);
+      }
+    }
   }
 
   const uint32_t n_tiles = (k_end + kTT - 1) / kTT;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) settle(qb[nt][ks]);
-  for (uint32_t kt = 0; kt < n_tiles && kt < uint32_t(kStages - 1); ++kt) issue(kt);
+  for (int ks = 0; ks < KS; ++ks) settle(qb[ks]);
+  for (uint32_t kt = 0; kt < n_tiles && kt < uint32_t(kStages - 1); ++kt) {
+    if (fast_tile(kt)) {
+      issue_fast(kt, wave_base(kt));
+    } else {
+      uint32_t off[L::NI];
+      lookup(kt, off);
+      issue(kt, off);
+    }
+  }
 
   // Tile kt's ring stage is complete and visible to every wave once each
   // thread has seen its own loads of kt land and the block has passed a
   // barrier (which also means every wave finished reading the stage the next
   // refill overwrites).  `later` = tiles issued after kt that may still be
   // in flight.
-  auto ready = [&](uint32_t kt, uint32_t later) {
+  auto ready = [&](uint32_t later) {
     if (later >= 2) wait_vm<2 * kLoadsPerTile>();
     else if (later == 1) wait_vm<kLoadsPerTile>();
     else wait_vm<0>();
-    const uint32_t t0 = kt * kTT;
-    if (t0 + kTT > k_end) {
-      // last tile: rows past the end hold whatever row 0 of page 0 holds;
-      // zero their V (a NaN there must not reach the product)
-      unsigned char *vt_lds = lds + (kt % kStages) * L::kStage + L::kTile;
-      block_sync_lds();
-      for (uint32_t e = tid; e < uint32_t(kTT * L::CPR); e += 256) {
-        const uint32_t r = e / L::CPR;
-        if (t0 + r >= k_end)
-          *reinterpret_cast<uint4 *>(vt_lds + r * L::kRowB + 16u * (e % L::CPR)) = make_uint4(0, 0, 0, 0);
-      }
-    }
     block_sync_lds();
   };
-  // S^T of key tile kt for both 16-row halves and both N-tiles: eight
-  // independent MFMA chains (even and odd k-steps apart), sixteen per SIMD
-  // with two waves, which keeps the 16x16x32 pipe full
-  auto scores = [&](uint32_t kt, f32x4_t (&sc)[2][2]) {
-    const unsigned char *kt_lds = lds + (kt % kStages) * L::kStage;
-    uint4 ka[2][KS];
+
+  // Operand reads.  Score product, k-step ks of the tile in `stage`; value
+  // product j = MB t + b (step t, value block b) of the tile in `stage`.
+  auto k_read = [&](const unsigned char *stage, int ks) {
+    return *reinterpret_cast<const uint4 *>(stage + k_off[ks]);
+  };
+  auto v_read = [&](const unsigned char *stage, int j) {
+    const unsigned char *p = stage + 16 * (j / MB) * L::kRowB;
+    const uint2 lo = lds_read_tr16(p + v_off[j % MB][0]), hi = lds_read_tr16(p + v_off[j % MB][1]);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
+  // S^T of a key tile alone (the pipeline's first tile): one chain of KS
+  // MFMAs over the stage's K rows.
+  auto scores = [&](const unsigned char *stage) {
+    f32x16_t acc;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const uint32_t r = 16u * mb + c16;
+    for (int x = 0; x < 16; ++x) acc[x] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[mb][ks] = *reinterpret_cast<const uint4 *>(kt_lds + r * L::kRowB +
-                                                      16u * ((4u * ks + j) ^ L::swz(r)));
-    }
-    f32x4_t acc[2][2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) acc[mb][nt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mb][nt][ks & 1] = M::qk(ka[mb][ks], qb[nt][ks], acc[mb][nt][ks & 1]);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sc[mb][nt] = acc[mb][nt][0] + acc[mb][nt][1];
+    for (int ks = 0; ks < KS; ++ks) acc = M::mma(k_read(stage, ks), qb[ks], acc);
+    return acc;
   };
 
-  // Software pipeline: the scores of tile kt+1 are issued before the
-  // softmax and value product of tile kt, so the matrix core works on the
-  // next tile while the VALU computes this tile's exponentials.
-  f32x4_t s[2][2];
-  if (n_tiles) {
-    ready(0, n_tiles - 1 < 2u ? n_tiles - 1 : 2u);
-    scores(0, s);
-  }
-  for (uint32_t kt = 0; kt < n_tiles; ++kt) {
-    const uint32_t t0 = kt * kTT;
-    unsigned char *vt_lds = lds + (kt % kStages) * L::kStage + L::kTile;
-    // issued so far: tiles 0 .. kt+2
-    if (kt + 1 < n_tiles) ready(kt + 1, kt + 2 < n_tiles ? 1u : 0u);
+  // Probabilities of a tile against the current reference, packed as the
+  // value product's B operands (pk[4t .. 4t+3] for step t), and this lane's
+  // sum of them.
+  auto probs = [&](const f32x16_t &x, uint32_t (&pk)[8]) {
+    float ts = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p0v = fast_exp2(__builtin_fmaf(x[2 * j], sl2, -m));
+      const float p1v = fast_exp2(__builtin_fmaf(x[2 * j + 1], sl2, -m));
+      pk[j] = M::pack2(p0v, p1v);
+      ts = M::add_pair(pk[j], ts);
+    }
+    return ts;
+  };
 
-    // scores of tile kt, masked where a key is not visible
-    float x[2][2][4];  // [N-tile][half][row]
+  // One step of the software pipeline for tile kt in ring stage ST.  The
+  // score MFMAs of tile kt + 1 (into s_next) are interleaved with the
+  // softmax arithmetic of tile kt (its scores s_cur came from the step
+  // before): the matrix core runs the independent products while the VALU
+  // works, in the same wave.  Then the value product of tile kt.  Each
+  // MFMA's LDS operand read is issued kAhead MFMAs ahead.
+  constexpr int NPV = 2 * MB;       // value-product MFMAs per tile
+  constexpr int kAhead = 2;
+  constexpr int PPS = 8 / KS;       // probability pairs per score MFMA
+  auto step = [&](auto st_c, uint32_t kt, f32x16_t &s_cur, f32x16_t &s_next) {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr int ST1 = (ST + 1) % kStages;
+    const unsigned char *st_lds = lds + ST * L::kStage;
+    const unsigned char *st1_lds = lds + ST1 * L::kStage;
+    const uint32_t t0 = kt * kTT;
+    // issued so far: tiles 0 .. kt+2; tile kt+1 ready (after the last tile
+    // the scores below read a stage whose contents are not used; in bounds,
+    // no load in flight to it)
+    if (kt + 1 < n_tiles) ready(kt + 2 < n_tiles ? 1u : 0u);
+    const bool refill = kt + kStages - 1 < n_tiles;
+    const bool rfast = refill && fast_tile(kt + kStages - 1);
+    uint32_t roff[L::NI], rwb = 0;
+    if (rfast) rwb = wave_base(kt + kStages - 1);
+    else if (refill) lookup(kt + kStages - 1, roff);
+
+    uint4 kb[kAhead + 1], vb[kAhead + 1];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[nt][mb][e] = s[mb][nt][e];
+    for (int j = 0; j < kAhead; ++j) kb[j] = k_read(st1_lds, j);
+
+    f32x16_t &x = s_cur;
     const bool full = a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
                                : (t0 + kTT <= k_end);
     if (!full) {
+      // result element 4i + e of this lane is key key_of_elem(i, e) + 2 hf
+      // of the tile: visible iff that is at most lim - t0
+      const int dl = int(lim) - int(t0) - 2 * int(hf);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        // key row 16mb + 4j + e of the tile is visible iff its index is at
-        // most lim[nt] - t0 - 4j (one signed compare per score)
-        const int d = int(lim[nt]) - int(t0) - int(4u * j);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[nt][mb][e] = 16 * mb + e <= d ? x[nt][mb][e] : -INFINITY;
-      }
+        for (int e = 0; e < 4; ++e) x[4 * i + e] = key_of_elem(i, e) <= dl ? x[4 * i + e] : -INFINITY;
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // One straight-line block: the MFMAs of tile kt+1's scores interleaved
-    // with tile kt's softmax arithmetic.  After the last tile the scores
-    // read a ring stage whose contents are not used (in bounds).
-    f32x4_t s_next[2][2];
-    scores(kt + 1, s_next);
-    // online softmax (base 2): each probability is exp2(score * scale_log2
-    // - m) with one FMA, against the row's current reference m
-    uint4 pb[2];
-    auto probs = [&](int nt) {
-      float p[2][4];
+    // scores of tile kt + 1 beside the probabilities of tile kt, packed as
+    // the value product's B operands (pk[4t .. 4t+3] for step t), and this
+    // lane's sum of them
+    uint32_t pk[8];
+    float ts = 0.f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int z = 0; z < 16; ++z) s_next[z] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[mb][e] = fast_exp2(__builtin_fmaf(x[nt][mb][e], sl2, -m[nt]));
-      // P^T operand in the value reads' row order (see pv_off): pack even
-      // and odd rows of each half, then one swap of lanes 32..63 of the even
-      // pairs with lanes 0..31 of the odd pairs
-      const auto lo = __builtin_amdgcn_permlane32_swap(M::pack2(p[0][0], p[0][2]),
-                                                       M::pack2(p[0][1], p[0][3]), false, false);
-      const auto hi = __builtin_amdgcn_permlane32_swap(M::pack2(p[1][0], p[1][2]),
-                                                       M::pack2(p[1][1], p[1][3]), false, false);
-      pb[nt] = make_uint4(lo[0], lo[1], hi[0], hi[1]);
-    };
-    // this lane's largest raw score of each N-tile (8 of the row's 32 keys)
-    float lmax[2];
+    for (int j = 0; j < KS; ++j) {
+      if (j + kAhead < KS) kb[(j + kAhead) % (kAhead + 1)] = k_read(st1_lds, j + kAhead);
+      if (j >= KS - kAhead) vb[j - (KS - kAhead)] = v_read(st_lds, j - (KS - kAhead));
+      s_next = M::mma(kb[j % (kAhead + 1)], qb[j], s_next);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      lmax[nt] = vmax3(vmax3(x[nt][0][0], x[nt][0][1], x[nt][0][2]),
-                       vmax3(x[nt][0][3], x[nt][1][0], x[nt][1][1]),
-                       vmax(x[nt][1][2], x[nt][1][3]));
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) probs(nt);
-    // schedule of the block: the key-tile reads first, then one MFMA per
-    // five VALU instructions
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-    // Lazy rescaling: the reference only moves when a row's max exceeds it
-    // by more than kSlack (base 2), so probabilities stay below 2^kSlack and
-    // most tiles take none of this.  The result is the same softmax:
-    // numerator and denominator share the reference.  A lane above its
-    // threshold means its row's max is too, so the row maxima are formed
-    // only here.
-    if (__any(lmax[0] > thr[0] || lmax[1] > thr[1])) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float mt = rows4_vmax(lmax[nt]) * sl2;
-        const float m_new = mt > m[nt] + kSlack ? mt : m[nt];
-        const float alpha = fast_exp2(m[nt] - m_new);
-        m[nt] = m_new;
-        thr[nt] = (m_new + kSlack) * inv_sl2;
-#pragma unroll
-        for (int b = 0; b < DB; ++b) o[nt][b] *= alpha;
-        lacc[nt] *= alpha;
-        probs(nt);
+      for (int u = 0; u < PPS; ++u) {
+        const int pr = PPS * j + u;
+        const float p0v = fast_exp2(__builtin_fmaf(x[2 * pr], sl2, -m));
+        const float p1v = fast_exp2(__builtin_fmaf(x[2 * pr + 1], sl2, -m));
+        pk[pr] = M::pack2(p0v, p1v);
+        ts = M::add_pair(pk[pr], ts);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // Lazy rescaling: the reference moves only when some lane's tile sum
+    // passes kSumLimit (so no probability exceeds it); numerator and
+    // denominator share the reference, so the result is the same softmax.
+    if (__any(ts > kSumLimit)) {
+      float lmax = vmax3(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], x[5]), vmax3(x[6], x[7], x[8]));
+      lmax = vmax3(lmax, vmax3(x[9], x[10], x[11]), vmax3(x[12], x[13], x[14]));
+      lmax = vmax(lmax, x[15]);
+      lmax = halves_max(lmax);  // both halves of the q-row
+      const float m_new = vmax(m, lmax * sl2);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) o[b] *= alpha;
+      lsum *= alpha;
+      ts = probs(x, pk);
+    }
+    lsum += ts;
+    __builtin_amdgcn_sched_barrier(0);
 
-    // The value product runs at a raised wave priority: the other wave of
-    // the SIMD (from another block) issues in its gaps, not the reverse.
-    __builtin_amdgcn_s_setprio(1);
-    // O^T += V^T . P^T over the 32 keys: K slots 8j .. 8j+3 are key rows
-    // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16.  The reads of
-    // block b + kPvAhead are issued before the MFMAs of block b and the
-    // order is fenced, so the transposed-read latency hides behind the
-    // MFMAs in flight.
-    {
-      constexpr int kPvAhead = 3;
-      auto load_v = [&](int b) -> uint4 {
-        const unsigned char *p0 = vt_lds + pv_off[b];
-        const uint2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * L::kRowB);
-        return make_uint4(lo.x, lo.y, hi.x, hi.y);
-      };
-      uint4 va[kPvAhead + 1];
+    // value product of tile kt
 #pragma unroll
-      for (int b = 0; b < kPvAhead && b < DB; ++b) va[b] = load_v(b);
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        if (b + kPvAhead < DB) va[(b + kPvAhead) % (kPvAhead + 1)] = load_v(b + kPvAhead);
-        o[0][b] = M::qk(va[b % (kPvAhead + 1)], pb[0], o[0][b]);
-        o[1][b] = M::qk(va[b % (kPvAhead + 1)], pb[1], o[1][b]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int j = 0; j < NPV; ++j) {
+      if (j + kAhead < NPV) vb[(j + kAhead) % (kAhead + 1)] = v_read(st_lds, j + kAhead);
+      const int t = j / MB, b = j % MB;
+      o[b] = M::mma(vb[j % (kAhead + 1)], make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]), o[b]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    lacc[0] = M::qk(ones, pb[0], lacc[0]);
-    lacc[1] = M::qk(ones, pb[1], lacc[1]);
-    __builtin_amdgcn_s_setprio(0);
-    // refill the stage of tile kt-1 (every wave passed this iteration's
-    // barrier, so none still reads it)
-    if (kt + kStages - 1 < n_tiles) issue(kt + kStages - 1);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) s[mb][nt] = s_next[mb][nt];
+    // refill the stage of tile kt-1 (every wave passed this step's barrier,
+    // so none still reads it)
+    if (rfast) issue_fast(kt + kStages - 1, rwb);
+    else if (refill) issue(kt + kStages - 1, roff);
+  };
+
+  f32x16_t sa, sb;
+  if (n_tiles) {
+    ready(n_tiles - 1 < 2u ? n_tiles - 1 : 2u);
+    sa = scores(lds);
   }
+  // whole groups of four tiles (ring stages 0..3 in order), then the rest
+  const uint32_t n4 = n_tiles & ~3u;
+  for (uint32_t kt = 0; kt < n4; kt += 4) {
+    step(IC<0>(), kt, sa, sb);
+    step(IC<1>(), kt + 1, sb, sa);
+    step(IC<2>(), kt + 2, sa, sb);
+    step(IC<3>(), kt + 3, sb, sa);
+  }
+  if (n4 < n_tiles) step(IC<0>(), n4, sa, sb);
+  if (n4 + 1 < n_tiles) step(IC<1>(), n4 + 1, sb, sa);
+  if (n4 + 2 < n_tiles) step(IC<2>(), n4 + 2, sa, sb);
 
-  // normalise and write: lane holds O^T[d = 16b + 4j + e][q-row c16]
+  // normalise and write: lane holds O^T[d = 32mb + 8i + 4hf + e][q-row c32]
+  const float l_tot = halves_sum(lsum);
+  if (!row_ok) return;
+  T *out = static_cast<T *>(a.out) + (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float l_tot = lacc[nt][0];  // every row of the ones block holds the sum
-    if (!row_ok[nt]) continue;
-    const uint32_t r = 32u * wv + 16u * nt + c16;
-    const uint32_t qq = r / grp, h = r % grp;
-    T *out = static_cast<T *>(a.out) + (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + h) * D;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  for (int b = 0; b < MB; ++b)
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
+    for (int i = 0; i < 4; ++i) {
       uint2 w;
-      w.x = M::pack2(o[nt][b][0] * inv, o[nt][b][1] * inv);
-      w.y = M::pack2(o[nt][b][2] * inv, o[nt][b][3] * inv);
-      *reinterpret_cast<uint2 *>(out + 16 * b + 4 * j) = w;
+      w.x = M::pack2(o[b][4 * i] * inv, o[b][4 * i + 1] * inv);
+      w.y = M::pack2(o[b][4 * i + 2] * inv, o[b][4 * i + 3] * inv);
+      *reinterpret_cast<uint2 *>(out + 32 * b + 8 * i + 4 * hf) = w;
     }
-  }
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
