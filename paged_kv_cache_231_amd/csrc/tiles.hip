@@ -169,6 +169,17 @@ __device__ __forceinline__ void settle(const uint4 &x) {
   asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
 }
 
+// A block-table entry beyond the LDS copy: one load, waited for in the same
+// instruction block.  The wait covers every earlier load too (the ring can
+// afford it on this path, taken only past kTableCache pages), and the
+// compiler never sees a pending load whose registers it might reuse: a load
+// it knew about would make it wait for all loads before later LDS reads.
+__device__ __forceinline__ uint32_t table_word(const uint32_t *p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -230,6 +241,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (each entry holds the element offset of the page's first row: K and V
   // share their strides since head_dim == value_dim)
   const uint32_t page_elems = uint32_t(a.k_page);
+  // element offset of a physical page (ids outside the pool read page 0)
+  auto page_of = [&](uint32_t pg) { return (pg < pv.N ? pg : 0u) * page_elems; };
   const uint32_t n_lp = (k_end + ps - 1) / ps;
   for (uint32_t e = tid; e < n_lp && e < uint32_t(kTableCache); e += 256) {
     const uint32_t pg = table[e];
@@ -303,14 +316,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint32_t lp = ok ? tok >> ps_shift : 0u;  // entry 0 exists whenever a tile does
         const uint32_t pbase = lp < uint32_t(kTableCache)
                                    ? tcache[lp]
-                                   : (table[lp] < pv.N ? table[lp] : 0u) * page_elems;
+                                   : page_of(table_word(table + lp));
         off[n] = ok ? pbase + tile_off + lane_off[n] : pbase + lane_off[n] - (rr & (ps - 1u)) * tok_elems;
       } else {
         const uint32_t lp = ok ? tok / ps : 0u;
         const uint32_t slot = ok ? tok - lp * ps : 0u;
         const uint32_t pbase = lp < uint32_t(kTableCache)
                                    ? tcache[lp]
-                                   : (table[lp] < pv.N ? table[lp] : 0u) * page_elems;
+                                   : page_of(table_word(table + lp));
         off[n] = pbase + slot * tok_elems + lane_off[n];
       }
     }
@@ -333,11 +346,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // constant address space, the entry is a scalar load)
   const __attribute__((address_space(4))) uint32_t *ctable =
       (const __attribute__((address_space(4))) uint32_t *)table;
-  auto wave_base = [&](uint32_t kt) -> uint32_t {
+  // the page of the wave's rows in tile kt (a raw table word), and the
+  // element offset of its first row
+  auto wave_page = [&](uint32_t kt) -> uint32_t {
     const uint32_t tw = __builtin_amdgcn_readfirstlane(kt * kTT + kWaveRows * wv);
-    const uint32_t pg = ctable[tw >> ps_shift];
-    return (pg < pv.N ? pg : 0u) * page_elems + (tw & (ps - 1u)) * tok_elems;
+    return ctable[tw >> ps_shift];
   };
+  auto wave_base_of = [&](uint32_t kt, uint32_t pg) -> uint32_t {
+    const uint32_t tw = kt * kTT + kWaveRows * wv;
+    return page_of(pg) + (tw & (ps - 1u)) * tok_elems;
+  };
+  auto wave_base = [&](uint32_t kt) { return wave_base_of(kt, wave_page(kt)); };
   auto issue_fast = [&](uint32_t kt, uint32_t wb) {
     unsigned char *stage = lds + (kt % kStages) * L::kStage;
     const T *kb = kbase + wb, *vb = vbase + wb;
@@ -402,6 +421,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       issue(kt, off);
     }
   }
+  // page of the next refill (fast path)
+  uint32_t rpg = fast_tile(kStages - 1) ? wave_page(kStages - 1) : 0u;
 
   // Tile kt's ring stage is complete and visible to every wave once each
   // thread has seen its own loads of kt land and the block has passed a
@@ -472,9 +493,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (kt + 1 < n_tiles) ready(kt + 2 < n_tiles ? 1u : 0u);
     const bool refill = kt + kStages - 1 < n_tiles;
     const bool rfast = refill && fast_tile(kt + kStages - 1);
-    uint32_t roff[L::NI], rwb = 0;
-    if (rfast) rwb = wave_base(kt + kStages - 1);
-    else if (refill) lookup(kt + kStages - 1, roff);
+    uint32_t roff[L::NI];
+    if (refill && !rfast) lookup(kt + kStages - 1, roff);
 
     uint4 kb[kAhead + 1], vb[kAhead + 1];
 #pragma unroll
@@ -545,8 +565,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     // refill the stage of tile kt-1 (every wave passed this step's barrier,
     // so none still reads it)
-    if (rfast) issue_fast(kt + kStages - 1, rwb);
+    if (rfast) issue_fast(kt + kStages - 1, wave_base_of(kt + kStages - 1, rpg));
     else if (refill) issue(kt + kStages - 1, roff);
+    // page of the next step's refill: its scalar read completes by that
+    // step's barrier
+    rpg = fast_tile(kt + kStages) ? wave_page(kt + kStages) : 0u;
   };
 
   f32x16_t sa, sb;

@@ -339,6 +339,15 @@ def test_prefill_tiles_page_sizes(causal, ps):
     assert_close(run(wl, splits=3), expected(wl), torch.bfloat16, f"prefill ps={ps} split")
 
 
+def test_prefill_tiles_long_table():
+    """A chunk behind a 16,600-token prior at page size 16: its block-table
+    row (over 1,040 pages) is longer than the kernel's LDS copy, so whole
+    tiles take their pages from the plan words directly and the last, partial
+    tile reads entries past the copy one by one."""
+    wl = _prefill_wl(torch.bfloat16, 8, 2, 128, 16, [(16600, 45)], [5], seed=977)
+    assert_close(run(wl), expected(wl), torch.bfloat16, "prefill long table")
+
+
 def test_graph_capture_mixed_prefill_and_decode():
     """A plan with prefill tiles, decode rows and a split merge, captured once
     into a graph and replayed after rebinding shorter priors and lengths
