@@ -1,8 +1,9 @@
 """GPU parity of attention over an FP8 E4M3 cache (pkv_attention_fp8)
 against the oracle's decoded-cache attention: every finite code through the
 kernel's widening (bit for bit), head dims, GQA groups, page sizes,
-unsplit / split / balanced, a window, chunk queries (run as rows), the
-decode workload at full size (sampled), and the argument errors."""
+unsplit / split / balanced, a window, chunk queries (run as rows) and the
+argument errors (the decode workload at full size is checked in
+test_gpu_full_size.py)."""
 
 import numpy as np
 import pytest
@@ -10,8 +11,8 @@ import torch
 
 import oracle
 import paged_kv_cache_231_amd as pkv
-from workloads import build_attention, config, decode_queries, fp8_caches
-from tests._gpu import assert_close, make_plan, to_dev
+from workloads import build_attention, decode_queries, fp8_caches
+from tests._gpu import assert_close, make_plan
 
 pytestmark = pytest.mark.gpu
 
@@ -93,21 +94,6 @@ def test_fp8_chunk_queries_run_as_rows():
     k8, v8 = fp8_caches(wl, KS, VS)
     for splits in (1, 0):
         assert_close(_run(wl, k8, v8, splits=splits), _want(wl, k8, v8), torch.bfloat16, "chunks")
-
-
-@pytest.mark.parametrize("splits", [0, 8])
-def test_fp8_full_size_sampled(splits):
-    wl = config(2)
-    k8, v8 = fp8_caches(wl, KS, VS)
-    got = _run(wl, k8, v8, splits=splits)
-    rng = np.random.default_rng(11)
-    idx = sorted(set(int(x) for x in rng.integers(0, wl.queries, size=10)) | {0, wl.queries - 1})
-    for i in idx:
-        h = int(rng.integers(0, wl.info["hq"]))
-        want, _ = oracle.attention_one_fp8(wl.tensors["q"], k8, v8, wl.lens, wl.qseq, wl.qpos,
-                                           wl.table, wl.page_size, wl.scale, wl.causal, i, h,
-                                           KS, VS)
-        assert_close(got[i, h][None], want[None], wl.dtype, f"row {i} head {h}")
 
 
 def test_fp8_argument_errors():

@@ -166,3 +166,37 @@ def test_prefill_tiles_d64_moving_reference():
                          poison=True)
     wl = _scale_rows(_quarter(wl, "v"), "k", _ramp)
     assert_close(run(wl), expected(wl), torch.float16, "prefill d=64 ramp")
+
+
+def _half_ulp(x, dtype):
+    """Half a unit in the last place of |x| in the output dtype (bf16: 8
+    significant bits, f16: 11), for normal values."""
+    bits = 8 if dtype == torch.bfloat16 else 11
+    e = np.floor(np.log2(np.maximum(np.abs(x), 1e-30)))
+    return np.ldexp(0.5, (e - (bits - 1)).astype(np.int64))
+
+
+@pytest.mark.parametrize("kernel", ["prefill", "decode", "balanced"])
+def test_peaked_rows_unscaled_within_rounding(kernel):
+    """The ramp cases with the value rows as drawn (no 1/4 factor): rows are
+    nearly one-hot, so outputs reach |out| >= 4, where half a bf16 unit in
+    the last place (2^-6 = 0.0156) already exceeds the absolute 1.5e-2.
+    Such outputs are held to 1.5e-2 plus half an output ulp, the bound the
+    rounding of the result alone allows."""
+    if kernel == "prefill":
+        wl = _scale_rows(_prefill(torch.bfloat16, 3700), "k", _ramp)
+        splits = 1
+    else:
+        lens = [300, 1000, 2500, 5000, 17]
+        wl = build_attention("rescale", 3800, torch.bfloat16, lens, decode_queries(lens), 32, 8, 128,
+                             128, 16, poison=True)
+        wl = _scale_rows(wl, "k", _ramp)
+        splits = 0 if kernel == "balanced" else 1
+    got = run(wl, splits=splits)
+    want = expected(wl)
+    assert np.isfinite(got).all()
+    assert np.abs(want).max() >= 4.0, "the case must reach outputs of magnitude 4"
+    err = np.abs(got - want)
+    bound = 1.5e-2 + _half_ulp(want, torch.bfloat16)
+    worst = float((err / bound).max())
+    assert worst <= 1.0, f"{kernel}: error above 1.5e-2 + half an ulp (ratio {worst:.3f})"

@@ -1,9 +1,9 @@
 """GPU parity of the sliding window (pkv_attention_window) against the
 oracle's windowed attention: windows shorter than a tile, on and off the
 16-key grid, longer than the sequence; page sizes on and off the tile grid;
-unsplit, split and balanced; chunk queries (which run as rows under a
-window); the benchmark workload at full size, sampled.  Tolerances as the
-other parity tests; unused cache slots are NaN."""
+unsplit, split and balanced; chunk queries.  The benchmark workload at
+full size is checked in test_gpu_full_size.py.  Tolerances as the other
+parity tests; unused cache slots are NaN."""
 
 import numpy as np
 import pytest
@@ -11,8 +11,7 @@ import torch
 
 import oracle
 import paged_kv_cache_231_amd as pkv
-from oracle import reference as ref
-from workloads import build_attention, config, decode_queries
+from workloads import build_attention, decode_queries
 from tests._gpu import assert_close, make_plan, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -98,21 +97,3 @@ def test_window_zero_is_attention():
     b = pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(a, b.double().cpu().numpy())
-
-
-@pytest.mark.parametrize("splits", [0, 8])
-def test_window_full_size_sampled(splits):
-    """The benchmark decode workload (64 sequences, L in 512..8192) with a
-    1024-key window, sampled rows against the oracle row by row."""
-    wl = config(2)
-    dev = to_dev(wl)
-    plan = make_plan(wl)
-    got = _run(wl, 1024, splits=splits, plan=plan, dev=dev)
-    rng = np.random.default_rng(7)
-    idx = sorted(set(int(x) for x in rng.integers(0, wl.queries, size=10)) | {0, wl.queries - 1})
-    t = wl.tensors
-    for i in idx:
-        h = int(rng.integers(0, wl.info["hq"]))
-        want, _ = ref.attention_one(t["q"], t["k"], t["v"], wl.lens, wl.qseq, wl.qpos, wl.table,
-                                    wl.page_size, wl.scale, wl.causal, i, h, window=1024)
-        assert_close(got[i, h][None], want[None], wl.dtype, f"row {i} head {h}")
