@@ -34,6 +34,9 @@ With --workload 4 (that mixed workload as the step) the roofline is the tile
 kernel's FLOP rate against the MFMA peak and `value` is useful TFLOP/s per
 step; with --workload 5 (MLA) the roofline is HBM with the MFMA fraction
 beside it.
+  prefill_window
+                the same tile kernel with every query limited to its last
+                1024 keys (useful FLOPs inside the windows).
   append, window, fp8
                 the cache append, sliding-window decode and FP8-cache decode
                 legs (per-kernel HIP-event durations).
@@ -173,9 +176,10 @@ def cpu_baseline(wl, budget_s: float):
                       f"(float64 numpy, {elapsed:.1f} s, {done_bytes / 1e9:.3f} GB of cache rows)"}
 
 
-def tile_query_flops(plan, wl) -> int:
+def tile_query_flops(plan, wl, window: int = 0) -> int:
     """Useful FLOPs of the queries the tile kernel owns: every query that is
-    not a decode row of the plan (plan words: header, lens, qseq, qpos, rows)."""
+    not a decode row of the plan (plan words: header, lens, qseq, qpos, rows);
+    under a window each query counts only the keys inside it."""
     words = plan.words
     R = int(words[7])
     S, Q = int(words[3]), int(words[2])
@@ -183,23 +187,30 @@ def tile_query_flops(plan, wl) -> int:
     in_rows = np.zeros(Q, dtype=bool)
     in_rows[np.asarray(words[rows_off:rows_off + R], dtype=np.int64)] = True
     vis = wl.visible().astype(np.int64)
+    if window:
+        vis = np.minimum(vis, window)
     hq, d, dv = wl.info["hq"], wl.info["d"], wl.info["dv"]
     return int(vis[~in_rows].sum()) * hq * 2 * (d + dv)
 
 
-def prefill_measure(torch, pkv, workloads, steps: int):
-    """Tile-kernel TFLOP/s on the mixed chunked-prefill workload."""
+def prefill_measure(torch, pkv, workloads, steps: int, window: int = 0):
+    """Tile-kernel TFLOP/s on the mixed chunked-prefill workload (with
+    ``window``: every query limited to its last ``window`` keys)."""
     wl = workloads.config(4)
     dev = {k: v.to("cuda") for k, v in wl.tensors.items()}
     stream = torch.cuda.current_stream()
     plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
     hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
     out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
-    splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
+    if window:
+        splits = 0
+    else:
+        splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
     ws = pkv.Workspace.for_splits(wl.queries, hq, dv, splits)
 
     def step():
-        pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws, out=out)
+        pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws, out=out,
+                      window=window)
 
     for _ in range(3):
         step()
@@ -212,14 +223,14 @@ def prefill_measure(torch, pkv, workloads, steps: int):
     n_r, ms_r = plan.timing_read("rows")
     plan.timing(False)
     T = int(plan.words[8])
-    flops = tile_query_flops(plan, wl)
+    flops = tile_query_flops(plan, wl, window)
     avg_t = ms_t / max(1, n_t)
     tfs = flops / (avg_t * 1e-3) / 1e12
     return {"value": round(tfs, 1), "unit": "TFLOP/s", "peak": MFMA_BF16_PEAK_TFS,
             "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "kernel": "chunked-prefill tiles",
             "avg_launch_us": round(avg_t * 1e3, 2), "launches": n_t, "flops_per_launch": flops,
             "tiles": T, "decode_rows_us": round(ms_r / max(1, n_r) * 1e3, 2),
-            "workload": wl.name}
+            "workload": wl.name + (f", window {window}" if window else "")}
 
 
 def append_measure(torch, pkv, workloads, steps: int):
@@ -578,6 +589,7 @@ def main():
     }
     if not args.no_prefill and wl.kind == "attention":
         line["prefill"] = prefill_measure(torch, pkv, workloads, args.prefill_steps)
+        line["prefill_window"] = prefill_measure(torch, pkv, workloads, args.prefill_steps, window=1024)
         line["append"] = append_measure(torch, pkv, workloads, args.prefill_steps)
         line["window"] = window_measure(torch, pkv, workloads, args.prefill_steps)
         line["fp8"] = fp8_measure(torch, pkv, workloads, args.prefill_steps)

@@ -266,10 +266,10 @@ pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q,
  * decode-attention geometry; the page shows the field, not its use): query
  * i sees only the last `window` of its visible keys, positions
  * [max(0, n - window), n) with n as in pkv_attention; window 0 is
- * pkv_attention.  With a window every query runs on the row kernels (decode
- * rows and chunk queries alike; the chunked-prefill tile kernel has no
- * window), with split, balanced or no workspace.  Arguments and errors as
- * pkv_attention. */
+ * pkv_attention.  Decode rows run on the row kernels (split, balanced or
+ * unsplit), chunk queries on the chunked-prefill tile kernel, which starts
+ * each block at its first query's window and reads nothing before it.
+ * Arguments and errors as pkv_attention. */
 pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype,
                                 const void *q, const void *k, const void *v,
                                 void *out, uint32_t q_heads, uint32_t kv_heads,

@@ -89,6 +89,7 @@ struct TileArgs {
   uint32_t n_tiles;
   uint32_t hq, hkv, d, dv;
   int causal;
+  uint32_t window;   // > 0: only the last `window` visible keys (0 = all)
   float scale_log2;
   const void *q, *k, *v;
   uint64_t k_page, k_tok, v_page, v_tok;

@@ -269,6 +269,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t pos_min = p0 + q_lo;
   // last visible key of the q-row: its position (causal) or the last key
   const uint32_t lim = a.causal && pos < k_end - 1u ? pos : k_end - 1u;
+  // Sliding window: a query with visible keys [0, n) sees [n - window, n).
+  // The block starts at the tile of its first query's first visible key;
+  // key tiles wholly at or above its last query's first key need no lower
+  // mask.
+  auto win_lo = [&](uint32_t n) { return a.window != 0u && n > a.window ? n - a.window : 0u; };
+  const uint32_t lo_min = win_lo(a.causal ? pos_min + 1u : k_end);
+  const uint32_t lo_max = win_lo(a.causal ? p0 + q_hi : k_end);
+  const uint32_t lo_row = a.causal ? win_lo(pos + 1u) : lo_min;
+  const uint32_t kt0 = lo_min / kTT;
 
   f32x16_t o[MB];
 #pragma unroll
@@ -298,12 +307,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   // DMA of key tile kt into its ring stage, in two parts: `lookup` finds
   // the element offset of each lane's cache row (block-table entries from
-  // the LDS cache, read one pipeline step before the loads are issued, so
-  // their latency hides behind that step), `issue` starts the loads.  Rows
-  // past the end read the sequence's token 0, which every query sees: its
-  // key's scores are masked out there and its probability is 0, so the
-  // product adds 0 x that value row, as it must (a value that is not finite
-  // there makes every output non-finite anyway).
+  // the LDS cache), `issue` starts the loads.  Rows past the end read the
+  // sequence's token 0 (any row inside the pool would do): their scores
+  // are masked out and their value rows are zeroed in LDS before use, so
+  // nothing of them reaches the output.
   auto lookup = [&](uint32_t kt, uint32_t (&off)[L::NI]) {
     const uint32_t tok0 = kt * kTT;
     const uint32_t tile_off = pow2 ? (tok0 & (ps - 1u)) * tok_elems : 0u;
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto wave_base = [&](uint32_t kt) { return wave_base_of(kt, wave_page(kt)); };
   auto issue_fast = [&](uint32_t kt, uint32_t wb) {
-    unsigned char *stage = lds + (kt % kStages) * L::kStage;
+    unsigned char *stage = lds + ((kt - kt0) % kStages) * L::kStage;
     const T *kb = kbase + wb, *vb = vbase + wb;
 #pragma unroll
     for (int n = 0; n < L::NI; ++n) {
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto fast_tile = [&](uint32_t kt) { return fast_dma && (kt + 1) * kTT <= k_end; };
 
   auto issue = [&](uint32_t kt, const uint32_t (&off)[L::NI]) {
-    unsigned char *stage = lds + (kt % kStages) * L::kStage;
+    unsigned char *stage = lds + ((kt - kt0) % kStages) * L::kStage;
 #pragma unroll
     for (int n = 0; n < L::NI; ++n) {
       const uint32_t r0 = L::RPW * (L::NI * wv + n);
@@ -409,10 +416,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  const uint32_t n_tiles = (k_end + kTT - 1) / kTT;
+  const uint32_t n_tiles = (k_end + kTT - 1) / kTT;  // key tiles kt0 .. n_tiles - 1
+  const uint32_t nt = n_tiles - kt0;                  // tiles this block walks
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(qb[ks]);
-  for (uint32_t kt = 0; kt < n_tiles && kt < uint32_t(kStages - 1); ++kt) {
+  for (uint32_t kt = kt0; kt < n_tiles && kt < kt0 + uint32_t(kStages - 1); ++kt) {
     if (fast_tile(kt)) {
       issue_fast(kt, wave_base(kt));
     } else {
@@ -422,7 +430,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   // page of the next refill (fast path)
-  uint32_t rpg = fast_tile(kStages - 1) ? wave_page(kStages - 1) : 0u;
+  uint32_t rpg = fast_tile(kt0 + kStages - 1) ? wave_page(kt0 + kStages - 1) : 0u;
+  // Value rows that no query of the block sees are zeroed in LDS once their
+  // tile has landed (after the barrier that makes it ready), and read only
+  // after one more barrier: the rows past the end of the last tile (if it is
+  // partial) and, under a window, the rows of the first tile before the
+  // first query's window.  (Rows some query of the block sees keep their
+  // values; for the others their probability is 0.)
+  const uint32_t tail_r0 = k_end % kTT;         // first row past the end, 0 if none
+  const uint32_t head_r1 = lo_min - kt0 * kTT;  // rows before the first window
+  auto zero_rows = [&](uint32_t j, uint32_t r0, uint32_t r1) {
+    unsigned char *vt = lds + (j % kStages) * L::kStage + L::kTile;
+    for (uint32_t e = tid; e < (r1 - r0) * uint32_t(L::CPR); e += 256)
+      *reinterpret_cast<uint4 *>(vt + (r0 + e / L::CPR) * L::kRowB + 16u * (e % L::CPR)) =
+          make_uint4(0, 0, 0, 0);
+  };
 
   // Tile kt's ring stage is complete and visible to every wave once each
   // thread has seen its own loads of kt land and the block has passed a
@@ -481,16 +503,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NPV = 2 * MB;       // value-product MFMAs per tile
   constexpr int kAhead = 2;
   constexpr int PPS = 8 / KS;       // probability pairs per score MFMA
-  auto step = [&](auto st_c, uint32_t kt, f32x16_t &s_cur, f32x16_t &s_next) {
-    constexpr int ST = decltype(st_c)::value;
+  auto step = [&](auto st_c, uint32_t j, f32x16_t &s_cur, f32x16_t &s_next) {
+    constexpr int ST = decltype(st_c)::value;  // == j % kStages
     constexpr int ST1 = (ST + 1) % kStages;
     const unsigned char *st_lds = lds + ST * L::kStage;
     const unsigned char *st1_lds = lds + ST1 * L::kStage;
+    const uint32_t kt = kt0 + j;
     const uint32_t t0 = kt * kTT;
-    // issued so far: tiles 0 .. kt+2; tile kt+1 ready (after the last tile
+    // issued so far: tiles up to kt+2; tile kt+1 ready (after the last tile
     // the scores below read a stage whose contents are not used; in bounds,
     // no load in flight to it)
-    if (kt + 1 < n_tiles) ready(kt + 2 < n_tiles ? 1u : 0u);
+    if (j + 1 < nt) {
+      ready(j + 2 < nt ? 1u : 0u);
+      if (tail_r0 != 0u && j + 2 == nt) zero_rows(j + 1, tail_r0, kTT);
+    } else if (tail_r0 != 0u && nt > 1) {
+      block_sync_lds();  // the zeroed rows of the last tile are visible
+    }
     const bool refill = kt + kStages - 1 < n_tiles;
     const bool rfast = refill && fast_tile(kt + kStages - 1);
     uint32_t roff[L::NI];
@@ -501,16 +529,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int j = 0; j < kAhead; ++j) kb[j] = k_read(st1_lds, j);
 
     f32x16_t &x = s_cur;
-    const bool full = a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
-                               : (t0 + kTT <= k_end);
+    const bool full = (a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
+                                : (t0 + kTT <= k_end)) && t0 >= lo_max;
     if (!full) {
       // result element 4i + e of this lane is key key_of_elem(i, e) + 2 hf
-      // of the tile: visible iff that is at most lim - t0
+      // of the tile: visible iff that lies in [lo_row - t0, lim - t0]
       const int dl = int(lim) - int(t0) - 2 * int(hf);
+      const int dlo = int(lo_row) - int(t0) - 2 * int(hf);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * i + e] = key_of_elem(i, e) <= dl ? x[4 * i + e] : -INFINITY;
+        for (int e = 0; e < 4; ++e)
+          x[4 * i + e] = key_of_elem(i, e) <= dl && key_of_elem(i, e) >= dlo ? x[4 * i + e] : -INFINITY;
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -573,21 +603,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   f32x16_t sa, sb;
-  if (n_tiles) {
-    ready(n_tiles - 1 < 2u ? n_tiles - 1 : 2u);
+  if (nt) {
+    ready(nt - 1 < 2u ? nt - 1 : 2u);
+    const bool tail0 = tail_r0 != 0u && nt == 1;
+    if (head_r1 != 0u) zero_rows(0, 0u, head_r1);
+    if (tail0) zero_rows(0, tail_r0, kTT);
+    if (head_r1 != 0u || tail0) block_sync_lds();
     sa = scores(lds);
   }
   // whole groups of four tiles (ring stages 0..3 in order), then the rest
-  const uint32_t n4 = n_tiles & ~3u;
-  for (uint32_t kt = 0; kt < n4; kt += 4) {
-    step(IC<0>(), kt, sa, sb);
-    step(IC<1>(), kt + 1, sb, sa);
-    step(IC<2>(), kt + 2, sa, sb);
-    step(IC<3>(), kt + 3, sb, sa);
+  const uint32_t n4 = nt & ~3u;
+  for (uint32_t j = 0; j < n4; j += 4) {
+    step(IC<0>(), j, sa, sb);
+    step(IC<1>(), j + 1, sb, sa);
+    step(IC<2>(), j + 2, sa, sb);
+    step(IC<3>(), j + 3, sb, sa);
   }
-  if (n4 < n_tiles) step(IC<0>(), n4, sa, sb);
-  if (n4 + 1 < n_tiles) step(IC<1>(), n4 + 1, sb, sa);
-  if (n4 + 2 < n_tiles) step(IC<2>(), n4 + 2, sa, sb);
+  if (n4 < nt) step(IC<0>(), n4, sa, sb);
+  if (n4 + 1 < nt) step(IC<1>(), n4 + 1, sb, sa);
+  if (n4 + 2 < nt) step(IC<2>(), n4 + 2, sa, sb);
 
   // normalise and write: lane holds O^T[d = 32mb + 8i + 4hf + e][q-row c32]
   const float l_tot = halves_sum(lsum);

@@ -72,20 +72,45 @@ def test_window_split_and_balanced(splits):
                      f"window {w} splits {splits}")
 
 
-def test_window_chunk_queries_run_as_rows():
-    """A plan with a prefill chunk: under a window every query runs on the
-    row kernels, each with its own window."""
-    chunks = [(77, 150), (0, 20)]
+def _poison_outside_windows(wl, window):
+    """NaN in every K/V cache slot that no query's window reaches (the pages
+    in front of a sequence's earliest window start and the slots past its
+    length; the workload already holds NaN in the latter)."""
+    for s_ in range(wl.sequences):
+        qs = np.flatnonzero(wl.qseq == s_)
+        if qs.size == 0:
+            continue
+        starts = [oracle.window_start(oracle.visible_count(wl.lens, wl.qseq, wl.qpos, int(i), wl.causal),
+                                      window) for i in qs]
+        for t in range(min(starts)):
+            page, slot = int(wl.table[s_, t // wl.page_size]), t % wl.page_size
+            for name in ("k", "v"):
+                wl.tensors[name][page, slot] = float("nan")
+    return wl
+
+
+@pytest.mark.parametrize("g,d,ps", [(4, 128, 16), (1, 128, 16), (8, 64, 16), (4, 128, 5)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_chunk_queries_on_tiles(g, d, ps, causal):
+    """Chunk queries under a window run on the tile kernel: windows inside
+    one query block's span, a tile wide, across tiles and longer than the
+    history, with the pages before every window poisoned with NaN (a block
+    may not read them) and ragged tails; decode rows alongside."""
+    chunks = [(77, 150), (0, 20), (1500, 200)]
     dec = [33, 300]
     lens = [p + c for p, c in chunks] + dec
     queries = []
-    for s, (p, c) in enumerate(chunks):
-        queries += [(s, p + j) for j in range(c)]
+    for s_, (p, c) in enumerate(chunks):
+        queries += [(s_, p + j) for j in range(c)]
     queries += [(len(chunks) + j, L - 1) for j, L in enumerate(dec)]
-    wl = build_attention("win", 3300, torch.bfloat16, lens, queries, 16, 4, 128, 128, 16,
-                         poison=True)
-    for w, splits in ((10, 1), (64, 3), (100, 0)):
-        assert_close(_run(wl, w, splits=splits), _want(wl, w), torch.bfloat16, f"chunk window {w}")
+    for w, splits in ((1, 1), (7, 0), (32, 1), (45, 3), (300, 0), (5000, 1)):
+        wl = build_attention("win", 3300 + g + d + ps + w, torch.bfloat16, lens, queries, 2 * g, 2, d,
+                             d, ps, causal=causal, poison=True)
+        plan = make_plan(wl)
+        assert plan.n_tiles > 0
+        _poison_outside_windows(wl, w)
+        assert_close(_run(wl, w, splits=splits, plan=plan), _want(wl, w), torch.bfloat16,
+                     f"chunk window {w} g={g} d={d} ps={ps} causal={causal}")
 
 
 def test_window_zero_is_attention():
