@@ -37,6 +37,8 @@ beside it.
   prefill_window
                 the same tile kernel with every query limited to its last
                 1024 keys (useful FLOPs inside the windows).
+  prefill_fp8   the same tile kernel over E4M3 K/V caches of the same
+                workload (codes widened to bf16 on the way into LDS).
   append, window, fp8
                 the cache append, sliding-window decode and FP8-cache decode
                 legs (per-kernel HIP-event durations).
@@ -193,24 +195,32 @@ def tile_query_flops(plan, wl, window: int = 0) -> int:
     return int(vis[~in_rows].sum()) * hq * 2 * (d + dv)
 
 
-def prefill_measure(torch, pkv, workloads, steps: int, window: int = 0):
+def prefill_measure(torch, pkv, workloads, steps: int, window: int = 0, fp8=None):
     """Tile-kernel TFLOP/s on the mixed chunked-prefill workload (with
-    ``window``: every query limited to its last ``window`` keys)."""
+    ``window``: every query limited to its last ``window`` keys; with
+    ``fp8`` = (k_scale, v_scale): over E4M3 caches of the same K/V)."""
     wl = workloads.config(4)
     dev = {k: v.to("cuda") for k, v in wl.tensors.items()}
+    if fp8:
+        k8, v8 = workloads.fp8_caches(wl, *fp8)
+        dev["k"], dev["v"] = k8.to("cuda"), v8.to("cuda")
     stream = torch.cuda.current_stream()
     plan = pkv.Plan(wl.lens, wl.qseq, wl.qpos, wl.table, wl.page_size, wl.pages, stream=stream)
     hq, hkv, d, dv = (wl.info[x] for x in ("hq", "hkv", "d", "dv"))
     out = torch.empty(wl.queries, hq, dv, dtype=wl.dtype, device="cuda")
-    if window:
+    if window or fp8:
         splits = 0
     else:
         splits = pkv.tune_splits(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, out=out)
     ws = pkv.Workspace.for_splits(wl.queries, hq, dv, splits)
 
     def step():
-        pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws, out=out,
-                      window=window)
+        if fp8:
+            pkv.attention_fp8(plan, dev["q"], dev["k"], dev["v"], wl.scale, *fp8, wl.causal,
+                              workspace=ws, out=out, window=window)
+        else:
+            pkv.attention(plan, dev["q"], dev["k"], dev["v"], wl.scale, wl.causal, workspace=ws,
+                          out=out, window=window)
 
     for _ in range(3):
         step()
@@ -230,7 +240,8 @@ def prefill_measure(torch, pkv, workloads, steps: int, window: int = 0):
             "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "kernel": "chunked-prefill tiles",
             "avg_launch_us": round(avg_t * 1e3, 2), "launches": n_t, "flops_per_launch": flops,
             "tiles": T, "decode_rows_us": round(ms_r / max(1, n_r) * 1e3, 2),
-            "workload": wl.name + (f", window {window}" if window else "")}
+            "workload": wl.name + (f", window {window}" if window else "")
+            + (", E4M3 K/V cache" if fp8 else "")}
 
 
 def append_measure(torch, pkv, workloads, steps: int):
@@ -590,6 +601,7 @@ def main():
     if not args.no_prefill and wl.kind == "attention":
         line["prefill"] = prefill_measure(torch, pkv, workloads, args.prefill_steps)
         line["prefill_window"] = prefill_measure(torch, pkv, workloads, args.prefill_steps, window=1024)
+        line["prefill_fp8"] = prefill_measure(torch, pkv, workloads, args.prefill_steps, fp8=(0.05, 0.04))
         line["append"] = append_measure(torch, pkv, workloads, args.prefill_steps)
         line["window"] = window_measure(torch, pkv, workloads, args.prefill_steps)
         line["fp8"] = fp8_measure(torch, pkv, workloads, args.prefill_steps)

@@ -286,9 +286,11 @@ pkv_status pkv_attention_window(const pkv_plan *plan, pkv_dtype dtype,
  * and the result is that of pkv_attention_window on those keys and values.
  *   q [Q, q_heads, head_dim] and out [Q, q_heads, value_dim]: F16 or BF16
  *   k [N, ps, kv_heads, head_dim], v [N, ps, kv_heads, value_dim]: bytes
- * head_dim == value_dim in {64, 128, 256}; q, k, v 16-byte aligned.  Every
- * query runs on the decode MFMA kernels (which widen the bytes exactly to
- * the query type in LDS), with split, balanced or no workspace.  Errors: as
+ * head_dim == value_dim in {64, 128, 256}; q, k, v 16-byte aligned.  Decode
+ * rows run on the decode MFMA kernels (split, balanced or unsplit) and, for
+ * head dims 64 and 128, chunk queries on the chunked-prefill tile kernel;
+ * both widen the bytes exactly to the query type on their way into LDS (at
+ * head dim 256 chunk queries run as rows).  Errors: as
  * pkv_attention; PKV_EINVAL for F32 queries, scales not finite and > 0 or
  * misaligned tensors; PKV_ESHAPE for other head dims. */
 pkv_status pkv_attention_fp8(const pkv_plan *plan, pkv_dtype dtype,

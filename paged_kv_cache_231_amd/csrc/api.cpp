@@ -726,6 +726,8 @@ pkv_status attention_impl(const pkv_plan *plan, pkv_dtype dtype, bool fp8, const
   ta.causal = ra.causal;
   ta.window = window;
   ta.scale_log2 = ra.scale_log2;
+  ta.kv_fp8 = ra.kv_fp8;
+  ta.v_scale = ra.v_scale;
   ta.q = q;
   ta.k = k;
   ta.v = v;
@@ -734,8 +736,7 @@ pkv_status attention_impl(const pkv_plan *plan, pkv_dtype dtype, bool fp8, const
   ta.v_page = ra.v_page;
   ta.v_tok = ra.v_tok;
   ta.out = out;
-  // the tile kernel has no FP8 cache: with one, every query runs as a row
-  const bool use_tiles = L.T > 0 && !fp8 && tiles_supported(ta, dtype);
+  const bool use_tiles = L.T > 0 && tiles_supported(ta, dtype);
   ra.qlist = use_tiles ? plan->dev + L.rows : nullptr;
   ra.n_queries = use_tiles ? L.R : L.Q;
 

@@ -90,7 +90,9 @@ struct TileArgs {
   uint32_t hq, hkv, d, dv;
   int causal;
   uint32_t window;   // > 0: only the last `window` visible keys (0 = all)
-  float scale_log2;
+  float scale_log2;  // includes the key scale of an FP8 cache
+  uint32_t kv_fp8;   // 1: k and v hold E4M3 codes
+  float v_scale;     // value scale of an FP8 cache (1 otherwise)
   const void *q, *k, *v;
   uint64_t k_page, k_tok, v_page, v_tok;
   void *out;

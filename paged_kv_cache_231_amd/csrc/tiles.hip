@@ -25,6 +25,14 @@
 // conflicts.  The block table of the sequence is cached in LDS.  Blocks that
 // share a (tile, KV head) are numbered so they land on one XCD and share its
 // L2.
+//
+// FP8 caches (E4M3 codes, one byte per element, with a key and a value scale)
+// cannot go HBM -> LDS directly: the MFMAs take 16-bit operands.  Each thread
+// loads its share of a tile's codes into registers two steps ahead, widens
+// them exactly to the query type (E4M3 values are all representable in bf16
+// and f16) and writes them into the ring stage in the same swizzled layout,
+// one step before the stage is read.  The key scale is folded into the score
+// scale and the value scale into the normalisation.
 
 #include "mfma_common.h"
 
@@ -185,17 +193,47 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Two E4M3 codes (bytes 0, 1 or 2, 3 of x) widened exactly to the query type.
+template <class DT>
+__device__ __forceinline__ uint32_t widen2(uint32_t x, bool hi);
+template <>
+__device__ __forceinline__ uint32_t widen2<BF16>(uint32_t x, bool hi) {
+  return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true))
+            : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen2<F16>(uint32_t x, bool hi) {
+  return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true))
+            : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
+}
+// Eight codes (two dwords) widened to one 16-byte chunk of the stage.
+template <class DT>
+__device__ __forceinline__ uint4 widen8(uint32_t lo, uint32_t hi) {
+  return make_uint4(widen2<DT>(lo, false), widen2<DT>(lo, true), widen2<DT>(hi, false), widen2<DT>(hi, true));
+}
+
+// Element type of the cache: the query type, or E4M3 codes.
+template <class T, bool F8>
+struct CacheElem {
+  using type = T;
+};
+template <class T>
+struct CacheElem<T, true> {
+  using type = uint8_t;
+};
+
 template <int N>
 struct IC {
   static constexpr int value = N;
 };
 
-template <class DT, int D>
+template <class DT, int D, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     TileArgs a, uint32_t n_sub, uint32_t n_groups) {
   using M = Mfma32<DT>;
   using L = PLds<D>;
   using T = typename DT::T;
+  using CT = typename CacheElem<T, F8>::type;
   constexpr int KS = D / 16;  // k-steps of the score product (8 values per lane half)
   constexpr int MB = D / 32;  // 32-row blocks of value dims
   constexpr int kLoadsPerTile = 2 * L::NI;  // per thread: K and V
@@ -278,6 +316,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t lo_max = win_lo(a.causal ? p0 + q_hi : k_end);
   const uint32_t lo_row = a.causal ? win_lo(pos + 1u) : lo_min;
   const uint32_t kt0 = lo_min / kTT;
+  const uint32_t n_tiles = (k_end + kTT - 1) / kTT;  // key tiles kt0 .. n_tiles - 1
+  const uint32_t nt = n_tiles - kt0;                  // tiles this block walks
 
   f32x16_t o[MB];
 #pragma unroll
@@ -287,8 +327,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m = kNoMax;  // the row's softmax reference (base 2, scaled)
   float lsum = 0.f;  // this lane's share of the row's denominator
   const float sl2 = a.scale_log2;
-  const T *kbase = static_cast<const T *>(a.k) + uint64_t(kvh) * D;
-  const T *vbase = static_cast<const T *>(a.v) + uint64_t(kvh) * D;
+  const CT *kbase = static_cast<const CT *>(a.k) + uint64_t(kvh) * D;
+  const CT *vbase = static_cast<const CT *>(a.v) + uint64_t(kvh) * D;
   __syncthreads();  // table cache ready (Q loads may still be in flight: fine)
 
   // Per-lane parts of the DMA addresses: load n of a wave covers rows
@@ -347,7 +387,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int n = 0; n < L::NI; ++n) {
     const uint32_t rr = L::RPW * (L::NI * wv + n) + lane / L::CPR;
     const uint32_t chunk = (lane % L::CPR) ^ L::swz(rr);
-    vo[n] = ((rr - kWaveRows * wv) * tok_elems + 8u * chunk) * uint32_t(sizeof(T));
+    vo[n] = ((rr - kWaveRows * wv) * tok_elems + 8u * chunk) * uint32_t(sizeof(CT));
   }
   // (the plan words do not change while a kernel runs: read through the
   // constant address space, the entry is a scalar load)
@@ -366,7 +406,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto wave_base = [&](uint32_t kt) { return wave_base_of(kt, wave_page(kt)); };
   auto issue_fast = [&](uint32_t kt, uint32_t wb) {
     unsigned char *stage = lds + ((kt - kt0) % kStages) * L::kStage;
-    const T *kb = kbase + wb, *vb = vbase + wb;
+    const CT *kb = kbase + wb, *vb = vbase + wb;
 #pragma unroll
     for (int n = 0; n < L::NI; ++n) {
       const uint32_t r0 = L::RPW * (L::NI * wv + n);
@@ -385,6 +425,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + r0 * L::kRowB));
       dma16(kbase + off[n], dst);
       dma16(vbase + off[n], dst + uint32_t(L::kTile));
+    }
+  };
+
+  // FP8: thread tid carries codes EPT (tid % 8) .. + EPT - 1 of row tid / 8
+  // of each key tile, K and V, staged in one of two register sets.  The
+  // loads are unconditional (a branch around them would make the compiler
+  // wait for them at its end): tiles past the last read the last tile again,
+  // rows past the end read the sequence's token 0.  Value rows no query of
+  // the block sees (past the end, or before the first query's window) are
+  // written as zeros; their keys' scores are masked.
+  constexpr uint32_t EPT = D / 8;
+  const uint32_t f_row = tid >> 3, f_col = (tid & 7u) * EPT;
+  uint4 f8k[2], f8v[2];
+  auto f8_load = [&](uint32_t kt, uint4 &rk, uint4 &rv) {
+    const uint32_t tok = (kt < n_tiles ? kt : n_tiles - 1u) * kTT + f_row;
+    const uint32_t t = tok < k_end ? tok : 0u;
+    const uint32_t lp = pow2 ? t >> ps_shift : t / ps;
+    const uint32_t slot = t - lp * ps;
+    const uint32_t pbase = lp < uint32_t(kTableCache) ? tcache[lp] : page_of(table_word(table + lp));
+    const uint32_t off = pbase + slot * tok_elems + f_col;
+    if constexpr (EPT == 16) {
+      rk = *reinterpret_cast<const uint4 *>(kbase + off);
+      rv = *reinterpret_cast<const uint4 *>(vbase + off);
+    } else {
+      const uint2 k2 = *reinterpret_cast<const uint2 *>(kbase + off);
+      const uint2 v2 = *reinterpret_cast<const uint2 *>(vbase + off);
+      rk = make_uint4(k2.x, k2.y, 0, 0);
+      rv = make_uint4(v2.x, v2.y, 0, 0);
+    }
+  };
+  // widened codes of key tile kt from a register set into ring stage `st`
+  auto f8_store = [&](uint32_t st, uint32_t kt, const uint4 &rk, const uint4 &rv) {
+    unsigned char *kr = lds + st * L::kStage + f_row * L::kRowB;
+    unsigned char *vr = kr + L::kTile;
+    const uint32_t tok = kt * kTT + f_row;
+    const bool seen = tok < k_end && tok >= lo_min;
+    const uint32_t sw = L::swz(f_row);
+    const uint32_t c0 = EPT == 16 ? 2u * (tid & 7u) : (tid & 7u);  // first 8-element chunk
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4 *>(kr + 16u * (c0 ^ sw)) = widen8<DT>(rk.x, rk.y);
+    *reinterpret_cast<uint4 *>(vr + 16u * (c0 ^ sw)) = seen ? widen8<DT>(rv.x, rv.y) : zero;
+    if constexpr (EPT == 16) {
+      *reinterpret_cast<uint4 *>(kr + 16u * ((c0 + 1u) ^ sw)) = widen8<DT>(rk.z, rk.w);
+      *reinterpret_cast<uint4 *>(vr + 16u * ((c0 + 1u) ^ sw)) = seen ? widen8<DT>(rv.z, rv.w) : zero;
     }
   };
 
@@ -416,21 +500,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  const uint32_t n_tiles = (k_end + kTT - 1) / kTT;  // key tiles kt0 .. n_tiles - 1
-  const uint32_t nt = n_tiles - kt0;                  // tiles this block walks
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(qb[ks]);
-  for (uint32_t kt = kt0; kt < n_tiles && kt < kt0 + uint32_t(kStages - 1); ++kt) {
-    if (fast_tile(kt)) {
-      issue_fast(kt, wave_base(kt));
-    } else {
-      uint32_t off[L::NI];
-      lookup(kt, off);
-      issue(kt, off);
+  uint32_t rpg = 0u;  // page of the next refill (fast path)
+  if constexpr (F8) {
+    // tiles 0 and 1 into their stages, 2 and 3 into the register sets
+    if (kt0 < n_tiles) {
+      f8_load(kt0, f8k[0], f8v[0]);
+      f8_load(kt0 + 1u, f8k[1], f8v[1]);
+      f8_store(0u, kt0, f8k[0], f8v[0]);
+      f8_store(1u, kt0 + 1u, f8k[1], f8v[1]);
+      f8_load(kt0 + 2u, f8k[0], f8v[0]);
+      f8_load(kt0 + 3u, f8k[1], f8v[1]);
     }
+  } else {
+    for (uint32_t kt = kt0; kt < n_tiles && kt < kt0 + uint32_t(kStages - 1); ++kt) {
+      if (fast_tile(kt)) {
+        issue_fast(kt, wave_base(kt));
+      } else {
+        uint32_t off[L::NI];
+        lookup(kt, off);
+        issue(kt, off);
+      }
+    }
+    rpg = fast_tile(kt0 + kStages - 1) ? wave_page(kt0 + kStages - 1) : 0u;
   }
-  // page of the next refill (fast path)
-  uint32_t rpg = fast_tile(kt0 + kStages - 1) ? wave_page(kt0 + kStages - 1) : 0u;
   // Value rows that no query of the block sees are zeroed in LDS once their
   // tile has landed (after the barrier that makes it ready), and read only
   // after one more barrier: the rows past the end of the last tile (if it is
@@ -513,13 +607,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // issued so far: tiles up to kt+2; tile kt+1 ready (after the last tile
     // the scores below read a stage whose contents are not used; in bounds,
     // no load in flight to it)
-    if (j + 1 < nt) {
+    // (FP8: stage of tile kt+1 written by the step before)
+    if constexpr (F8) {
+      if (j + 1 < nt) block_sync_lds();
+    } else if (j + 1 < nt) {
       ready(j + 2 < nt ? 1u : 0u);
       if (tail_r0 != 0u && j + 2 == nt) zero_rows(j + 1, tail_r0, kTT);
     } else if (tail_r0 != 0u && nt > 1) {
       block_sync_lds();  // the zeroed rows of the last tile are visible
     }
-    const bool refill = kt + kStages - 1 < n_tiles;
+    const bool refill = !F8 && kt + kStages - 1 < n_tiles;
     const bool rfast = refill && fast_tile(kt + kStages - 1);
     uint32_t roff[L::NI];
     if (refill && !rfast) lookup(kt + kStages - 1, roff);
@@ -593,22 +690,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       o[b] = M::mma(vb[j % (kAhead + 1)], make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]), o[b]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // refill the stage of tile kt-1 (every wave passed this step's barrier,
-    // so none still reads it)
-    if (rfast) issue_fast(kt + kStages - 1, wave_base_of(kt + kStages - 1, rpg));
-    else if (refill) issue(kt + kStages - 1, roff);
-    // page of the next step's refill: its scalar read completes by that
-    // step's barrier
-    rpg = fast_tile(kt + kStages) ? wave_page(kt + kStages) : 0u;
+    if constexpr (F8) {
+      // tile kt+2 from its register set into the stage of tile kt-2 (every
+      // wave passed this step's barrier, so none still reads it), then tile
+      // kt+4 into that register set
+      constexpr int RS = ST % 2;
+      if (j + 2 < nt) f8_store((ST + 2) % kStages, kt + 2u, f8k[RS], f8v[RS]);
+      f8_load(kt + 4u, f8k[RS], f8v[RS]);
+    } else {
+      // refill the stage of tile kt-1 (every wave passed this step's
+      // barrier, so none still reads it)
+      if (rfast) issue_fast(kt + kStages - 1, wave_base_of(kt + kStages - 1, rpg));
+      else if (refill) issue(kt + kStages - 1, roff);
+      // page of the next step's refill: its scalar read completes by that
+      // step's barrier
+      rpg = fast_tile(kt + kStages) ? wave_page(kt + kStages) : 0u;
+    }
   };
 
   f32x16_t sa, sb;
   if (nt) {
-    ready(nt - 1 < 2u ? nt - 1 : 2u);
-    const bool tail0 = tail_r0 != 0u && nt == 1;
-    if (head_r1 != 0u) zero_rows(0, 0u, head_r1);
-    if (tail0) zero_rows(0, tail_r0, kTT);
-    if (head_r1 != 0u || tail0) block_sync_lds();
+    if constexpr (F8) {
+      block_sync_lds();
+    } else {
+      ready(nt - 1 < 2u ? nt - 1 : 2u);
+      const bool tail0 = tail_r0 != 0u && nt == 1;
+      if (head_r1 != 0u) zero_rows(0, 0u, head_r1);
+      if (tail0) zero_rows(0, tail_r0, kTT);
+      if (head_r1 != 0u || tail0) block_sync_lds();
+    }
     sa = scores(lds);
   }
   // whole groups of four tiles (ring stages 0..3 in order), then the rest
@@ -622,12 +732,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (n4 < nt) step(IC<0>(), n4, sa, sb);
   if (n4 + 1 < nt) step(IC<1>(), n4 + 1, sb, sa);
   if (n4 + 2 < nt) step(IC<2>(), n4 + 2, sa, sb);
+  if constexpr (F8) wait_vm<0>();  // the register loads past the last tile
 
   // normalise and write: lane holds O^T[d = 32mb + 8i + 4hf + e][q-row c32]
   const float l_tot = halves_sum(lsum);
   if (!row_ok) return;
   T *out = static_cast<T *>(a.out) + (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (F8 ? a.v_scale : 1.f) / l_tot : 0.f;
 #pragma unroll
   for (int b = 0; b < MB; ++b)
 #pragma unroll
@@ -661,12 +772,21 @@ hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st) {
   if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<uint32_t>(blocks));
   const uint32_t ng = uint32_t(n_groups);
-  if (dt == PKV_BF16) {
-    if (a.d == 64) launch_k((prefill_kernel<BF16, 64>), grid, dim3(256), 0, st, a, n_sub, ng);
-    else launch_k((prefill_kernel<BF16, 128>), grid, dim3(256), 0, st, a, n_sub, ng);
+  const bool d64 = a.d == 64;
+  if (a.kv_fp8) {
+    if (dt == PKV_BF16) {
+      if (d64) launch_k((prefill_kernel<BF16, 64, true>), grid, dim3(256), 0, st, a, n_sub, ng);
+      else launch_k((prefill_kernel<BF16, 128, true>), grid, dim3(256), 0, st, a, n_sub, ng);
+    } else {
+      if (d64) launch_k((prefill_kernel<F16, 64, true>), grid, dim3(256), 0, st, a, n_sub, ng);
+      else launch_k((prefill_kernel<F16, 128, true>), grid, dim3(256), 0, st, a, n_sub, ng);
+    }
+  } else if (dt == PKV_BF16) {
+    if (d64) launch_k((prefill_kernel<BF16, 64, false>), grid, dim3(256), 0, st, a, n_sub, ng);
+    else launch_k((prefill_kernel<BF16, 128, false>), grid, dim3(256), 0, st, a, n_sub, ng);
   } else {
-    if (a.d == 64) launch_k((prefill_kernel<F16, 64>), grid, dim3(256), 0, st, a, n_sub, ng);
-    else launch_k((prefill_kernel<F16, 128>), grid, dim3(256), 0, st, a, n_sub, ng);
+    if (d64) launch_k((prefill_kernel<F16, 64, false>), grid, dim3(256), 0, st, a, n_sub, ng);
+    else launch_k((prefill_kernel<F16, 128, false>), grid, dim3(256), 0, st, a, n_sub, ng);
   }
   return hipGetLastError();
 }

@@ -1,8 +1,8 @@
 """GPU parity of attention over an FP8 E4M3 cache (pkv_attention_fp8)
 against the oracle's decoded-cache attention: every finite code through the
 kernel's widening (bit for bit), head dims, GQA groups, page sizes,
-unsplit / split / balanced, a window, chunk queries (run as rows) and the
-argument errors (the decode workload at full size is checked in
+unsplit / split / balanced, a window, chunk queries on the tile kernel (with
+and without a window) and the argument errors (the decode workload at full size is checked in
 test_gpu_full_size.py)."""
 
 import numpy as np
@@ -81,19 +81,77 @@ def test_fp8_page_sizes_splits(ps, splits):
                  torch.bfloat16, f"fp8 window ps={ps} splits={splits}")
 
 
-def test_fp8_chunk_queries_run_as_rows():
-    chunks = [(77, 150), (0, 20)]
-    dec = [33, 300]
-    lens = [p + c for p, c in chunks] + dec
+def _chunk_workload(dtype, g, d, ps, causal, seed, chunks=((77, 150), (0, 20), (1500, 200)),
+                    dec=(33, 300)):
+    lens = [p + c for p, c in chunks] + list(dec)
     queries = []
     for s, (p, c) in enumerate(chunks):
         queries += [(s, p + j) for j in range(c)]
     queries += [(len(chunks) + j, L - 1) for j, L in enumerate(dec)]
-    wl = build_attention("f8", 4200, torch.bfloat16, lens, queries, 16, 4, 128, 128, 16,
-                         poison=True)
+    return build_attention("f8", seed, dtype, lens, queries, 2 * g, 2, d, d, ps, causal=causal,
+                           poison=True)
+
+
+def _poison_before_windows(wl, k8, v8, window):
+    """E4M3 NaN (0x7F) in every cache slot in front of a sequence's earliest
+    window start (the slots past its length already hold NaN)."""
+    for s in range(wl.sequences):
+        qs = np.flatnonzero(wl.qseq == s)
+        if qs.size == 0:
+            continue
+        starts = [oracle.window_start(oracle.visible_count(wl.lens, wl.qseq, wl.qpos, int(i), wl.causal),
+                                      window) for i in qs]
+        for t in range(min(starts)):
+            page, slot = int(wl.table[s, t // wl.page_size]), t % wl.page_size
+            k8[page, slot] = 0x7F
+            v8[page, slot] = 0x7F
+
+
+def _run_on_tiles(wl, k8, v8, splits, window=0):
+    """Library output, asserting that the chunk queries ran on the tile kernel."""
+    plan = make_plan(wl)
+    assert plan.n_tiles > 0
+    plan.timing(True, kernels=["tiles"])
+    got = _run(wl, k8, v8, splits=splits, window=window, plan=plan)
+    assert plan.timing_read("tiles")[0] == 1, "chunk queries did not run on the tile kernel"
+    return got
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("g,d,ps", [(4, 128, 16), (1, 128, 16), (8, 64, 16), (4, 128, 5), (4, 64, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_chunk_queries_on_tiles(dtype, g, d, ps, causal):
+    """Chunk queries over an FP8 cache run on the tile kernel (codes widened
+    in registers): ragged key tails, a chunk behind a long prior, decode rows
+    alongside, unsplit and balanced."""
+    wl = _chunk_workload(dtype, g, d, ps, causal, seed=4200 + g + d + ps)
     k8, v8 = fp8_caches(wl, KS, VS)
+    want = _want(wl, k8, v8)
     for splits in (1, 0):
-        assert_close(_run(wl, k8, v8, splits=splits), _want(wl, k8, v8), torch.bfloat16, "chunks")
+        assert_close(_run_on_tiles(wl, k8, v8, splits), want, dtype,
+                     f"fp8 chunks g={g} d={d} ps={ps} causal={causal} splits={splits}")
+
+
+@pytest.mark.parametrize("g,d,ps", [(4, 128, 16), (8, 64, 16), (4, 128, 5)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_chunk_queries_window_on_tiles(g, d, ps, causal):
+    """FP8 chunk queries under a sliding window on the tile kernel, with E4M3
+    NaN in front of every window."""
+    for w, splits in ((1, 1), (45, 0), (300, 1), (5000, 0)):
+        wl = _chunk_workload(torch.bfloat16, g, d, ps, causal, seed=4250 + g + d + ps + w)
+        k8, v8 = fp8_caches(wl, KS, VS)
+        _poison_before_windows(wl, k8, v8, w)
+        assert_close(_run_on_tiles(wl, k8, v8, splits, window=w), _want(wl, k8, v8, window=w),
+                     torch.bfloat16, f"fp8 chunk window {w} g={g} d={d} ps={ps} causal={causal}")
+
+
+def test_fp8_chunk_behind_long_table():
+    """A chunk whose keys span more block-table entries than the kernel keeps
+    in LDS (16600 prior tokens, 16-token pages)."""
+    wl = _chunk_workload(torch.bfloat16, 4, 128, 16, True, seed=4290, chunks=((16600, 45),),
+                         dec=(5,))
+    k8, v8 = fp8_caches(wl, KS, VS)
+    assert_close(_run_on_tiles(wl, k8, v8, 1), _want(wl, k8, v8), torch.bfloat16, "fp8 long table")
 
 
 def test_fp8_argument_errors():
