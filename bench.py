@@ -89,7 +89,18 @@ def _parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--copy-probe", action="store_true")
-    return p.parse_args()
+    p.add_argument("--legs", default="all",
+                   help="comma-separated extra legs to run (" + ",".join(LEGS) + "), or all")
+    args = p.parse_args()
+    args.legs = set(LEGS) if args.legs == "all" else set(x for x in args.legs.split(",") if x)
+    unknown = args.legs - set(LEGS)
+    if unknown:
+        raise SystemExit(f"unknown legs: {sorted(unknown)}")
+    return args
+
+
+LEGS = ("prefill", "prefill_window", "prefill_fp8", "append", "window", "fp8", "decode_step",
+        "f32_decode", "long_decode", "mla")
 
 
 def _fixed_splits(arg: str) -> int:
@@ -347,7 +358,9 @@ def decode_step_measure(torch, pkv, workloads, steps: int):
     """A captured decode step on the packed-decode workload: one graph holds
     the append of every sequence's new K/V row at its own position and the
     attention over the grown caches (balanced schedule).  Reported: the
-    replay time per step, the same calls launched eagerly, and the step's
+    replay time per step, the same calls launched eagerly, the per-step
+    time of a graph holding two steps (what one launch costs shows as the
+    difference), and the step's
     bytes (K/V rows read by the attention, plus the append's reads and
     writes) per replay time against the HBM peak."""
     wl = workloads.config(2)
@@ -382,12 +395,20 @@ def decode_step_measure(torch, pkv, workloads, steps: int):
         with torch.cuda.graph(g, stream=s):
             step()
         graph_us = timed(g.replay)
+        # the same step captured twice into one graph: per-step time when
+        # one launch carries two steps
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=s):
+            step()
+            step()
+        graph2_us = timed(g2.replay) / 2
     nbytes = workloads.attention_bytes(wl) + 2 * (nk.numel() + nv.numel()) * nk.element_size()
     gbs = nbytes / (graph_us * 1e-6) / 1e9
     return {"value": round(gbs, 1), "unit": "GB/s", "peak": HBM_PEAK_GBS,
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "kernel": "captured decode step: cache append + split-KV decode + merge",
             "graph_us": round(graph_us, 2), "eager_us": round(eager_us, 2),
+            "graph_two_steps_per_launch_us": round(graph2_us, 2),
             "bytes_per_step": nbytes, "workload": f"{wl.name}, one new token per sequence"}
 
 
@@ -599,17 +620,21 @@ def main():
         "kernel_breakdown": kernels,
     }
     if not args.no_prefill and wl.kind == "attention":
-        line["prefill"] = prefill_measure(torch, pkv, workloads, args.prefill_steps)
-        line["prefill_window"] = prefill_measure(torch, pkv, workloads, args.prefill_steps, window=1024)
-        line["prefill_fp8"] = prefill_measure(torch, pkv, workloads, args.prefill_steps, fp8=(0.05, 0.04))
-        line["append"] = append_measure(torch, pkv, workloads, args.prefill_steps)
-        line["window"] = window_measure(torch, pkv, workloads, args.prefill_steps)
-        line["fp8"] = fp8_measure(torch, pkv, workloads, args.prefill_steps)
-        line["decode_step"] = decode_step_measure(torch, pkv, workloads, args.prefill_steps)
+        ps, legs = args.prefill_steps, args.legs
+        runs = (("prefill", lambda: prefill_measure(torch, pkv, workloads, ps)),
+                ("prefill_window", lambda: prefill_measure(torch, pkv, workloads, ps, window=1024)),
+                ("prefill_fp8", lambda: prefill_measure(torch, pkv, workloads, ps, fp8=(0.05, 0.04))),
+                ("append", lambda: append_measure(torch, pkv, workloads, ps)),
+                ("window", lambda: window_measure(torch, pkv, workloads, ps)),
+                ("fp8", lambda: fp8_measure(torch, pkv, workloads, ps)),
+                ("decode_step", lambda: decode_step_measure(torch, pkv, workloads, ps)))
+        for name, run in runs:
+            if name in legs:
+                line[name] = run()
         # the other workloads, each as a leg of its own (never the one timed above)
         for name, n in (("f32_decode", 1), ("long_decode", 3), ("mla", 5)):
-            if n != args.workload:
-                line[name] = workload_leg(torch, pkv, workloads, n, args.prefill_steps)
+            if n != args.workload and name in legs:
+                line[name] = workload_leg(torch, pkv, workloads, n, ps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
