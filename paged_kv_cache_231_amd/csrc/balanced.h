@@ -31,12 +31,17 @@ __device__ __forceinline__ uint32_t row_tiles(const RowArgs &a, uint32_t r) {
   return ceil_div_u(n, TT) - window_lo(n, a.window) / TT;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= uint32_t(o)) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes of a full wave, on DPP: shifts by
+// 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside
+// the row add 0), then the last lane of row 0 added to row 1 and of row 2
+// to row 3, then lane 31 added to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 
@@ -86,20 +91,55 @@ __device__ __forceinline__ bool find_range(Range &rg, const RowArgs &a, uint32_t
   // Total tiles T and the super-chunk of row queries holding this group's
   // first tile: chunks of 64 queries (coalesced loads, one wave sum each);
   // lane l adds up chunks l*m .. l*m + m - 1.
+  // The tile counts of kBatch chunks are loaded together, each level of
+  // the plan-word indirection (row list, query words, sequence length) for
+  // all of them at once with no branch between the loads; rows past the end
+  // read the last row and count 0.
+  constexpr uint32_t kBatch = 8;
   const uint32_t nch = (R + 63u) / 64u;
   const uint32_t m = (nch + 63u) / 64u;
+  const uint64_t reach = uint64_t(a.plan.W) * a.plan.ps;
+  const uint32_t *words = a.plan.words;
   uint32_t s = 0, carry = 0;
-  for (uint32_t c = 0; c < nch; ++c) {
-    const uint32_t r = c * 64u + lane;
-    const uint32_t v = r < R ? row_tiles<TT>(a, r) : 0u;
-    const uint32_t x = wave_incl_scan(v, lane);
-    const uint32_t tot = __builtin_amdgcn_readlane(x, 63);
-    if (c / m == lane) s += tot;
-    if (record && r < R) {
-      a.bal_rec[2u * r] = carry + x - v;
-      a.bal_rec[2u * r + 1u] = v;
+  for (uint32_t c0 = 0; c0 < nch; c0 += kBatch) {
+    uint32_t vb[kBatch], qi[kBatch], sq[kBatch], pq[kBatch];
+#pragma unroll
+    for (uint32_t b = 0; b < kBatch; ++b) {
+      const uint32_t r = (c0 + b) * 64u + lane;
+      qi[b] = r < R ? r : R - 1u;
     }
-    carry += tot;
+    if (a.qlist) {
+#pragma unroll
+      for (uint32_t b = 0; b < kBatch; ++b) qi[b] = a.qlist[qi[b]];
+    }
+#pragma unroll
+    for (uint32_t b = 0; b < kBatch; ++b) {
+      sq[b] = words[a.plan.qseq + qi[b]];
+      pq[b] = words[a.plan.qpos + qi[b]];
+    }
+#pragma unroll
+    for (uint32_t b = 0; b < kBatch; ++b) {
+      const uint32_t len = words[a.plan.lens + sq[b]];
+      uint64_t n = a.causal ? uint64_t(pq[b]) + 1u : uint64_t(len);
+      if (n > reach) n = reach;
+      const uint32_t t = ceil_div_u(uint32_t(n), TT) - window_lo(uint32_t(n), a.window) / TT;
+      vb[b] = (c0 + b) * 64u + lane < R ? t : 0u;
+    }
+#pragma unroll
+    for (uint32_t b = 0; b < kBatch; ++b) {
+      const uint32_t c = c0 + b;
+      if (c >= nch) break;
+      const uint32_t r = c * 64u + lane;
+      const uint32_t v = vb[b];
+      const uint32_t x = wave_incl_scan(v, lane);
+      const uint32_t tot = __builtin_amdgcn_readlane(x, 63);
+      if (c / m == lane) s += tot;
+      if (record && r < R) {
+        a.bal_rec[2u * r] = carry + x - v;
+        a.bal_rec[2u * r + 1u] = v;
+      }
+      carry += tot;
+    }
   }
   const uint32_t sx = wave_incl_scan(s, lane);
   const uint32_t T = __builtin_amdgcn_readlane(sx, 63);
