@@ -8,15 +8,17 @@
 //   O^T[rank x heads]  += latent^T . P^T                        (token-deep)
 // A block owns one (query, split part, 64-head group) in the split grid, or
 // one equal range of the queries' 32-token tiles and a 64-head group in the
-// balanced grid (pieces of several queries in turn); its four waves (one
-// per SIMD) own 16 heads each, with the 512 x 16 f32 output tile in VGPRs
-// and the loop-invariant query operands in AGPRs (MFMA reads them there).
-// Latent and k_pos rows travel HBM -> LDS directly into a four-stage ring
-// (three 32-token tiles ahead); the latent is read from LDS as the A operand
-// of q.k and, transposed, as the A operand of the value product (16x16x32
-// with 32 tokens per step).  The online softmax is kept in base 2 with lazy
-// rescaling.  Split parts, and balanced pieces cut by a range boundary,
-// write f32 partials that a merge kernel combines.
+// balanced grid (pieces of several queries in turn).  Its eight waves (two
+// per SIMD) take two roles: four score waves (16 heads each: scores, online
+// softmax, probabilities into LDS) work on tile kt while four value waves
+// (128 output dims of all 64 heads each, the 128 x 64 f32 tile in VGPRs)
+// accumulate tile kt - 1, so on every SIMD one wave's softmax arithmetic
+// runs under the other's matrix instructions.  Latent and k_pos rows travel
+// HBM -> LDS directly into a four-stage ring; the latent is read from LDS as
+// the A operand of q.k and, transposed, as the A operand of the value
+// product (16x16x32 with 32 tokens per step).  The online softmax is kept in
+// base 2 with lazy rescaling.  Split parts, and balanced pieces cut by a
+// range boundary, write f32 partials that a merge kernel combines.
 
 #include "balanced.h"
 #include "mfma_common.h"
@@ -25,8 +27,10 @@ namespace pkv {
 
 namespace {
 
-constexpr int kWaves = 4;          // one wave per SIMD
-constexpr int kHeadsPerBlock = kWaves * 16;
+constexpr int kWaves = 8;          // two per SIMD: four score waves, four value waves
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRoleWaves = 4;      // waves per role
+constexpr int kHeadsPerBlock = kRoleWaves * 16;
 static_assert(kHeadsPerBlock == int(kMlaBlockHeads), "slot rows per block of the balanced merge");
 constexpr int kTT = 32;            // tokens per tile (two 16-row M-tiles)
 constexpr int kStages = 4;         // LDS ring stages
@@ -94,28 +98,42 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // One piece of work for the whole block: query i (sequence seq), tokens
-// [t_lo, t_hi), this wave's 16 heads from h0.  The result goes to the output
-// rows of the query (direct) or, normalised with its base-2 lse, to f32
-// rows row0 + c16 of ws_o / ws_lse.  Every wave of the block calls it with
-// the same query and tokens; it starts by rewriting the table cache and the
+// [t_lo, t_hi), the block's 64 heads from hb.  The result goes to the output
+// rows of the query (direct) or, normalised with its base-2 lse, to f32 rows
+// row_base + (head - hb) of ws_o / ws_lse.  Every wave of the block calls it
+// with the same arguments; it starts by rewriting the table cache and the
 // ring, so a caller running pieces back to back passes a block barrier
 // first.
+//
+// Schedule.  Barrier B_k (k = 0 .. n) opens interval k, in which score
+// waves process tile k (k < n) into probability buffer k % 2 and value
+// waves accumulate tile k - 1 (k >= 1) from buffer (k - 1) % 2; every wave
+// issues its share of tile k + 2's DMA into the stage tile k - 2 used, and
+// before B_{k+1} waits for its share of tile k + 1.  One more interval
+// hands the denominators to the value waves.
 template <class DT, int R, int P>
 __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t seq, uint32_t t_lo,
-                                          uint32_t t_hi, uint32_t h0, bool direct, uint64_t row0) {
+                                          uint32_t t_hi, uint32_t hb, bool direct, uint64_t row_base) {
   using M = Mfma<DT>;
   using L = MLds<R, P>;
   using T = typename DT::T;
-  constexpr int KS = R / 32;   // q.k steps over the latent (16)
-  constexpr int KP = P / 32;   // q.k steps over the position part (2)
-  constexpr int DB = R / 16;   // 16-wide output blocks (32)
+  constexpr int KS = R / 32;                  // q.k steps over the latent (16)
+  constexpr int KP = P / 32;                  // q.k steps over the position part (2)
+  constexpr int MBW = R / 16 / kRoleWaves;    // 16-dim output blocks per value wave (8)
+  constexpr int NBW = kHeadsPerBlock / 16;    // 16-head column blocks (4)
+  constexpr int kPRow = 2 * kTT + 16;         // bytes per head row of P (32 bf16 + 16 pad)
   constexpr int kLoads = L::kLatPerWave + 1;  // DMA instructions per wave per tile
   __shared__ __align__(1024) unsigned char lds[L::kBytes];
   __shared__ uint32_t tcache[kTableCache];
+  __shared__ __align__(16) unsigned char pl[2][kHeadsPerBlock * kPRow];
+  __shared__ float pal[2][kHeadsPerBlock];    // per head: rescale factor of the tile
+  __shared__ float fin[2][kHeadsPerBlock];    // per head: final reference and denominator
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t c16 = lane & 15u, j = lane >> 4;
+  const bool scorer = wv < uint32_t(kRoleWaves);
+  const uint32_t rw = scorer ? wv : wv - uint32_t(kRoleWaves);  // index within the role
   const uint32_t ps = a.plan.ps;
   const bool pow2 = (ps & (ps - 1)) == 0;
   const uint32_t ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 0u;
@@ -128,50 +146,29 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
   const uint32_t lp_end = t_hi > t_lo ? page_of(t_hi - 1) + 1 : 0u;
   uint32_t wb = page_of(t_lo);
   auto fill_window = [&]() {
-    for (uint32_t e = tid; e < uint32_t(kTableCache) && wb + e < lp_end; e += 256) {
+    for (uint32_t e = tid; e < uint32_t(kTableCache) && wb + e < lp_end; e += kThreads) {
       const uint32_t pg = table[wb + e];
       tcache[e] = pg < a.plan.N ? pg : 0u;  // never read outside the pool
     }
   };
   fill_window();
 
-  // this wave's heads: column c16 -> head h0 + c16; columns of heads past hq
-  // compute on head 0's query and are not stored
-  uint4 qa[KS], qp[KP];
-  {
-    const uint32_t h = h0 + c16;
-    const uint64_t row = uint64_t(i) * a.hq + (h < a.hq ? h : 0u);
-    const T *qrow = static_cast<const T *>(a.q) + row * R;
-    const T *prow = static_cast<const T *>(a.qp) + row * P;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j));
-#pragma unroll
-    for (int ks = 0; ks < KP; ++ks) qp[ks] = *reinterpret_cast<const uint4 *>(prow + 8 * (4 * ks + j));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) to_agpr(qa[ks]);
-#pragma unroll
-    for (int ks = 0; ks < KP; ++ks) to_agpr(qp[ks]);
-  }
-  f32x4_t o[DB];
-#pragma unroll
-  for (int b = 0; b < DB; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kNoMax, lsum = 0.f;
   const float sl2 = a.scale_log2;
   const T *lat = static_cast<const T *>(a.k);
   const T *kpos = static_cast<const T *>(a.kp);
   __syncthreads();  // table cache ready
 
-  // DMA of tile kt: wave wv loads latent rows 8wv .. 8wv+7 (one whole row
+  // DMA of tile kt: wave wv loads latent rows 4wv .. 4wv+3 (one whole row
   // per instruction: uniform row base, per-lane chunk offset) and position
-  // rows 8wv .. 8wv+7 (one instruction, lane l row 8wv + l/8).  Lane l
-  // locates row 8wv + l/8; the latent loads take the page and slot of lanes
-  // 0, 8, .., 56.  Rows past the end read row 0 of page 0; their latent is
-  // zeroed before use.
+  // rows 4wv .. 4wv+3 (one instruction, lanes 0..31, lane l row 4wv + l/8).
+  // Lane l locates row 4wv + (l/8 mod 4); the latent loads take the page and
+  // slot of lanes 0, 8, 16, 24.  Rows past the end read row 0 of page 0;
+  // their latent is zeroed before the value product.
   uint32_t lat_voff[L::kLatPerWave];  // byte offset of the chunk lane l fetches
 #pragma unroll
   for (int n2 = 0; n2 < L::kLatPerWave; ++n2)
     lat_voff[n2] = 16u * L::lat_slot(lane, wv * uint32_t(L::kLatPerWave) + n2);
-  const uint32_t pos_r = wv * uint32_t(L::kLatPerWave) + (lane >> 3);
+  const uint32_t pos_r = wv * uint32_t(L::kLatPerWave) + ((lane >> 3) & 3u);
   const uint32_t pos_voff = 16u * L::pos_slot(lane % L::kPosCPR, pos_r);
   auto issue = [&](uint32_t kt) {
     unsigned char *stage = lds + (kt % kStages) * L::kStage;
@@ -190,10 +187,12 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
       dma16_s(row, lat_voff[n2], __builtin_amdgcn_readfirstlane(lds_addr(stage + rr * L::kLatRow)));
     }
     const uint32_t off = page * uint32_t(a.kp_page) + slot * uint32_t(a.kp_tok);
-    dma16(reinterpret_cast<const unsigned char *>(kpos + off) + pos_voff,
-          __builtin_amdgcn_readfirstlane(lds_addr(stage + L::kLat + 8u * wv * L::kPosRow)));
+    if (lane < 32u)
+      dma16(reinterpret_cast<const unsigned char *>(kpos + off) + pos_voff,
+            __builtin_amdgcn_readfirstlane(lds_addr(stage + L::kLat + 4u * wv * L::kPosRow)));
   };
-  // before issuing tile kt: move the table window if the tile reaches past it
+  // before issuing tile kt: move the table window if the tile reaches past
+  // it (every wave calls this at the same point of an interval)
   auto window_for = [&](uint32_t kt) {
     const uint32_t t0 = t_lo + kt * kTT;
     const uint32_t last = (t0 + kTT < t_hi ? t0 + kTT : t_hi) - 1u;
@@ -205,198 +204,261 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
     }
   };
 
-  // Per-lane LDS read offsets.  The swizzle only permutes 16-byte chunks
-  // inside a 256-byte segment of a row, so each read is a per-lane base plus
-  // an immediate segment offset.
-  //   q.k:  lane (j, c16) reads chunk 4ks + j of row c16 (+16 for M-tile 1):
-  //         segment ks >> 2, in-segment slot (4 (ks & 3) + j) ^ c16
-  //   pos:  chunk 4ks + j of position row c16 (+16)
-  //   V^T:  a transposed read gives lane (j, i) dim 16b + i of four rows,
-  //         supplied by the group's lanes: lane (j, c16) supplies row
-  //         pv_row(j, c16 >> 2) (+16 for the second read), dims 16b +
-  //         4 (c16 & 3) .. +3, i.e. chunk 2b + ((c16 & 3) >> 1), half c16 & 1.
-  //         pv_row(j, e) = 4 (j & 1) + (j >> 1) + 2 (e & 1) + 8 (e >> 1): the
-  //         rows of lanes 0..31 are 0,2,4,..,14, those of lanes 32..63 the
-  //         odd rows, one row of each slot pair per LDS cycle.
+  // Token order.  The value product's K slots of lane group j are the rows
+  // pv_row(j, 0..3) of the tile, then the same rows + 16 (the order that
+  // keeps its transposed reads free of bank conflicts, see below).  The
+  // score product's A row m of M-tile mt is token 16 mt + pv_row(m >> 2,
+  // m & 3), so a score lane (c16, j) ends up holding the probabilities of K
+  // slots 8j .. 8j+7 of the value product: one 16-byte store into P.
+  //   pv_row(j, e) = 4 (j & 1) + (j >> 1) + 2 (e & 1) + 8 (e >> 1): the rows
+  //   of lanes 0..31 are 0,2,4,..,14, those of lanes 32..63 the odd rows,
+  //   one row of each slot pair per LDS cycle.
+  auto pv_row_of = [](uint32_t jj, uint32_t e) {
+    return 4u * (jj & 1u) + (jj >> 1) + 2u * (e & 1u) + 8u * (e >> 1);
+  };
+  // q.k: lane (j, c16) reads chunk 4ks + j of token row qr + 16 mt (the
+  // swizzle permutes chunks inside 256-byte segments: a per-lane base plus
+  // an immediate segment offset); position rows likewise.
+  const uint32_t qr = pv_row_of(c16 >> 2, c16 & 3u);
   uint32_t qk_off[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) qk_off[u] = c16 * L::kLatRow + 16u * ((4u * u + j) ^ c16);
+  for (int u = 0; u < 4; ++u) qk_off[u] = qr * L::kLatRow + 16u * ((4u * u + j) ^ qr);
   uint32_t pos_off[KP];
 #pragma unroll
-  for (int ks = 0; ks < KP; ++ks) pos_off[ks] = c16 * L::kPosRow + 16u * L::pos_slot(4u * ks + j, c16);
+  for (int ks = 0; ks < KP; ++ks) pos_off[ks] = qr * L::kPosRow + 16u * L::pos_slot(4u * ks + j, qr);
+  // V^T: a transposed read gives lane (j, i) dim 16b + i of four rows,
+  // supplied by the group's lanes: lane (j, c16) supplies row pv_row(j,
+  // c16 >> 2) (+16 for the second read), dims 16b + 4 (c16 & 3) .. +3, i.e.
+  // chunk 2b + ((c16 & 3) >> 1), half c16 & 1; a value wave's blocks are
+  // b = 8 rw + mb.
   const uint32_t e4 = c16 >> 2, q4 = c16 & 3u;
-  const uint32_t pv_row = 4u * (j & 1u) + (j >> 1) + 2u * (e4 & 1u) + 8u * (e4 >> 1);
-  uint32_t pv_off[8];
+  const uint32_t pv_row = pv_row_of(j, e4);
+  uint32_t pv_off[MBW];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    pv_off[u] = pv_row * L::kLatRow + 8u * (q4 & 1u) + 16u * ((2u * u + (q4 >> 1)) ^ pv_row);
+  for (int mb = 0; mb < MBW; ++mb)
+    pv_off[mb] = pv_row * L::kLatRow + 8u * (q4 & 1u) + 16u * ((2u * mb + (q4 >> 1)) ^ pv_row) + 256u * rw;
 
   const uint32_t n_tiles = t_hi > t_lo ? (t_hi - t_lo + kTT - 1) / kTT : 0u;
-  for (uint32_t kt = 0; kt < n_tiles && kt < uint32_t(kStages - 1); ++kt) {
-    window_for(kt);
-    issue(kt);
+  // the interval skeleton shared by both roles (same barriers in every wave)
+  auto prologue = [&]() {
+    if (n_tiles > 0u) issue(0);
+    if (n_tiles > 1u) {
+      window_for(1);
+      issue(1);
+    }
+    if (n_tiles > 1u) wait_vm<kLoads>();
+    else wait_vm<0>();
+    block_sync_lds();  // B_0: tile 0 ready
+  };
+  auto interval_head = [&](uint32_t k) {
+    if (k + 2 < n_tiles) {
+      window_for(k + 2);
+      issue(k + 2);
+    }
+  };
+  auto interval_tail = [&](uint32_t k) {
+    // this wave's share of tile k + 1 has landed (tile k + 2's may not)
+    if (k + 2 < n_tiles) wait_vm<kLoads>();
+    else wait_vm<0>();
+    block_sync_lds();  // B_{k+1}
+  };
+
+  if (scorer) {
+    // Score waves: column c16 is head hb + 16 rw + c16 (heads past hq
+    // compute on head 0's query and are never stored).
+    uint4 qa[KS], qp[KP];
+    {
+      const uint32_t h = hb + 16u * rw + c16;
+      const uint64_t row = uint64_t(i) * a.hq + (h < a.hq ? h : 0u);
+      const T *qrow = static_cast<const T *>(a.q) + row * R;
+      const T *prow = static_cast<const T *>(a.qp) + row * P;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const uint4 *>(qrow + 8 * (4 * ks + j));
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks) qp[ks] = *reinterpret_cast<const uint4 *>(prow + 8 * (4 * ks + j));
+      // finish these loads here: a wait the compiler placed at their first
+      // use would also drain the ring's DMA loads
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qa[ks].x), "v"(qa[ks].y), "v"(qa[ks].z), "v"(qa[ks].w));
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks) asm volatile("" ::"v"(qp[ks].x), "v"(qp[ks].y), "v"(qp[ks].z), "v"(qp[ks].w));
+    }
+    float m = kNoMax, lsum = 0.f;  // the head's reference (base 2), this lane's share of l
+    prologue();
+    for (uint32_t k = 0; k <= n_tiles; ++k) {
+      interval_head(k);
+      if (k < n_tiles) {
+        const uint32_t t0 = t_lo + k * kTT;
+        const unsigned char *st_lat = lds + (k % kStages) * L::kStage;
+        const unsigned char *st_pos = st_lat + L::kLat;
+        // S^T: both M-tiles (tokens 16 mt + pv_row order) of this wave's
+        // 16 heads, two accumulators each; read r (k-step r / 2, M-tile
+        // r % 2) is issued kAhead reads ahead and the order is fenced.
+        f32x4_t acc[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        {
+          constexpr int kReads = 2 * (KS + KP), kAhead = 6;
+          auto load_a = [&](int r) -> uint4 {
+            const int ks = r >> 1, mt = r & 1;
+            if (ks < KS)
+              return *reinterpret_cast<const uint4 *>(st_lat + mt * (16 * L::kLatRow) + qk_off[ks & 3] +
+                                                      256 * (ks >> 2));
+            return *reinterpret_cast<const uint4 *>(st_pos + mt * (16 * L::kPosRow) + pos_off[ks - KS]);
+          };
+          uint4 ka[kAhead + 1];
+#pragma unroll
+          for (int r = 0; r < kAhead; ++r) ka[r] = load_a(r);
+#pragma unroll
+          for (int r = 0; r < kReads; ++r) {
+            if (r + kAhead < kReads) ka[(r + kAhead) % (kAhead + 1)] = load_a(r + kAhead);
+            const int ks = r >> 1, mt = r & 1;
+            acc[mt][ks & 1] = M::qk(ka[r % (kAhead + 1)], ks < KS ? qa[ks] : qp[ks - KS], acc[mt][ks & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // lane (j, c16) holds tokens 16 mt + pv_row(j, e) of head 16 rw +
+        // c16: masked past the end, scaled to base 2
+        float x[2][4];
+        float lmx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool vis = t0 + 16u * mt + pv_row_of(j, uint32_t(e)) < t_hi;
+            x[mt][e] = vis ? (acc[mt][0][e] + acc[mt][1][e]) * sl2 : -INFINITY;
+            lmx = fmaxf(lmx, x[mt][e]);
+          }
+        // Lazy rescaling: the reference moves only when the head's tile max
+        // passes it by more than kSlack, so probabilities stay below
+        // 2^kSlack; the factor goes to the value waves with the
+        // probabilities.
+        const float tm = rows4_max(lmx);
+        float alpha = 1.f;
+        if (tm > m + kSlack) {
+          alpha = fast_exp2(m - tm);
+          m = tm;
+          lsum *= alpha;
+        }
+        float pr[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pr[mt][e] = fast_exp2(x[mt][e] - m);
+        lsum += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
+        *reinterpret_cast<uint4 *>(&pl[k & 1u][(16u * rw + c16) * kPRow + 16u * j]) =
+            make_uint4(M::pack2(pr[0][0], pr[0][1]), M::pack2(pr[0][2], pr[0][3]),
+                       M::pack2(pr[1][0], pr[1][1]), M::pack2(pr[1][2], pr[1][3]));
+        if (j == 0u) pal[k & 1u][16u * rw + c16] = alpha;
+      } else {
+        // denominators and references for the value waves
+        const float l_tot = rows4_sum(lsum);
+        if (j == 0u) {
+          fin[0][16u * rw + c16] = m;
+          fin[1][16u * rw + c16] = l_tot;
+        }
+      }
+      interval_tail(k);
+    }
+    return;
   }
 
-  for (uint32_t kt = 0; kt < n_tiles; ++kt) {
-    const uint32_t t0 = t_lo + kt * kTT;
-    const uint32_t ahead = n_tiles - 1 - kt;
-    if (ahead >= 2) wait_vm<2 * kLoads>();
-    else if (ahead == 1) wait_vm<kLoads>();
-    else wait_vm<0>();
-    unsigned char *st_lat = lds + (kt % kStages) * L::kStage;
-    unsigned char *st_pos = st_lat + L::kLat;
-    if (t0 + kTT > t_hi) {
-      // last tile: zero the latent of rows past the end (it is also V)
-      block_sync_lds();
-      for (uint32_t e = tid; e < uint32_t(kTT * L::kLatCPR); e += 256) {
-        const uint32_t r = e / L::kLatCPR;
-        if (t0 + r >= t_hi)
-          *reinterpret_cast<uint4 *>(st_lat + r * L::kLatRow + 16u * (e % L::kLatCPR)) =
-              make_uint4(0, 0, 0, 0);
+  // Value waves: o[mb][nb] holds O^T[dim 128 rw + 16 mb + 4 j + e][head hb +
+  // 16 nb + c16].
+  f32x4_t o[MBW][NBW];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) o[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  prologue();
+  for (uint32_t k = 0; k <= n_tiles; ++k) {
+    interval_head(k);
+    if (k >= 1u) {
+      // value product of tile k - 1
+      const uint32_t kv = k - 1u;
+      const unsigned char *st_lat = lds + (kv % kStages) * L::kStage;
+      float al[NBW];
+      bool moved = false;
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        al[nb] = pal[kv & 1u][16u * nb + c16];
+        moved |= al[nb] != 1.f;
       }
-    }
-    block_sync_lds();
-
-    // S^T = latent . q_abs^T + k_pos . q_pos^T; M-tile mt holds tokens
-    // 16 mt + c16 (A rows).  Both M-tiles advance together with four
-    // accumulators each (k-step mod 4): eight independent MFMA chains.
-    // Reads r = 0 .. 2 (KS + KP) - 1 go in order (k-step r / 2, M-tile
-    // r % 2); read r + kAhead is issued before the MFMA of read r, and the
-    // order is fenced so the LDS latency hides behind the MFMAs in flight.
-    constexpr int kCh = 4;
-    f32x4_t acc[2][kCh];
+      if (__any(moved)) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+        for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-      for (int c = 0; c < kCh; ++c) acc[mt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    {
-      constexpr int kReads = 2 * (KS + KP), kAhead = 6;
-      auto load_a = [&](int r) -> uint4 {
-        const int ks = r >> 1, mt = r & 1;
-        if (ks < KS)
-          return *reinterpret_cast<const uint4 *>(st_lat + mt * (16 * L::kLatRow) + qk_off[ks & 3] +
-                                                  256 * (ks >> 2));
-        return *reinterpret_cast<const uint4 *>(st_pos + mt * (16 * L::kPosRow) + pos_off[ks - KS]);
-      };
-      uint4 ka[kAhead + 1];
-#pragma unroll
-      for (int r = 0; r < kAhead; ++r) ka[r] = load_a(r);
-#pragma unroll
-      for (int r = 0; r < kReads; ++r) {
-        if (r + kAhead < kReads) ka[(r + kAhead) % (kAhead + 1)] = load_a(r + kAhead);
-        const int ks = r >> 1, mt = r & 1;
-        acc[mt][ks % kCh] = M::qk(ka[r % (kAhead + 1)], ks < KS ? qa[ks] : qp[ks - KS], acc[mt][ks % kCh]);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int nb = 0; nb < NBW; ++nb) o[mb][nb] *= al[nb];
       }
-    }
-    f32x4_t s[2];
+      uint4 pb[NBW];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) s[mt] = (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
-
-    // online softmax per head; lane (j, c16) holds tokens 16 mt + 4 j + e.
-    // Probabilities are exp2 of the scaled score minus the head's current
-    // reference m.  Lazy rescaling: the reference only moves when a head's
-    // max exceeds it by more than kSlack (base 2), so probabilities stay
-    // below 2^kSlack and most tiles skip what follows the threshold test.
-    // A lane above m + kSlack means its head's max is too, so the head
-    // maxima are formed only then.
-    float x[2][4];
-    float lmx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool vis = t0 + 16u * mt + 4u * j + e < t_hi;
-        x[mt][e] = vis ? s[mt][e] * sl2 : -INFINITY;
-        lmx = fmaxf(lmx, x[mt][e]);
-      }
-    float p[2][4];
-    uint4 pb;
-    // P^T operand in the value reads' row order: lane (j, c16) holds rows
-    // 4j .. 4j+3 of each M-tile and needs rows pv_row(j, 0..3).  Pack the
-    // even and odd rows separately; one swap of lanes 32..63 of the even
-    // pairs with lanes 0..31 of the odd pairs delivers them: lanes of j = 0
-    // get rows (0, 2) and (8, 10), j = 1 (4, 6) (12, 14), j = 2 (1, 3)
-    // (9, 11), j = 3 (5, 7) (13, 15).
-    auto probs = [&]() {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[mt][e] = fast_exp2(x[mt][e] - m);
-      const auto lo = __builtin_amdgcn_permlane32_swap(M::pack2(p[0][0], p[0][2]), M::pack2(p[0][1], p[0][3]),
-                                                       false, false);
-      const auto hi = __builtin_amdgcn_permlane32_swap(M::pack2(p[1][0], p[1][2]), M::pack2(p[1][1], p[1][3]),
-                                                       false, false);
-      pb = make_uint4(lo[0], lo[1], hi[0], hi[1]);
-    };
-    probs();
-    if (__any(lmx > m + kSlack)) {
-      const float mx = rows4_max(lmx);
-      const float m_new = mx > m + kSlack ? mx : m;
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      lsum *= alpha;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) o[b] *= alpha;
-      probs();
-    }
-    lsum += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-
-    // O^T += latent^T . P^T over 32 tokens: K slots 8j .. 8j+3 are rows
-    // pv_row(j, 0..3), slots 8j+4 .. 8j+7 the same rows + 16.  The two
-    // transposed reads of block b + kPvAhead are issued before the MFMA of
-    // block b and the order is fenced, so every MFMA finds its operand
-    // loaded (left to itself the compiler reads one block at a time and
-    // waits for each pair).
-    {
-      constexpr int kPvAhead = 4;
-      auto load_v = [&](int b) -> uint4 {
-        const unsigned char *p0 = st_lat + pv_off[b & 7] + 256 * (b >> 3);
+      for (int nb = 0; nb < NBW; ++nb)
+        pb[nb] = *reinterpret_cast<const uint4 *>(&pl[kv & 1u][(16u * nb + c16) * kPRow + 16u * j]);
+      constexpr int kPvAhead = 3;
+      auto load_v = [&](int mb) -> uint4 {
+        const unsigned char *p0 = st_lat + pv_off[mb];
         const uint2 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * L::kLatRow);
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
       };
       uint4 va[kPvAhead + 1];
 #pragma unroll
-      for (int b = 0; b < kPvAhead; ++b) va[b] = load_v(b);
+      for (int mb = 0; mb < kPvAhead; ++mb) va[mb] = load_v(mb);
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        if (b + kPvAhead < DB) va[(b + kPvAhead) % (kPvAhead + 1)] = load_v(b + kPvAhead);
-        o[b] = M::qk(va[b % (kPvAhead + 1)], pb, o[b]);
+      for (int mb = 0; mb < MBW; ++mb) {
+        if (mb + kPvAhead < MBW) va[(mb + kPvAhead) % (kPvAhead + 1)] = load_v(mb + kPvAhead);
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) o[mb][nb] = M::qk(va[mb % (kPvAhead + 1)], pb[nb], o[mb][nb]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kt + kStages - 1 < n_tiles) {
-      window_for(kt + kStages - 1);
-      issue(kt + kStages - 1);
+    if (k + 1 == n_tiles) {
+      // tile k is the last: zero its latent rows past the end (they are
+      // also V; no value wave reads the stage before the next barrier, and
+      // the score waves mask those rows)
+      const uint32_t t0 = t_lo + k * kTT;
+      unsigned char *st_lat = lds + (k % kStages) * L::kStage;
+      if (t0 + kTT > t_hi)
+        for (uint32_t e = tid - 64u * kRoleWaves; e < uint32_t(kTT * L::kLatCPR); e += 64u * kRoleWaves) {
+          const uint32_t r = e / L::kLatCPR;
+          if (t0 + r >= t_hi)
+            *reinterpret_cast<uint4 *>(st_lat + r * L::kLatRow + 16u * (e % L::kLatCPR)) =
+                make_uint4(0, 0, 0, 0);
+        }
     }
+    interval_tail(k);
   }
 
-  // normalise and write: lane holds O^T[d = 16b + 4j + e][head c16]
-  const float l_tot = rows4_sum(lsum);
-  const uint32_t h = h0 + c16;
-  if (h >= a.hq) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (direct) {
-    T *out = static_cast<T *>(a.out) + (uint64_t(i) * a.hq + h) * R;
+  // normalise and write: lane holds O^T[dim 128 rw + 16 mb + 4j + e][head hb + 16 nb + c16]
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      uint2 w;
-      w.x = M::pack2(o[b][0] * inv, o[b][1] * inv);
-      w.y = M::pack2(o[b][2] * inv, o[b][3] * inv);
-      *reinterpret_cast<uint2 *>(out + 16 * b + 4 * j) = w;
+  for (int nb = 0; nb < NBW; ++nb) {
+    const uint32_t hl = 16u * nb + c16, h = hb + hl;
+    if (h >= a.hq) continue;
+    const float mh = fin[0][hl], l_tot = fin[1][hl];
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (direct) {
+      T *out = static_cast<T *>(a.out) + (uint64_t(i) * a.hq + h) * R + 128u * rw + 4u * j;
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb) {
+        uint2 w;
+        w.x = M::pack2(o[mb][nb][0] * inv, o[mb][nb][1] * inv);
+        w.y = M::pack2(o[mb][nb][2] * inv, o[mb][nb][3] * inv);
+        *reinterpret_cast<uint2 *>(out + 16 * mb) = w;
+      }
+    } else {
+      const uint64_t r = row_base + hl;
+      float *wo = a.ws_o + r * R + 128u * rw + 4u * j;
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb) *reinterpret_cast<f32x4_t *>(wo + 16 * mb) = o[mb][nb] * inv;
+      if (rw == 0u && j == 0u) a.ws_lse[r] = mh + fast_log2(l_tot);
     }
-  } else {
-    const uint64_t r = row0 + c16;
-    float *wo = a.ws_o + r * R;
-#pragma unroll
-    for (int b = 0; b < DB; ++b) *reinterpret_cast<f32x4_t *>(wo + 16 * b + 4 * j) = o[b] * inv;
-    if (j == 0) a.ws_lse[r] = m + fast_log2(l_tot);
   }
 }
 
 // Split grid: one block per (query, split part, 64-head group).
 template <class DT, int R, int P>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_kernel(RowArgs a, uint32_t head_groups) {
   // Blocks are dispatched round-robin over the eight XCDs.  The head groups
   // of one (query, part) read the same cache rows, so they get consecutive
@@ -418,10 +480,9 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
   if (a.splits > 1 && lo64 >= n) return;  // empty part: the merge skips it
   const uint32_t t_lo = uint32_t(lo64 < n ? lo64 : n);
   const uint32_t t_hi = uint32_t(lo64 + span < n ? lo64 + span : n);
-  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t h0 = hgi * kHeadsPerBlock + wv * 16u;
-  mla_piece<DT, R, P>(a, i, seq, t_lo, t_hi, h0, a.splits == 1,
-                      (uint64_t(i) * a.splits + part) * a.hq + h0);
+  const uint32_t hb = hgi * kHeadsPerBlock;
+  mla_piece<DT, R, P>(a, i, seq, t_lo, t_hi, hb, a.splits == 1,
+                      (uint64_t(i) * a.splits + part) * a.hq + hb);
 }
 
 // Balanced grid (balanced.h) with blocks as units: block u of the launch
@@ -430,7 +491,7 @@ void mla_kernel(RowArgs a, uint32_t head_groups) {
 // mix.  The head groups of one range are numbered onto one XCD and run side
 // by side, so the second read of each latent tile hits that XCD's L2.
 template <class DT, int R, int P>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_balanced_kernel(RowArgs a, uint32_t head_groups) {
   const uint32_t bid = blockIdx.x, span8 = 8u * head_groups;
   const uint32_t u = (bid / span8) * span8 + (bid % 8u) * head_groups + (bid % span8) / 8u;
@@ -441,7 +502,7 @@ void mla_balanced_kernel(RowArgs a, uint32_t head_groups) {
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   bal::Range rg;
   if (!bal::find_range<kTT>(rg, a, groups, grp_k, u == 0u && wv == 0u, lane)) return;
-  const uint32_t h0 = g * kHeadsPerBlock + wv * 16u;
+  const uint32_t hb = g * kHeadsPerBlock;
   bal::Piece pc;
   while (bal::next_piece<kTT>(rg, a, lane, pc)) {
     const uint32_t i = __builtin_amdgcn_readfirstlane(a.qlist ? a.qlist[pc.qi] : pc.qi);
@@ -453,8 +514,7 @@ void mla_balanced_kernel(RowArgs a, uint32_t head_groups) {
     const bool whole = pc.tt0 == 0u && pc.tt1 == pc.ntq;
     const uint32_t slot = bal::piece_slot(pc, u);
     __syncthreads();  // the previous piece's ring and table cache are free
-    mla_piece<DT, R, P>(a, i, seq, t_lo, t_hi, h0, whole,
-                        uint64_t(slot) * kHeadsPerBlock + wv * 16u);
+    mla_piece<DT, R, P>(a, i, seq, t_lo, t_hi, hb, whole, uint64_t(slot) * kHeadsPerBlock);
   }
 }
 
@@ -490,9 +550,9 @@ hipError_t launch_mla_balanced(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
   if (a.bal_waves == 0 || a.bal_waves % (8 * hg) != 0) return hipErrorInvalidValue;
   const dim3 grid(a.bal_waves);
   if (dt == PKV_BF16)
-    launch_k((mla_balanced_kernel<BF16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+    launch_k((mla_balanced_kernel<BF16, 512, 64>), grid, dim3(kThreads), 0, st, a, hg);
   else
-    launch_k((mla_balanced_kernel<F16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+    launch_k((mla_balanced_kernel<F16, 512, 64>), grid, dim3(kThreads), 0, st, a, hg);
   return hipGetLastError();
 }
 
@@ -502,9 +562,9 @@ hipError_t launch_mla_mfma(const RowArgs &a, pkv_dtype dt, hipStream_t st) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(blocks));  // a multiple of 8 * hg
   if (dt == PKV_BF16)
-    launch_k((mla_kernel<BF16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+    launch_k((mla_kernel<BF16, 512, 64>), grid, dim3(kThreads), 0, st, a, hg);
   else
-    launch_k((mla_kernel<F16, 512, 64>), grid, dim3(256), 0, st, a, hg);
+    launch_k((mla_kernel<F16, 512, 64>), grid, dim3(kThreads), 0, st, a, hg);
   return hipGetLastError();
 }
 
