@@ -34,6 +34,8 @@
 // one step before the stage is read.  The key scale is folded into the score
 // scale and the value scale into the normalisation.
 
+#include <type_traits>
+
 #include "mfma_common.h"
 
 namespace pkv {
@@ -227,7 +229,9 @@ struct IC {
   static constexpr int value = N;
 };
 
-template <class DT, int D, bool F8>
+// WIN: a sliding window is in force (without one the block starts at key 0
+// and the masks are one-sided).
+template <class DT, int D, bool F8, bool WIN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     TileArgs a, uint32_t n_sub, uint32_t n_groups) {
   using M = Mfma32<DT>;
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // The block starts at the tile of its first query's first visible key;
   // key tiles wholly at or above its last query's first key need no lower
   // mask.
-  auto win_lo = [&](uint32_t n) { return a.window != 0u && n > a.window ? n - a.window : 0u; };
+  auto win_lo = [&](uint32_t n) { return WIN && n > a.window ? n - a.window : 0u; };
   const uint32_t lo_min = win_lo(a.causal ? pos_min + 1u : k_end);
   const uint32_t lo_max = win_lo(a.causal ? p0 + q_hi : k_end);
   const uint32_t lo_row = a.causal ? win_lo(pos + 1u) : lo_min;
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     f32x16_t &x = s_cur;
     const bool full = (a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
-                                : (t0 + kTT <= k_end)) && t0 >= lo_max;
+                                : (t0 + kTT <= k_end)) && (!WIN || t0 >= lo_max);
     if (!full) {
       // result element 4i + e of this lane is key key_of_elem(i, e) + 2 hf
       // of the tile: visible iff that lies in [lo_row - t0, lim - t0]
@@ -637,7 +641,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          x[4 * i + e] = key_of_elem(i, e) <= dl && key_of_elem(i, e) >= dlo ? x[4 * i + e] : -INFINITY;
+          x[4 * i + e] = key_of_elem(i, e) <= dl && (!WIN || key_of_elem(i, e) >= dlo) ? x[4 * i + e] : -INFINITY;
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -772,22 +776,24 @@ hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st) {
   if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<uint32_t>(blocks));
   const uint32_t ng = uint32_t(n_groups);
-  const bool d64 = a.d == 64;
-  if (a.kv_fp8) {
-    if (dt == PKV_BF16) {
-      if (d64) launch_k((prefill_kernel<BF16, 64, true>), grid, dim3(256), 0, st, a, n_sub, ng);
-      else launch_k((prefill_kernel<BF16, 128, true>), grid, dim3(256), 0, st, a, n_sub, ng);
-    } else {
-      if (d64) launch_k((prefill_kernel<F16, 64, true>), grid, dim3(256), 0, st, a, n_sub, ng);
-      else launch_k((prefill_kernel<F16, 128, true>), grid, dim3(256), 0, st, a, n_sub, ng);
-    }
-  } else if (dt == PKV_BF16) {
-    if (d64) launch_k((prefill_kernel<BF16, 64, false>), grid, dim3(256), 0, st, a, n_sub, ng);
-    else launch_k((prefill_kernel<BF16, 128, false>), grid, dim3(256), 0, st, a, n_sub, ng);
-  } else {
-    if (d64) launch_k((prefill_kernel<F16, 64, false>), grid, dim3(256), 0, st, a, n_sub, ng);
-    else launch_k((prefill_kernel<F16, 128, false>), grid, dim3(256), 0, st, a, n_sub, ng);
-  }
+  const bool d64 = a.d == 64, win = a.window != 0u;
+  // (DT, D, FP8 cache, window) -> kernel
+  auto pick = [&](auto dt_c, auto f8_c, auto win_c) {
+    using DTT = decltype(dt_c);
+    constexpr bool F8 = decltype(f8_c)::value, WIN = decltype(win_c)::value;
+    if (d64) launch_k((prefill_kernel<DTT, 64, F8, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
+    else launch_k((prefill_kernel<DTT, 128, F8, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
+  };
+  auto pick_win = [&](auto dt_c, auto f8_c) {
+    if (win) pick(dt_c, f8_c, std::true_type());
+    else pick(dt_c, f8_c, std::false_type());
+  };
+  auto pick_f8 = [&](auto dt_c) {
+    if (a.kv_fp8) pick_win(dt_c, std::true_type());
+    else pick_win(dt_c, std::false_type());
+  };
+  if (dt == PKV_BF16) pick_f8(BF16());
+  else pick_f8(F16());
   return hipGetLastError();
 }
 
