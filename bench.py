@@ -72,7 +72,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "decode_bf16_gqa_64seq_hbm_traffic.md")
 # sources of the dominant (decode) kernel: the traffic figure is only used
 # while these are unchanged
-DECODE_SOURCES = ("decode_mfma.hip", "device_common.h", "mfma_common.h", "kernels.h")
+DECODE_SOURCES = ("decode_mfma.hip", "balanced.h", "device_common.h", "mfma_common.h", "kernels.h")
 
 
 def _parse():

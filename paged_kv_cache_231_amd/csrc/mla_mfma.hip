@@ -39,12 +39,15 @@ constexpr float kSlack = 8.0f;     // lazy-rescale threshold (log2 units)
 
 // LDS layout of one ring stage: 32 latent rows of R bf16/f16 (row stride 2R
 // bytes), then 32 position rows of P.  Within each 256-byte segment of a
-// latent row, 16-byte chunk c of row r sits in slot c ^ (r & 15): the q.k
-// operand reads (one row per lane, eight lanes per LDS cycle) then fall into
-// distinct banks.  The transposed value reads (32 lanes per cycle, four
-// lanes per row) take their rows in an order that puts the eight rows of a
-// cycle into distinct 32-byte slot pairs (see pv_row below).  Position rows
-// (128 bytes) keep chunk c of row r in slot c ^ ((r >> 1) & 7).
+// latent row, 16-byte chunk c of row r sits in slot c ^ (r & 15).  A
+// 16-byte LDS read is served eight lanes at a time, and is free of bank
+// conflicts when each eight lanes take eight distinct 16-byte units of one
+// 128-byte half (measured): the q.k operand reads (one row per lane, lanes
+// c16 = 0..7 rows 0..7) are.  The transposed value reads (32 lanes per
+// cycle, four lanes per row) take their rows in an order that puts the
+// eight rows of a cycle into distinct 32-byte slot pairs (see pv_row
+// below).  Position rows (128 bytes) keep chunk c of row r in slot
+// c ^ ((r >> 1) & 7).
 
 template <int R, int P>
 struct MLds {
@@ -121,11 +124,14 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
   constexpr int KP = P / 32;                  // q.k steps over the position part (2)
   constexpr int MBW = R / 16 / kRoleWaves;    // 16-dim output blocks per value wave (8)
   constexpr int NBW = kHeadsPerBlock / 16;    // 16-head column blocks (4)
-  constexpr int kPRow = 2 * kTT + 16;         // bytes per head row of P (32 bf16 + 16 pad)
+  constexpr int kPBytes = kHeadsPerBlock * kTT * 2;  // one tile's probabilities, bf16/f16
   constexpr int kLoads = L::kLatPerWave + 1;  // DMA instructions per wave per tile
   __shared__ __align__(1024) unsigned char lds[L::kBytes];
   __shared__ uint32_t tcache[kTableCache];
-  __shared__ __align__(16) unsigned char pl[2][kHeadsPerBlock * kPRow];
+  // P of a tile: the 16-byte chunk j (K slots 8j .. 8j+7 of the value
+  // product) of head 16 nb + c16 at 1024 nb + 256 j + 16 c16, so every eight
+  // lanes of a store or load touch eight consecutive chunks
+  __shared__ __align__(16) unsigned char pl[2][kPBytes];
   __shared__ float pal[2][kHeadsPerBlock];    // per head: rescale factor of the tile
   __shared__ float fin[2][kHeadsPerBlock];    // per head: final reference and denominator
 
@@ -206,26 +212,24 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
 
   // Token order.  The value product's K slots of lane group j are the rows
   // pv_row(j, 0..3) of the tile, then the same rows + 16 (the order that
-  // keeps its transposed reads free of bank conflicts, see below).  The
-  // score product's A row m of M-tile mt is token 16 mt + pv_row(m >> 2,
-  // m & 3), so a score lane (c16, j) ends up holding the probabilities of K
-  // slots 8j .. 8j+7 of the value product: one 16-byte store into P.
+  // keeps its transposed reads free of bank conflicts, see below).
   //   pv_row(j, e) = 4 (j & 1) + (j >> 1) + 2 (e & 1) + 8 (e >> 1): the rows
   //   of lanes 0..31 are 0,2,4,..,14, those of lanes 32..63 the odd rows,
   //   one row of each slot pair per LDS cycle.
+  // A score lane (j, c16) holds rows 4j .. 4j+3 of each M-tile; one lane
+  // swap (below) gives it rows pv_row(j, 0..3) instead, its value K slots.
   auto pv_row_of = [](uint32_t jj, uint32_t e) {
     return 4u * (jj & 1u) + (jj >> 1) + 2u * (e & 1u) + 8u * (e >> 1);
   };
-  // q.k: lane (j, c16) reads chunk 4ks + j of token row qr + 16 mt (the
-  // swizzle permutes chunks inside 256-byte segments: a per-lane base plus
-  // an immediate segment offset); position rows likewise.
-  const uint32_t qr = pv_row_of(c16 >> 2, c16 & 3u);
+  // q.k: lane (j, c16) reads chunk 4ks + j of row c16 + 16 mt (the swizzle
+  // permutes chunks inside 256-byte segments: a per-lane base plus an
+  // immediate segment offset); position rows likewise.
   uint32_t qk_off[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) qk_off[u] = qr * L::kLatRow + 16u * ((4u * u + j) ^ qr);
+  for (int u = 0; u < 4; ++u) qk_off[u] = c16 * L::kLatRow + 16u * L::lat_slot(4u * u + j, c16);
   uint32_t pos_off[KP];
 #pragma unroll
-  for (int ks = 0; ks < KP; ++ks) pos_off[ks] = qr * L::kPosRow + 16u * L::pos_slot(4u * ks + j, qr);
+  for (int ks = 0; ks < KP; ++ks) pos_off[ks] = c16 * L::kPosRow + 16u * L::pos_slot(4u * ks + j, c16);
   // V^T: a transposed read gives lane (j, i) dim 16b + i of four rows,
   // supplied by the group's lanes: lane (j, c16) supplies row pv_row(j,
   // c16 >> 2) (+16 for the second read), dims 16b + 4 (c16 & 3) .. +3, i.e.
@@ -236,7 +240,7 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
   uint32_t pv_off[MBW];
 #pragma unroll
   for (int mb = 0; mb < MBW; ++mb)
-    pv_off[mb] = pv_row * L::kLatRow + 8u * (q4 & 1u) + 16u * ((2u * mb + (q4 >> 1)) ^ pv_row) + 256u * rw;
+    pv_off[mb] = pv_row * L::kLatRow + 8u * (q4 & 1u) + 16u * L::lat_slot(2u * mb + (q4 >> 1), pv_row) + 256u * rw;
 
   const uint32_t n_tiles = t_hi > t_lo ? (t_hi - t_lo + kTT - 1) / kTT : 0u;
   // the interval skeleton shared by both roles (same barriers in every wave)
@@ -291,9 +295,9 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
         const uint32_t t0 = t_lo + k * kTT;
         const unsigned char *st_lat = lds + (k % kStages) * L::kStage;
         const unsigned char *st_pos = st_lat + L::kLat;
-        // S^T: both M-tiles (tokens 16 mt + pv_row order) of this wave's
-        // 16 heads, two accumulators each; read r (k-step r / 2, M-tile
-        // r % 2) is issued kAhead reads ahead and the order is fenced.
+        // S^T: both M-tiles of this wave's 16 heads, two accumulators each;
+        // read r (k-step r / 2, M-tile r % 2) is issued kAhead reads ahead
+        // and the order is fenced.
         f32x4_t acc[2][2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -319,15 +323,15 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        // lane (j, c16) holds tokens 16 mt + pv_row(j, e) of head 16 rw +
-        // c16: masked past the end, scaled to base 2
+        // lane (j, c16) holds tokens 16 mt + 4 j + e of head 16 rw + c16:
+        // masked past the end, scaled to base 2
         float x[2][4];
         float lmx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bool vis = t0 + 16u * mt + pv_row_of(j, uint32_t(e)) < t_hi;
+            const bool vis = t0 + 16u * mt + 4u * j + uint32_t(e) < t_hi;
             x[mt][e] = vis ? (acc[mt][0][e] + acc[mt][1][e]) * sl2 : -INFINITY;
             lmx = fmaxf(lmx, x[mt][e]);
           }
@@ -348,9 +352,17 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
 #pragma unroll
           for (int e = 0; e < 4; ++e) pr[mt][e] = fast_exp2(x[mt][e] - m);
         lsum += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
-        *reinterpret_cast<uint4 *>(&pl[k & 1u][(16u * rw + c16) * kPRow + 16u * j]) =
-            make_uint4(M::pack2(pr[0][0], pr[0][1]), M::pack2(pr[0][2], pr[0][3]),
-                       M::pack2(pr[1][0], pr[1][1]), M::pack2(pr[1][2], pr[1][3]));
+        // into value-product order: pack the even and odd rows separately;
+        // one swap of lanes 32..63 of the even pairs with lanes 0..31 of the
+        // odd pairs delivers them (lanes of j = 0 get rows (0, 2) and
+        // (8, 10), j = 1 (4, 6) (12, 14), j = 2 (1, 3) (9, 11), j = 3 (5, 7)
+        // (13, 15)), rows + 16 from the second M-tile
+        const auto lo = __builtin_amdgcn_permlane32_swap(M::pack2(pr[0][0], pr[0][2]), M::pack2(pr[0][1], pr[0][3]),
+                                                         false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(M::pack2(pr[1][0], pr[1][2]), M::pack2(pr[1][1], pr[1][3]),
+                                                         false, false);
+        *reinterpret_cast<uint4 *>(&pl[k & 1u][1024u * rw + 256u * j + 16u * c16]) =
+            make_uint4(lo[0], lo[1], hi[0], hi[1]);
         if (j == 0u) pal[k & 1u][16u * rw + c16] = alpha;
       } else {
         // denominators and references for the value waves
@@ -395,7 +407,7 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
       uint4 pb[NBW];
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
-        pb[nb] = *reinterpret_cast<const uint4 *>(&pl[kv & 1u][(16u * nb + c16) * kPRow + 16u * j]);
+        pb[nb] = *reinterpret_cast<const uint4 *>(&pl[kv & 1u][1024u * nb + 256u * j + 16u * c16]);
       constexpr int kPvAhead = 3;
       auto load_v = [&](int mb) -> uint4 {
         const unsigned char *p0 = st_lat + pv_off[mb];
