@@ -36,6 +36,12 @@ constexpr int kTT = 32;            // tokens per tile (two 16-row M-tiles)
 constexpr int kStages = 4;         // LDS ring stages
 constexpr int kTableCache = 1024;  // block-table entries cached in LDS
 constexpr float kSlack = 8.0f;     // lazy-rescale threshold (log2 units)
+// Waves that issue the ring's DMA: 0 all eight, 1 the value waves, 2 the
+// score waves.
+constexpr int kDmaRole = 2;
+// The refill of interval k (tile k + 2) is issued at its start (false) or
+// at its end, just before the barrier (true).
+constexpr bool kDmaAtTail = false;
 
 // LDS layout of one ring stage: 32 latent rows of R bf16/f16 (row stride 2R
 // bytes), then 32 position rows of P.  Within each 256-byte segment of a
@@ -59,7 +65,6 @@ struct MLds {
   static constexpr int kBytes = kStages * kStage;
   static constexpr int kLatCPR = R / 8;            // 16-byte chunks per latent row
   static constexpr int kPosCPR = P / 8;            // per position row
-  static constexpr int kLatPerWave = kTT / kWaves;  // latent rows each wave loads
   static __device__ __forceinline__ uint32_t lat_slot(uint32_t c, uint32_t r) { return c ^ (r & 15u); }
   static __device__ __forceinline__ uint32_t pos_slot(uint32_t c, uint32_t r) { return c ^ ((r >> 1) & 7u); }
 };
@@ -125,7 +130,7 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
   constexpr int MBW = R / 16 / kRoleWaves;    // 16-dim output blocks per value wave (8)
   constexpr int NBW = kHeadsPerBlock / 16;    // 16-head column blocks (4)
   constexpr int kPBytes = kHeadsPerBlock * kTT * 2;  // one tile's probabilities, bf16/f16
-  constexpr int kLoads = L::kLatPerWave + 1;  // DMA instructions per wave per tile
+  constexpr int kLoads = kTT / (kDmaRole == 0 ? kWaves : kRoleWaves) + 1;  // DMA instructions per issuing wave per tile
   __shared__ __align__(1024) unsigned char lds[L::kBytes];
   __shared__ uint32_t tcache[kTableCache];
   // P of a tile: the 16-byte chunk j (K slots 8j .. 8j+7 of the value
@@ -164,19 +169,25 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
   const T *kpos = static_cast<const T *>(a.kp);
   __syncthreads();  // table cache ready
 
-  // DMA of tile kt: wave wv loads latent rows 4wv .. 4wv+3 (one whole row
-  // per instruction: uniform row base, per-lane chunk offset) and position
-  // rows 4wv .. 4wv+3 (one instruction, lanes 0..31, lane l row 4wv + l/8).
-  // Lane l locates row 4wv + (l/8 mod 4); the latent loads take the page and
-  // slot of lanes 0, 8, 16, 24.  Rows past the end read row 0 of page 0;
-  // their latent is zeroed before the value product.
-  uint32_t lat_voff[L::kLatPerWave];  // byte offset of the chunk lane l fetches
+  // DMA of tile kt, issued by the waves of kDmaRole (all eight, or the four
+  // of one role): issuing wave d of nd loads latent rows (32 / nd) d ..
+  // (one whole row per instruction: uniform row base, per-lane chunk
+  // offset) and the position rows beside them (one instruction; with eight
+  // issuers lanes 0..31 only).  Lane l locates row (32 / nd) d + l/8 (mod
+  // the rows it owns); the latent loads take the page and slot of lanes 0,
+  // 8, 16, ...  Rows past the end read row 0 of page 0; their latent is
+  // zeroed before the value product.
+  constexpr int nd = kDmaRole == 0 ? kWaves : kRoleWaves;
+  constexpr int kRowsPer = kTT / nd;  // latent rows per issuing wave
+  const bool issuer = kDmaRole == 0 || (kDmaRole == 1) == !scorer;
+  const uint32_t dw = kDmaRole == 0 ? wv : rw;  // index among the issuers
+  uint32_t lat_voff[kRowsPer];  // byte offset of the chunk lane l fetches
 #pragma unroll
-  for (int n2 = 0; n2 < L::kLatPerWave; ++n2)
-    lat_voff[n2] = 16u * L::lat_slot(lane, wv * uint32_t(L::kLatPerWave) + n2);
-  const uint32_t pos_r = wv * uint32_t(L::kLatPerWave) + ((lane >> 3) & 3u);
+  for (int n2 = 0; n2 < kRowsPer; ++n2) lat_voff[n2] = 16u * L::lat_slot(lane, dw * uint32_t(kRowsPer) + n2);
+  const uint32_t pos_r = dw * uint32_t(kRowsPer) + ((lane >> 3) % uint32_t(kRowsPer));
   const uint32_t pos_voff = 16u * L::pos_slot(lane % L::kPosCPR, pos_r);
   auto issue = [&](uint32_t kt) {
+    if (!issuer) return;
     unsigned char *stage = lds + (kt % kStages) * L::kStage;
     const uint32_t t0 = t_lo + kt * kTT;
     const uint32_t tok = t0 + pos_r;
@@ -185,17 +196,17 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
     const uint32_t slot = ok ? tok - lp * ps : 0u;
     const uint32_t page = ok ? tcache[lp - wb] : 0u;
 #pragma unroll
-    for (int n2 = 0; n2 < L::kLatPerWave; ++n2) {
-      const uint32_t rr = wv * uint32_t(L::kLatPerWave) + n2;
+    for (int n2 = 0; n2 < kRowsPer; ++n2) {
+      const uint32_t rr = dw * uint32_t(kRowsPer) + n2;
       const uint32_t pg = __builtin_amdgcn_readlane(page, 8 * n2);
       const uint32_t sl = __builtin_amdgcn_readlane(slot, 8 * n2);
       const T *row = lat + (pg * uint32_t(a.k_page) + sl * uint32_t(a.k_tok));
       dma16_s(row, lat_voff[n2], __builtin_amdgcn_readfirstlane(lds_addr(stage + rr * L::kLatRow)));
     }
     const uint32_t off = page * uint32_t(a.kp_page) + slot * uint32_t(a.kp_tok);
-    if (lane < 32u)
+    if (lane < 8u * uint32_t(kRowsPer))
       dma16(reinterpret_cast<const unsigned char *>(kpos + off) + pos_voff,
-            __builtin_amdgcn_readfirstlane(lds_addr(stage + L::kLat + 4u * wv * L::kPosRow)));
+            __builtin_amdgcn_readfirstlane(lds_addr(stage + L::kLat + uint32_t(kRowsPer) * dw * L::kPosRow)));
   };
   // before issuing tile kt: move the table window if the tile reaches past
   // it (every wave calls this at the same point of an interval)
@@ -257,10 +268,11 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
   auto interval_head = [&](uint32_t k) {
     if (k + 2 < n_tiles) {
       window_for(k + 2);
-      issue(k + 2);
+      if (!kDmaAtTail) issue(k + 2);
     }
   };
   auto interval_tail = [&](uint32_t k) {
+    if (kDmaAtTail && k + 2 < n_tiles) issue(k + 2);
     // this wave's share of tile k + 1 has landed (tile k + 2's may not)
     if (k + 2 < n_tiles) wait_vm<kLoads>();
     else wait_vm<0>();
