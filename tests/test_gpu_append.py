@@ -42,6 +42,9 @@ def _bits_equal(a, b):
 
 CASES = [  # hkv, d, dv: 16-byte, 4-byte and 2-byte copy units
     (2, 128, 128), (8, 64, 32), (3, 48, 80), (1, 10, 6), (1, 5, 3),
+    # several 256-unit chunks per query (one wave each): 16-byte units, and
+    # 4-byte (f32) or 2-byte (f16, bf16) units with a ragged last chunk
+    (8, 256, 256), (1, 301, 300),
 ]
 
 
