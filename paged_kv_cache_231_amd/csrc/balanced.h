@@ -21,13 +21,18 @@
 namespace pkv {
 namespace bal {
 
-// Tiles of TT keys of row query r, on the TT-key grid from the tile that
-// holds its first visible key (the window's start).
+// Visible keys of query i (the causal count needs no length load), capped
+// at the table's reach.
+__device__ __forceinline__ uint32_t row_keys(const RowArgs &a, uint32_t seq, uint32_t pos) {
+  const uint64_t reach = uint64_t(a.plan.W) * a.plan.ps;
+  uint64_t n = a.causal ? uint64_t(pos) + 1u : uint64_t(a.plan.words[a.plan.lens + seq]);
+  return uint32_t(n < reach ? n : reach);
+}
+
+// Tiles of TT keys of a query with n visible keys, on the TT-key grid from
+// the tile that holds its first visible key (the window's start).
 template <uint32_t TT>
-__device__ __forceinline__ uint32_t row_tiles(const RowArgs &a, uint32_t r) {
-  const uint32_t i = a.qlist ? a.qlist[r] : r;
-  uint32_t seq;
-  const uint32_t n = visible_keys(a.plan, i, a.causal, &seq);
+__device__ __forceinline__ uint32_t key_tiles(const RowArgs &a, uint32_t n) {
   return ceil_div_u(n, TT) - window_lo(n, a.window) / TT;
 }
 
@@ -47,22 +52,31 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t) {
 
 // Tile prefix over 64 consecutive row queries base .. base + 63: lane l
 // holds v = tiles of query base + l (0 past the end) and excl = first tile
-// of that query; end = first tile after the chunk.
+// of that query, with the query's index i, sequence and visible keys n (so
+// a piece needs no second look-up); end = first tile after the chunk.
 struct Chunk {
   uint32_t base, end;
   uint32_t v, excl;
+  uint32_t i, seq, n;
 };
 
 template <uint32_t TT>
 __device__ __forceinline__ void scan_chunk(Chunk &c, const RowArgs &a, uint32_t base,
                                            uint32_t carry, uint32_t lane) {
   const uint32_t r = base + lane;
-  const uint32_t v = r < a.n_queries ? row_tiles<TT>(a, r) : 0u;
+  const uint32_t rc = r < a.n_queries ? r : a.n_queries - 1u;
+  const uint32_t i = a.qlist ? a.qlist[rc] : rc;
+  const uint32_t seq = a.plan.words[a.plan.qseq + i];
+  const uint32_t n = row_keys(a, seq, a.plan.words[a.plan.qpos + i]);
+  const uint32_t v = r < a.n_queries ? key_tiles<TT>(a, n) : 0u;
   const uint32_t x = wave_incl_scan(v, lane);
   c.base = base;
   c.v = v;
   c.excl = carry + x - v;
   c.end = carry + __builtin_amdgcn_readlane(x, 63);
+  c.i = i;
+  c.seq = seq;
+  c.n = n;
 }
 
 // One unit's walk over its range [t0, t_end): the chunk holding the current
@@ -72,10 +86,11 @@ struct Range {
   Chunk ch;
 };
 
-// A piece: row query qi, its tiles [tt0, tt1) of ntq; first = the unit's
-// first piece.
+// A piece: row query qi (query i of sequence seq, n visible keys), its
+// tiles [tt0, tt1) of ntq; first = the unit's first piece.
 struct Piece {
   uint32_t qi, tt0, tt1, ntq;
+  uint32_t i, seq, n;
   bool first;
 };
 
@@ -95,14 +110,19 @@ __device__ __forceinline__ bool find_range(Range &rg, const RowArgs &a, uint32_t
   // the plan-word indirection (row list, query words, sequence length) for
   // all of them at once with no branch between the loads; rows past the end
   // read the last row and count 0.
+  // (The causal count needs no length: that level is skipped.)  When all
+  // chunks fit one batch (R <= 64 kBatch), the batch's chunks stay in
+  // registers, so the range's chunk is taken from them instead of loaded
+  // again.
   constexpr uint32_t kBatch = 8;
   const uint32_t nch = (R + 63u) / 64u;
   const uint32_t m = (nch + 63u) / 64u;
   const uint64_t reach = uint64_t(a.plan.W) * a.plan.ps;
   const uint32_t *words = a.plan.words;
   uint32_t s = 0, carry = 0;
+  Chunk kc[kBatch];
   for (uint32_t c0 = 0; c0 < nch; c0 += kBatch) {
-    uint32_t vb[kBatch], qi[kBatch], sq[kBatch], pq[kBatch];
+    uint32_t vb[kBatch], nb[kBatch], qi[kBatch], sq[kBatch], pq[kBatch];
 #pragma unroll
     for (uint32_t b = 0; b < kBatch; ++b) {
       const uint32_t r = (c0 + b) * 64u + lane;
@@ -117,13 +137,17 @@ __device__ __forceinline__ bool find_range(Range &rg, const RowArgs &a, uint32_t
       sq[b] = words[a.plan.qseq + qi[b]];
       pq[b] = words[a.plan.qpos + qi[b]];
     }
+    if (a.causal) {
+#pragma unroll
+      for (uint32_t b = 0; b < kBatch; ++b) nb[b] = pq[b] + 1u;
+    } else {
+#pragma unroll
+      for (uint32_t b = 0; b < kBatch; ++b) nb[b] = words[a.plan.lens + sq[b]];
+    }
 #pragma unroll
     for (uint32_t b = 0; b < kBatch; ++b) {
-      const uint32_t len = words[a.plan.lens + sq[b]];
-      uint64_t n = a.causal ? uint64_t(pq[b]) + 1u : uint64_t(len);
-      if (n > reach) n = reach;
-      const uint32_t t = ceil_div_u(uint32_t(n), TT) - window_lo(uint32_t(n), a.window) / TT;
-      vb[b] = (c0 + b) * 64u + lane < R ? t : 0u;
+      if (uint64_t(nb[b]) > reach) nb[b] = uint32_t(reach);
+      vb[b] = (c0 + b) * 64u + lane < R ? ceil_div_u(nb[b], TT) - window_lo(nb[b], a.window) / TT : 0u;
     }
 #pragma unroll
     for (uint32_t b = 0; b < kBatch; ++b) {
@@ -138,6 +162,15 @@ __device__ __forceinline__ bool find_range(Range &rg, const RowArgs &a, uint32_t
         a.bal_rec[2u * r] = carry + x - v;
         a.bal_rec[2u * r + 1u] = v;
       }
+      if (c0 == 0u) {
+        kc[b].base = c * 64u;
+        kc[b].v = v;
+        kc[b].excl = carry + x - v;
+        kc[b].end = carry + tot;
+        kc[b].i = qi[b];
+        kc[b].seq = sq[b];
+        kc[b].n = nb[b];
+      }
       carry += tot;
     }
   }
@@ -148,11 +181,22 @@ __device__ __forceinline__ bool find_range(Range &rg, const RowArgs &a, uint32_t
   rg.t0 = rg.t = grp_k * tpg;
   if (rg.t >= T) return false;
   rg.t_end = T - rg.t < tpg ? T : rg.t + tpg;
-  // super-chunk lane: the last one starting at or before t (its sum is > 0)
-  const uint64_t sel = __ballot(sx - s <= rg.t);
-  const uint32_t lb = 63u - uint32_t(__builtin_clzll(sel));
-  scan_chunk<TT>(rg.ch, a, lb * m * 64u, __builtin_amdgcn_readlane(sx - s, lb), lane);
-  while (rg.ch.end <= rg.t) scan_chunk<TT>(rg.ch, a, rg.ch.base + 64u, rg.ch.end, lane);
+  if (nch <= kBatch) {
+    // the first kept chunk that ends after t (t < T, so one does)
+    bool found = false;
+#pragma unroll
+    for (uint32_t b = 0; b < kBatch; ++b)
+      if (!found && b < nch && kc[b].end > rg.t) {
+        rg.ch = kc[b];
+        found = true;
+      }
+  } else {
+    // super-chunk lane: the last one starting at or before t (its sum is > 0)
+    const uint64_t sel = __ballot(sx - s <= rg.t);
+    const uint32_t lb = 63u - uint32_t(__builtin_clzll(sel));
+    scan_chunk<TT>(rg.ch, a, lb * m * 64u, __builtin_amdgcn_readlane(sx - s, lb), lane);
+    while (rg.ch.end <= rg.t) scan_chunk<TT>(rg.ch, a, rg.ch.base + 64u, rg.ch.end, lane);
+  }
   rg.qi = rg.ch.base + 63u - uint32_t(__builtin_clzll(__ballot(rg.ch.excl <= rg.t)));
   return true;
 }
@@ -170,6 +214,9 @@ __device__ __forceinline__ bool next_piece(Range &rg, const RowArgs &a, uint32_t
       continue;
     }
     p.qi = rg.qi;
+    p.i = __builtin_amdgcn_readlane(rg.ch.i, li);
+    p.seq = __builtin_amdgcn_readlane(rg.ch.seq, li);
+    p.n = __builtin_amdgcn_readlane(rg.ch.n, li);
     p.ntq = ntq;
     p.tt0 = rg.t - c0;
     p.tt1 = ntq - p.tt0 < rg.t_end - rg.t ? ntq : p.tt0 + (rg.t_end - rg.t);

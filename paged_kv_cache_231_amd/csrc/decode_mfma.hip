@@ -478,10 +478,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(RowArgs a) {
   bal::Piece pc;
   while (bal::next_piece<16>(rg, a, lane, pc)) {
     const uint32_t tt0 = pc.tt0, tt1 = pc.tt1;
-    const uint32_t i = __builtin_amdgcn_readfirstlane(a.qlist ? a.qlist[pc.qi] : pc.qi);
-    uint32_t seq;
-    const uint32_t n = __builtin_amdgcn_readfirstlane(visible_keys(a.plan, i, a.causal, &seq));
-    seq = __builtin_amdgcn_readfirstlane(seq);
+    const uint32_t i = pc.i, seq = pc.seq, n = pc.n;  // found with the range
     const uint32_t lo = window_lo(n, a.window);
     const uint32_t tb = lo / 16u;  // tile tt of the query is grid tile tb + tt
     const uint32_t t_hi = (tb + tt1) * 16u < n ? (tb + tt1) * 16u : n;

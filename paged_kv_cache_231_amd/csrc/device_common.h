@@ -100,8 +100,9 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ uint32_t visible_keys(const PlanView &p, uint32_t i, int causal,
                                                  uint32_t *seq_out) {
   const uint32_t seq = p.words[p.qseq + i];
-  const uint32_t L = p.words[p.lens + seq];
-  uint64_t n = causal ? uint64_t(p.words[p.qpos + i]) + 1 : uint64_t(L);
+  uint64_t n;  // the causal count needs no length
+  if (causal) n = uint64_t(p.words[p.qpos + i]) + 1;
+  else n = p.words[p.lens + seq];
   const uint64_t reach = uint64_t(p.W) * p.ps;
   if (n > reach) n = reach;
   *seq_out = seq;

@@ -529,10 +529,7 @@ void mla_balanced_kernel(RowArgs a, uint32_t head_groups) {
   const uint32_t hb = g * kHeadsPerBlock;
   bal::Piece pc;
   while (bal::next_piece<kTT>(rg, a, lane, pc)) {
-    const uint32_t i = __builtin_amdgcn_readfirstlane(a.qlist ? a.qlist[pc.qi] : pc.qi);
-    uint32_t seq;
-    const uint32_t n = __builtin_amdgcn_readfirstlane(visible_keys(a.plan, i, a.causal, &seq));
-    seq = __builtin_amdgcn_readfirstlane(seq);
+    const uint32_t i = pc.i, seq = pc.seq, n = pc.n;  // found with the range
     const uint32_t t_lo = pc.tt0 * kTT;
     const uint32_t t_hi = pc.tt1 * kTT < n ? pc.tt1 * kTT : n;
     const bool whole = pc.tt0 == 0u && pc.tt1 == pc.ntq;

@@ -61,6 +61,17 @@ def test_mla_balanced_many_pieces(causal):
     assert_close(run(wl, splits=0), expected(wl), torch.bfloat16, "mla balanced many")
 
 
+@pytest.mark.parametrize("n_rows", [300, 700])
+def test_mla_balanced_many_queries(n_rows):
+    """Hundreds of short queries: ranges that start in any of the first eight
+    64-query chunks (kept from the counting pass) and, past 512 queries, in
+    chunks found by the two-level search."""
+    rng = np.random.default_rng(2350 + n_rows)
+    lens = [int(x) for x in rng.integers(1, 200, size=n_rows)]
+    wl = _mla(torch.bfloat16, 16, 16, lens, 2350 + n_rows)
+    assert_close(run(wl, splits=0), expected(wl), torch.bfloat16, f"mla balanced {n_rows} queries")
+
+
 def test_mla_balanced_launches_and_reuse():
     """One MLA kernel and one merge per call; repeated calls on one workspace
     stay correct; the unbalanced path is unchanged."""
