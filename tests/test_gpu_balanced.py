@@ -54,13 +54,14 @@ def test_balanced_many_tiles_per_wave():
     assert_close(run(wl, splits=0), expected(wl), torch.bfloat16, "balanced 25k tiles")
 
 
-@pytest.mark.parametrize("n_rows", [300, 700])
+@pytest.mark.parametrize("n_rows", [300, 512, 513, 700])
 @pytest.mark.parametrize("causal", [True, False])
 def test_balanced_many_row_queries(n_rows, causal):
     """Hundreds of row queries: ranges that start in any of the first eight
     64-query chunks (kept in registers from the counting pass) and, past 512
-    rows, in chunks found by the two-level search; some queries see one
-    token.  Causal and full visibility (the causal count reads no length)."""
+    rows, in chunks found by the two-level search (512 and 513 are the two
+    sides of that boundary); some queries see one token.  Causal and full
+    visibility (the causal count reads no length)."""
     rng = np.random.default_rng(1250 + n_rows)
     lens = [int(x) for x in rng.integers(1, 400, size=n_rows)]
     wl = _wl(torch.bfloat16, 8, 2, 64, 16, lens, seed=1250 + n_rows, causal=causal)
