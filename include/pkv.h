@@ -253,7 +253,8 @@ pkv_status pkv_tune_splits_mla(const pkv_plan *plan, pkv_dtype dtype,
  * Q == 0 returns PKV_OK with no launch.
  * Errors: PKV_EINVAL (null pointer, bad dtype, scale not finite and > 0,
  * out overlapping an input), PKV_ESHAPE (q_heads % kv_heads, head_dim or
- * value_dim outside 1..1024), PKV_ERANGE (a tensor above u32 elements),
+ * value_dim outside 1..1024), PKV_ERANGE (q or out above u32 elements,
+ * or a cache above 2^63 bytes: caches are addressed with 64-bit offsets),
  * PKV_EDEVICE, PKV_EWORKSPACE (ws built for other queries/heads/dv/stream),
  * PKV_EHIP (launch failure). */
 pkv_status pkv_attention(const pkv_plan *plan, pkv_dtype dtype, const void *q,
@@ -365,7 +366,8 @@ pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs,
  * Errors: PKV_EINVAL (null pointer, bad dtype, a conflicting write plan,
  * new rows, caches or copies overlapping each other, K and V caches
  * overlapping), PKV_ESHAPE (a zero head count or dim, a dim above 1024),
- * PKV_ERANGE (a tensor above u32 elements), PKV_EDEVICE, PKV_EHIP. */
+ * PKV_ERANGE (a new-row tensor above u32 elements, or a cache above 2^63
+ * bytes), PKV_EDEVICE, PKV_EHIP. */
 typedef struct {
   uint32_t key_copied;    /* the key cache was copied before the append   */
   uint32_t value_copied;  /* the value cache was copied before the append */

@@ -65,6 +65,18 @@ bool u32_elems(std::initializer_list<uint64_t> dims) {
   return n <= kU32Max;
 }
 
+// A cache tensor may hold more than 2^32 elements (the kernels address the
+// caches with 64-bit offsets); its size in bytes, at four bytes an element
+// at most, has to fit in 63 bits.
+bool cache_fits(std::initializer_list<uint64_t> dims) {
+  unsigned __int128 p = 4;
+  for (uint64_t d : dims) {
+    p *= d;
+    if (p >> 63) return false;
+  }
+  return true;
+}
+
 bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) {
   if (!a || !b || a_bytes == 0 || b_bytes == 0) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -673,9 +685,9 @@ pkv_status attention_impl(const pkv_plan *plan, pkv_dtype dtype, bool fp8, const
       return fail(PKV_EINVAL, "an FP8 cache needs 16-byte aligned q, k and v");
   }
   const PlanLayout &L = plan->L;
-  if (!u32_elems({L.Q, hq, d}) || !u32_elems({L.N, L.ps, hkv, d}) || !u32_elems({L.N, L.ps, hkv, dv}) ||
-      !u32_elems({L.Q, hq, dv}))
-    return fail(PKV_ERANGE, "a tensor has more than 2^32 - 1 elements");
+  if (!u32_elems({L.Q, hq, d}) || !u32_elems({L.Q, hq, dv}) || !cache_fits({L.N, L.ps, hkv, d}) ||
+      !cache_fits({L.N, L.ps, hkv, dv}))
+    return fail(PKV_ERANGE, "a query or output tensor has more than 2^32 - 1 elements, or a cache 2^63 bytes");
   pkv_status st = check_binding(plan, stream);
   if (st != PKV_OK) return st;
   st = check_workspace(ws, plan, hq, dv, stream);
@@ -883,9 +895,9 @@ pkv_status pkv_append(const pkv_plan *plan, pkv_dtype dtype, const void *new_k, 
   if (hkv == 0 || d == 0 || dv == 0 || d > 1024 || dv > 1024)
     return fail(PKV_ESHAPE, "append needs nonzero head counts and head dims of at most 1024");
   const PlanLayout &L = plan->L;
-  if (!u32_elems({L.Q, hkv, d}) || !u32_elems({L.Q, hkv, dv}) || !u32_elems({L.N, L.ps, hkv, d}) ||
-      !u32_elems({L.N, L.ps, hkv, dv}))
-    return fail(PKV_ERANGE, "a tensor has more than 2^32 - 1 elements");
+  if (!u32_elems({L.Q, hkv, d}) || !u32_elems({L.Q, hkv, dv}) || !cache_fits({L.N, L.ps, hkv, d}) ||
+      !cache_fits({L.N, L.ps, hkv, dv}))
+    return fail(PKV_ERANGE, "a new-row tensor has more than 2^32 - 1 elements, or a cache 2^63 bytes");
   pkv_status st = check_binding(plan, stream);
   if (st != PKV_OK) return st;
   st = validate_writes(plan->host.data(), L);
@@ -955,8 +967,8 @@ pkv_status pkv_mla(const pkv_plan *plan, pkv_dtype dtype, const void *q_abs, con
   if (!std::isfinite(scale) || scale <= 0.f) return fail(PKV_EINVAL, "scale must be finite and positive");
   const PlanLayout &L = plan->L;
   if (!u32_elems({L.Q, heads, rank}) || !u32_elems({L.Q, heads, pos_dim}) ||
-      !u32_elems({L.N, L.ps, 1, rank}) || !u32_elems({L.N, L.ps, 1, pos_dim}))
-    return fail(PKV_ERANGE, "a tensor has more than 2^32 - 1 elements");
+      !cache_fits({L.N, L.ps, 1, rank}) || !cache_fits({L.N, L.ps, 1, pos_dim}))
+    return fail(PKV_ERANGE, "a query or output tensor has more than 2^32 - 1 elements, or a cache 2^63 bytes");
   pkv_status st = check_binding(plan, stream);
   if (st != PKV_OK) return st;
   st = check_workspace(ws, plan, heads, rank, stream);

@@ -116,8 +116,8 @@ __device__ __forceinline__ void load_tile(TileRegs<D, F8> &t, const RowArgs &a, 
   // token exists).  Its K feeds only scores masked to -inf and its V is
   // replaced by zeros when staged (a select, so NaN never leaks).  The loads
   // are unconditional, which keeps them in flight across the attention of
-  // the previous tile.  Element offsets fit in 32 bits: every cache tensor
-  // has < 2^32 elements.
+  // the previous tile.  Element offsets are 64-bit: a cache tensor may hold
+  // more than 2^32 elements.
   if constexpr (PU) {
     const uint32_t page = __builtin_amdgcn_readlane(map.lane_page, k - map.base);
     const uint32_t rows = map.t_hi - t0 < 16u ? map.t_hi - t0 : 16u;
@@ -125,14 +125,16 @@ __device__ __forceinline__ void load_tile(TileRegs<D, F8> &t, const RowArgs &a, 
     const uint32_t before = map.lo > t0 ? map.lo - t0 : 0u;  // rows before the window
     t.valid16 = page_ok && before < 16u ? ((1u << rows) - 1u) & ~((1u << before) - 1u) : 0u;
     const uint32_t slot0 = t0 & (map.ps - 1);
+    // the page's first element (uniform: scalar arithmetic)
+    const uint64_t kpb = uint64_t(page) * a.k_page, vpb = uint64_t(page) * a.v_page;
 #pragma unroll
     for (int n = 0; n < TR::NL; ++n) {
       const uint32_t r = TR::RPI * n + lane / TR::CPR;
       const bool ok = page_ok && r < rows;
-      const uint32_t ko = ok ? page * uint32_t(a.k_page) + (slot0 + r) * uint32_t(a.k_tok) : 0u;
-      const uint32_t vo = ok ? page * uint32_t(a.v_page) + (slot0 + r) * uint32_t(a.v_tok) : 0u;
-      t.k[n] = load_stream16(kbase + uint64_t(ko) * TR::EB + 16u * chunk);
-      t.v[n] = load_stream16(vbase + uint64_t(vo) * TR::EB + 16u * chunk);
+      const uint64_t ko = ok ? kpb + uint64_t(slot0 + r) * a.k_tok : 0u;
+      const uint64_t vo = ok ? vpb + uint64_t(slot0 + r) * a.v_tok : 0u;
+      t.k[n] = load_stream16(kbase + ko * TR::EB + 16u * chunk);
+      t.v[n] = load_stream16(vbase + vo * TR::EB + 16u * chunk);
     }
   } else {
     uint32_t valid = 0;
@@ -146,10 +148,10 @@ __device__ __forceinline__ void load_tile(TileRegs<D, F8> &t, const RowArgs &a, 
       const uint32_t page = ok ? map.table[lp] : 0u;
       ok = ok && page < map.n_pages_pool;  // never read outside the pool
       valid |= ok ? 1u << r : 0u;
-      const uint32_t ko = ok ? page * uint32_t(a.k_page) + slot * uint32_t(a.k_tok) : 0u;
-      const uint32_t vo = ok ? page * uint32_t(a.v_page) + slot * uint32_t(a.v_tok) : 0u;
-      t.k[n] = load_stream16(kbase + uint64_t(ko) * TR::EB + 16u * chunk);
-      t.v[n] = load_stream16(vbase + uint64_t(vo) * TR::EB + 16u * chunk);
+      const uint64_t ko = ok ? uint64_t(page) * a.k_page + uint64_t(slot) * a.k_tok : 0u;
+      const uint64_t vo = ok ? uint64_t(page) * a.v_page + uint64_t(slot) * a.v_tok : 0u;
+      t.k[n] = load_stream16(kbase + ko * TR::EB + 16u * chunk);
+      t.v[n] = load_stream16(vbase + vo * TR::EB + 16u * chunk);
     }
     // every lane knows the rows it loaded; OR them across the wave
     uint32_t all = valid;

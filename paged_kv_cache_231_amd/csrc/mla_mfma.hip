@@ -195,15 +195,21 @@ __device__ __forceinline__ void mla_piece(const RowArgs &a, uint32_t i, uint32_t
     const uint32_t lp = ok ? page_of(tok) : wb;
     const uint32_t slot = ok ? tok - lp * ps : 0u;
     const uint32_t page = ok ? tcache[lp - wb] : 0u;
+    // every lane forms the 64-bit address of the row it locates (vector
+    // arithmetic, once per tile: a cache may hold more than 2^32 elements);
+    // each row's instruction then reads the two halves of its row's address
+    const uint64_t ra = reinterpret_cast<uint64_t>(lat + (uint64_t(page) * a.k_page + uint64_t(slot) * a.k_tok));
+    const uint32_t ra_lo = uint32_t(ra), ra_hi = uint32_t(ra >> 32);
 #pragma unroll
     for (int n2 = 0; n2 < kRowsPer; ++n2) {
       const uint32_t rr = dw * uint32_t(kRowsPer) + n2;
-      const uint32_t pg = __builtin_amdgcn_readlane(page, 8 * n2);
-      const uint32_t sl = __builtin_amdgcn_readlane(slot, 8 * n2);
-      const T *row = lat + (pg * uint32_t(a.k_page) + sl * uint32_t(a.k_tok));
-      dma16_s(row, lat_voff[n2], __builtin_amdgcn_readfirstlane(lds_addr(stage + rr * L::kLatRow)));
+      // (the builtin returns int: widen through uint32_t, never sign-extend)
+      const uint64_t rs = uint64_t(uint32_t(__builtin_amdgcn_readlane(ra_lo, 8 * n2))) |
+                          (uint64_t(uint32_t(__builtin_amdgcn_readlane(ra_hi, 8 * n2))) << 32);
+      dma16_s(reinterpret_cast<const T *>(rs), lat_voff[n2],
+              __builtin_amdgcn_readfirstlane(lds_addr(stage + rr * L::kLatRow)));
     }
-    const uint32_t off = page * uint32_t(a.kp_page) + slot * uint32_t(a.kp_tok);
+    const uint64_t off = uint64_t(page) * a.kp_page + uint64_t(slot) * a.kp_tok;
     if (lane < 8u * uint32_t(kRowsPer))
       dma16(reinterpret_cast<const unsigned char *>(kpos + off) + pos_voff,
             __builtin_amdgcn_readfirstlane(lds_addr(stage + L::kLat + uint32_t(kRowsPer) * dw * L::kPosRow)));

@@ -280,15 +280,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // block table of the sequence, first kTableCache entries, into LDS
   const uint32_t *table = pv.words + pv.table + uint64_t(seq) * pv.W;
-  // (each entry holds the element offset of the page's first row: K and V
-  // share their strides since head_dim == value_dim)
-  const uint32_t page_elems = uint32_t(a.k_page);
-  // element offset of a physical page (ids outside the pool read page 0)
-  auto page_of = [&](uint32_t pg) { return (pg < pv.N ? pg : 0u) * page_elems; };
+  // (each entry holds a physical page, ids outside the pool replaced by
+  // page 0; K and V share their strides since head_dim == value_dim)
+  const uint64_t page_elems = a.k_page;
+  // 64-bit element offset of a physical page's first row (a cache tensor may
+  // hold more than 2^32 elements; ids outside the pool read page 0)
+  auto page_of = [&](uint32_t pg) { return uint64_t(pg < pv.N ? pg : 0u) * page_elems; };
   const uint32_t n_lp = (k_end + ps - 1) / ps;
   for (uint32_t e = tid; e < n_lp && e < uint32_t(kTableCache); e += 256) {
     const uint32_t pg = table[e];
-    tcache[e] = (pg < pv.N ? pg : 0u) * page_elems;  // never read outside the pool
+    tcache[e] = pg < pv.N ? pg : 0u;  // never read outside the pool
   }
 
   // This lane's q-row (column c32 of the wave's N block) and its half of
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // sequence's token 0 (any row inside the pool would do): their scores
   // are masked out and their value rows are zeroed in LDS before use, so
   // nothing of them reaches the output.
-  auto lookup = [&](uint32_t kt, uint32_t (&off)[L::NI]) {
+  auto lookup = [&](uint32_t kt, uint64_t (&off)[L::NI]) {
     const uint32_t tok0 = kt * kTT;
     const uint32_t tile_off = pow2 ? (tok0 & (ps - 1u)) * tok_elems : 0u;
 #pragma unroll
@@ -365,16 +366,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const bool ok = tok < k_end;
       if (pow2) {
         const uint32_t lp = ok ? tok >> ps_shift : 0u;  // entry 0 exists whenever a tile does
-        const uint32_t pbase = lp < uint32_t(kTableCache)
-                                   ? tcache[lp]
-                                   : page_of(table_word(table + lp));
+        const uint64_t pbase = page_of(lp < uint32_t(kTableCache) ? tcache[lp] : table_word(table + lp));
         off[n] = ok ? pbase + tile_off + lane_off[n] : pbase + lane_off[n] - (rr & (ps - 1u)) * tok_elems;
       } else {
         const uint32_t lp = ok ? tok / ps : 0u;
         const uint32_t slot = ok ? tok - lp * ps : 0u;
-        const uint32_t pbase = lp < uint32_t(kTableCache)
-                                   ? tcache[lp]
-                                   : page_of(table_word(table + lp));
+        const uint64_t pbase = page_of(lp < uint32_t(kTableCache) ? tcache[lp] : table_word(table + lp));
         off[n] = pbase + slot * tok_elems + lane_off[n];
       }
     }
@@ -403,12 +400,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t tw = __builtin_amdgcn_readfirstlane(kt * kTT + kWaveRows * wv);
     return ctable[tw >> ps_shift];
   };
-  auto wave_base_of = [&](uint32_t kt, uint32_t pg) -> uint32_t {
+  auto wave_base_of = [&](uint32_t kt, uint32_t pg) -> uint64_t {
     const uint32_t tw = kt * kTT + kWaveRows * wv;
     return page_of(pg) + (tw & (ps - 1u)) * tok_elems;
   };
   auto wave_base = [&](uint32_t kt) { return wave_base_of(kt, wave_page(kt)); };
-  auto issue_fast = [&](uint32_t kt, uint32_t wb) {
+  auto issue_fast = [&](uint32_t kt, uint64_t wb) {
     unsigned char *stage = lds + ((kt - kt0) % kStages) * L::kStage;
     const CT *kb = kbase + wb, *vb = vbase + wb;
 #pragma unroll
@@ -421,7 +418,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto fast_tile = [&](uint32_t kt) { return fast_dma && (kt + 1) * kTT <= k_end; };
 
-  auto issue = [&](uint32_t kt, const uint32_t (&off)[L::NI]) {
+  auto issue = [&](uint32_t kt, const uint64_t (&off)[L::NI]) {
     unsigned char *stage = lds + ((kt - kt0) % kStages) * L::kStage;
 #pragma unroll
     for (int n = 0; n < L::NI; ++n) {
@@ -447,8 +444,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t t = tok < k_end ? tok : 0u;
     const uint32_t lp = pow2 ? t >> ps_shift : t / ps;
     const uint32_t slot = t - lp * ps;
-    const uint32_t pbase = lp < uint32_t(kTableCache) ? tcache[lp] : page_of(table_word(table + lp));
-    const uint32_t off = pbase + slot * tok_elems + f_col;
+    const uint64_t pbase = page_of(lp < uint32_t(kTableCache) ? tcache[lp] : table_word(table + lp));
+    const uint64_t off = pbase + slot * tok_elems + f_col;
     if constexpr (EPT == 16) {
       rk = *reinterpret_cast<const uint4 *>(kbase + off);
       rv = *reinterpret_cast<const uint4 *>(vbase + off);
@@ -522,7 +519,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (fast_tile(kt)) {
         issue_fast(kt, wave_base(kt));
       } else {
-        uint32_t off[L::NI];
+        uint64_t off[L::NI];
         lookup(kt, off);
         issue(kt, off);
       }
@@ -622,7 +619,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const bool refill = !F8 && kt + kStages - 1 < n_tiles;
     const bool rfast = refill && fast_tile(kt + kStages - 1);
-    uint32_t roff[L::NI];
+    uint64_t roff[L::NI];
     if (refill && !rfast) lookup(kt + kStages - 1, roff);
 
     uint4 kb[kAhead + 1], vb[kAhead + 1];
