@@ -99,3 +99,25 @@ def test_mla_pages_past_2_32_elements(splits):
     assert_close(got.double().cpu().numpy(), expected(wl), torch.bfloat16, f"big mla splits={splits}")
     del lat, kp
     torch.cuda.empty_cache()
+
+
+def test_size_limits_launch_nothing():
+    """Query and output tensors stay below 2^32 elements and a cache below
+    2^63 bytes: both are refused with ERANGE before anything runs."""
+    lib = pkv.lib()
+    buf = torch.full((1 << 16,), 7.0, dtype=torch.bfloat16, device="cuda")
+    ptr = buf.data_ptr()
+
+    def call(plan, hq, hkv, d):
+        return pkv.STATUS[lib.pkv_attention(plan.handle, 2, ptr, ptr, ptr, ptr, hq, hkv, d, d, 0.1, 1,
+                                            None, None)]
+
+    # 4097 queries x 1024 heads x 1024 dims: q and out above 2^32 elements
+    n = 4097
+    plan_q = pkv.Plan([n], [0] * n, list(range(n)), np.array([[0, 1]]), 4096, 2)
+    assert call(plan_q, 1024, 1, 1024) == "ERANGE"
+    # 2^32 - 1 pages of 4096 tokens x 1024 heads x 1024 dims: a cache of 2^66 bytes
+    plan_k = pkv.Plan([1], [0], [0], np.array([[0]]), 4096, (1 << 32) - 1)
+    assert call(plan_k, 1024, 1024, 1024) == "ERANGE"
+    torch.cuda.synchronize()
+    assert (buf == 7.0).all(), "a rejected call wrote memory"
