@@ -92,14 +92,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
       (__attribute__((address_space(3))) const char *)(p)));
 }
 
-// Keep a loop-invariant MFMA operand in AGPRs (the MFMA reads it there).
-__device__ __forceinline__ void to_agpr(uint4 &x) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 v = __builtin_bit_cast(u32x4, x);
-  asm volatile("" : "+a"(v));
-  x = __builtin_bit_cast(uint4, v);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
