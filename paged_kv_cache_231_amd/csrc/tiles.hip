@@ -8,6 +8,12 @@
 // key rows 0..p_last, and every (query, q head) of one KV head forms a dense
 // contraction with those rows.
 //
+// Two kernels share the tiling and the operand layouts below: for 16-bit
+// caches the role-split kernel (prefill_rs_kernel, eight waves per block:
+// four compute the scores and the softmax, four the value product and the
+// ring loads), for FP8 caches prefill_kernel (four waves, each doing all of
+// it), described first.
+//
 // A block owns 128 q-rows (a q-row is one (query, q head) pair; with G q
 // heads per KV head that is 128/G queries x G heads) of one tile and one KV
 // head; each of its four waves owns 32 q-rows, the N side of 32x32x16 MFMAs.
@@ -751,6 +757,385 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Role-split form of the kernel above for 16-bit caches.  A block runs
+// eight waves for the same 128 q-rows: waves 0-3 (score waves) compute
+// S^T = K . Q^T of their 32 q-rows, mask it, run the online softmax and
+// hand the packed probabilities and the rescale factor to LDS; waves 4-7
+// (value waves, wave w + 4 beside score wave w on one SIMD) accumulate
+// O^T += V^T . P^T one tile behind and issue every ring load.  A wave's own
+// VALU work does not run beside its own MFMAs, but it does beside another
+// wave's, so the softmax of one wave hides under the value product of its
+// SIMD neighbour, and a wave held at a load issue holds back only itself.
+// K and V have rings of three stages each: in interval k (between two block
+// barriers) the score waves read K of tile k, the value waves V of tile
+// k - 1, and the loads of K of tile k + 2 and V of tile k + 1 are issued.
+// Rows no query of the block sees (before the first query's window, past
+// the end) are loaded from the first row the block sees, so the ring never
+// holds values the probabilities do not zero exactly.  Two blocks fit a CU
+// (71 KB of LDS each for D = 128, at most 128 VGPRs per wave).
+template <class DT, int D, bool WIN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void prefill_rs_kernel(
+    TileArgs a, uint32_t n_sub, uint32_t n_groups) {
+  using M = Mfma32<DT>;
+  using L = PLds<D>;
+  using T = typename DT::T;
+  constexpr int KS = D / 16;  // k-steps of the score product
+  constexpr int MB = D / 32;  // 32-row blocks of value dims
+  constexpr int NPV = 2 * MB; // value-product MFMAs per tile
+  constexpr uint32_t kRS = 3; // ring stages, K and V each
+  constexpr uint32_t kTileB = uint32_t(L::kTile);
+  constexpr uint32_t kVRing = kRS * kTileB;        // V ring after the K ring
+  constexpr uint32_t kPB = 2u * kRS * kTileB;       // probabilities [wave][buf][half][lane] 16 B
+  constexpr uint32_t kAB = kPB + 4u * 2u * 2048u;   // rescale factors [wave][buf][lane]
+  constexpr uint32_t kIB = kAB + 4u * 2u * 256u;    // 1 / denominator [wave][lane]
+  constexpr uint32_t kBytes = kIB + 4u * 256u;
+  __shared__ __align__(1024) unsigned char lds[kBytes];
+  __shared__ uint32_t tcache[kTableCache];
+
+  // block -> (tile, KV head, sub-block): as in the kernel above
+  const uint32_t kb = blockIdx.x / 8u;
+  const uint32_t group = (kb / n_sub) * 8u + blockIdx.x % 8u;
+  if (group >= n_groups) return;
+  const uint32_t sub = kb % n_sub;
+  const uint32_t kvh = group % a.hkv;
+  const uint32_t tile = group / a.hkv;
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool vrole = wv >= 4u;
+  const uint32_t wq = wv & 3u;  // the wave's 32 q-rows (both roles)
+  const uint32_t c32 = lane & 31u, hf = lane >> 5;
+  const PlanView &pv = a.plan;
+  const uint32_t first = a.tiles[2 * tile], count = a.tiles[2 * tile + 1];
+  const uint32_t grp = a.hq / a.hkv;
+  const uint32_t qb_n = kRowsPerBlock / grp;
+  const uint32_t q_lo = sub * qb_n;
+  if (q_lo >= count) return;
+  const uint32_t q_hi = q_lo + qb_n < count ? q_lo + qb_n : count;
+  const uint32_t seq = pv.words[pv.qseq + first];
+  const uint32_t p0 = pv.words[pv.qpos + first];
+  const uint32_t len = pv.words[pv.lens + seq];
+  uint64_t k_end64 = a.causal ? uint64_t(p0) + q_hi : uint64_t(len);
+  const uint64_t reach = uint64_t(pv.W) * pv.ps;
+  if (k_end64 > reach) k_end64 = reach;
+  const uint32_t k_end = uint32_t(k_end64);
+  const uint32_t ps = pv.ps;
+  const bool pow2 = (ps & (ps - 1)) == 0;
+  const uint32_t ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 0u;
+  const uint32_t *table = pv.words + pv.table + uint64_t(seq) * pv.W;
+  const uint64_t page_elems = a.k_page;
+  auto page_of = [&](uint32_t pg) { return uint64_t(pg < pv.N ? pg : 0u) * page_elems; };
+  const uint32_t n_lp = (k_end + ps - 1) / ps;
+  for (uint32_t e = tid; e < n_lp && e < uint32_t(kTableCache); e += 512) {
+    const uint32_t pg = table[e];
+    tcache[e] = pg < pv.N ? pg : 0u;
+  }
+
+  const uint32_t r = 32u * wq + c32;
+  const uint32_t qq = r / grp, hh = r % grp;
+  const bool row_ok = r < qb_n * grp && q_lo + qq < q_hi;
+  const uint32_t pos = p0 + q_lo + qq;
+  const uint32_t pos_min = p0 + q_lo;
+  const uint32_t lim = a.causal && pos < k_end - 1u ? pos : k_end - 1u;
+  auto win_lo = [&](uint32_t n) { return WIN && n > a.window ? n - a.window : 0u; };
+  const uint32_t lo_min = win_lo(a.causal ? pos_min + 1u : k_end);
+  const uint32_t lo_max = win_lo(a.causal ? p0 + q_hi : k_end);
+  const uint32_t lo_row = a.causal ? win_lo(pos + 1u) : lo_min;
+  const uint32_t kt0 = lo_min / kTT;
+  const uint32_t n_tiles = (k_end + kTT - 1) / kTT;
+  const uint32_t nt = n_tiles - kt0;  // >= 1: the first query sees key lo_min < k_end
+
+  unsigned char *pbw = lds + kPB + wq * 4096u + lane * 16u;              // + buf 2048 + half 1024
+  float *abw = reinterpret_cast<float *>(lds + kAB + wq * 512u) + lane;  // + buf 64
+  float *ibw = reinterpret_cast<float *>(lds + kIB + wq * 256u) + lane;
+
+  if (!vrole) {
+    // ---------------- score waves ----------------
+    uint4 qb[KS];
+    {
+      const T *qrow = static_cast<const T *>(a.q) +
+                      (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D + (D / 2) * hf;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qb[ks] = row_ok ? *reinterpret_cast<const uint4 *>(qrow + 8 * ks) : make_uint4(0, 0, 0, 0);
+    }
+    block_sync_lds();  // table cache ready (the query loads may still be in flight)
+    uint32_t k_off[KS];
+    {
+      const uint32_t kr = key_of_mrow(c32);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        k_off[ks] = kr * L::kRowB + 16u * ((uint32_t(L::CPR / 2) * hf + ks) ^ L::swz(kr));
+    }
+    float m = kNoMax, lsum = 0.f;
+    const float sl2 = a.scale_log2;
+    block_sync_lds();  // B_0: K of the first tile is in the ring
+
+    auto interval = [&](auto j_c, uint32_t kk) {
+      constexpr uint32_t J = decltype(j_c)::value;  // == kk mod 6
+      constexpr uint32_t ST = J % kRS, BUF = J % 2u;
+      const unsigned char *kst = lds + ST * kTileB;
+      const uint32_t t0 = (kt0 + kk) * kTT;
+      uint4 kbuf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kbuf[ks] = *reinterpret_cast<const uint4 *>(kst + k_off[ks]);
+      f32x16_t x;
+#pragma unroll
+      for (int z = 0; z < 16; ++z) x[z] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) x = M::mma(kbuf[ks], qb[ks], x);
+      const bool full = (a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
+                                  : (t0 + kTT <= k_end)) && (!WIN || t0 >= lo_max);
+      if (!full) {
+        const int dl = int(lim) - int(t0) - 2 * int(hf);
+        const int dlo = int(lo_row) - int(t0) - 2 * int(hf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[4 * i + e] = key_of_elem(i, e) <= dl && (!WIN || key_of_elem(i, e) >= dlo) ? x[4 * i + e] : -INFINITY;
+      }
+      uint32_t pk[8];
+      float ts = 0.f;
+      auto probs = [&]() {
+        ts = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p0v = fast_exp2(__builtin_fmaf(x[2 * j], sl2, -m));
+          const float p1v = fast_exp2(__builtin_fmaf(x[2 * j + 1], sl2, -m));
+          pk[j] = M::pack2(p0v, p1v);
+          ts = M::add_pair(pk[j], ts);
+        }
+      };
+      probs();
+      // lazy rescaling, as in the kernel above; the factor goes to the value
+      // wave, which scales O before it adds this tile
+      float alpha = 1.f;
+      if (__any(ts > kSumLimit)) {
+        float lmax = vmax3(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], x[5]), vmax3(x[6], x[7], x[8]));
+        lmax = vmax3(lmax, vmax3(x[9], x[10], x[11]), vmax3(x[12], x[13], x[14]));
+        lmax = vmax(lmax, x[15]);
+        lmax = halves_max(lmax);
+        const float m_new = vmax(m, lmax * sl2);
+        alpha = fast_exp2(m - m_new);
+        m = m_new;
+        lsum *= alpha;
+        probs();
+      }
+      lsum += ts;
+      *reinterpret_cast<uint4 *>(pbw + BUF * 2048u) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      *reinterpret_cast<uint4 *>(pbw + BUF * 2048u + 1024u) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      abw[BUF * 64u] = alpha;
+      if (kk + 1u == nt) {
+        const float l_tot = halves_sum(lsum);
+        *ibw = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      }
+      block_sync_lds();  // B_{kk+1}
+    };
+    uint32_t kk = 0;
+    for (; kk + 6u <= nt; kk += 6u) {
+      interval(IC<0>(), kk);
+      interval(IC<1>(), kk + 1u);
+      interval(IC<2>(), kk + 2u);
+      interval(IC<3>(), kk + 3u);
+      interval(IC<4>(), kk + 4u);
+      interval(IC<5>(), kk + 5u);
+    }
+    if (kk < nt) interval(IC<0>(), kk);
+    if (kk + 1u < nt) interval(IC<1>(), kk + 1u);
+    if (kk + 2u < nt) interval(IC<2>(), kk + 2u);
+    if (kk + 3u < nt) interval(IC<3>(), kk + 3u);
+    if (kk + 4u < nt) interval(IC<4>(), kk + 4u);
+    return;
+  }
+
+  // ---------------- value waves ----------------
+  const uint32_t tok_elems = uint32_t(a.k_tok);
+  const T *kbase = static_cast<const T *>(a.k) + uint64_t(kvh) * D;
+  const T *vbase = static_cast<const T *>(a.v) + uint64_t(kvh) * D;
+  // Load n of this wave covers rows RPW (NI wq + n) .. + RPW - 1 of a tile;
+  // lane -> row + lane / CPR, LDS slot lane % CPR holding chunk
+  // slot ^ swz(row) of the cache row.
+  constexpr uint32_t kWaveRows = uint32_t(L::RPW * L::NI);
+  uint32_t chunk_el[L::NI], vo[L::NI];
+#pragma unroll
+  for (int n = 0; n < L::NI; ++n) {
+    const uint32_t rr = L::RPW * (L::NI * wq + n) + lane / L::CPR;
+    const uint32_t chunk = (lane % L::CPR) ^ L::swz(rr);
+    chunk_el[n] = 8u * chunk;
+    vo[n] = ((rr - kWaveRows * wq) * tok_elems + 8u * chunk) * uint32_t(sizeof(T));
+  }
+  const uint32_t vis_lo = lo_min, vis_hi = k_end;
+  // element offset of the cache row of token tok (rows no query of the
+  // block sees read row vis_lo instead)
+  auto row_off = [&](uint32_t tok) -> uint64_t {
+    const uint32_t t = tok >= vis_lo && tok < vis_hi ? tok : vis_lo;
+    const uint32_t lp = pow2 ? t >> ps_shift : t / ps;
+    const uint32_t slot = t - lp * ps;
+    const uint32_t pg = lp < uint32_t(kTableCache) ? tcache[lp] : table_word(table + lp);
+    return page_of(pg) + uint64_t(slot) * tok_elems;
+  };
+  // Fast path: power-of-two pages of at least 8 tokens and a tile whose rows
+  // are all seen: a wave's 8 rows are consecutive tokens of one page.
+  const bool fast_dma = pow2 && ps >= 8u;
+  auto fast_tile = [&](uint32_t j) {
+    const uint32_t t0 = (kt0 + j) * kTT;
+    return fast_dma && t0 >= vis_lo && t0 + kTT <= vis_hi;
+  };
+  const __attribute__((address_space(4))) uint32_t *ctable =
+      (const __attribute__((address_space(4))) uint32_t *)table;
+  auto wave_page = [&](uint32_t j) -> uint32_t {
+    const uint32_t tw = __builtin_amdgcn_readfirstlane((kt0 + j) * kTT + kWaveRows * wq);
+    return ctable[tw >> ps_shift];
+  };
+  // loads of tile j (local index) of K (is_v false) or V into its stage;
+  // pg: the wave's page of that tile when fast_tile(j)
+  auto issue = [&](bool is_v, uint32_t j, uint32_t pg) {
+    const uint32_t st_off = (is_v ? kVRing : 0u) + (j % kRS) * kTileB;
+    const T *base = is_v ? vbase : kbase;
+    if (fast_tile(j)) {
+      const uint32_t tw = (kt0 + j) * kTT + kWaveRows * wq;
+      const T *wb = base + (page_of(pg) + uint64_t(tw & (ps - 1u)) * tok_elems);
+#pragma unroll
+      for (int n = 0; n < L::NI; ++n) {
+        const uint32_t r0 = L::RPW * (L::NI * wq + n);
+        dma16s(vo[n], wb, __builtin_amdgcn_readfirstlane(lds_addr(lds + st_off + r0 * L::kRowB)));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < L::NI; ++n) {
+        const uint32_t r0 = L::RPW * (L::NI * wq + n);
+        const uint32_t rr = r0 + lane / L::CPR;
+        const uint64_t off = row_off((kt0 + j) * kTT + rr) + chunk_el[n];
+        dma16(base + off, __builtin_amdgcn_readfirstlane(lds_addr(lds + st_off + r0 * L::kRowB)));
+      }
+    }
+  };
+  // this interval's loads may stay in flight: wait for the rest
+  auto wait_all_but = [&](uint32_t groups) {
+    if (groups >= 2u) wait_vm<2 * L::NI>();
+    else if (groups == 1u) wait_vm<L::NI>();
+    else wait_vm<0>();
+  };
+
+  // Value product, block mb, step t, read rr: as in the kernel above, the V
+  // ring's stage added per tile.
+  uint32_t v_off[MB][2];
+  {
+    const uint32_t g = (lane >> 4) & 1u, e = (lane >> 2) & 3u, q4 = lane & 3u;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const uint32_t kr = key_of_mrow(8u * rr + 4u * hf + e);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint32_t dv = 32u * mb + 16u * g + 4u * q4;
+        v_off[mb][rr] = kVRing + kr * L::kRowB + 16u * ((dv / 8u) ^ L::swz(kr)) + 2u * (dv % 8u);
+      }
+    }
+  }
+  auto v_read = [&](const unsigned char *stage, int j) {
+    const unsigned char *p = stage + 16 * (j / MB) * L::kRowB;
+    const uint2 lo = lds_read_tr16(p + v_off[j % MB][0]), hi = lds_read_tr16(p + v_off[j % MB][1]);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
+
+  f32x16_t o[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) o[b][x] = 0.f;
+
+  // Prologue: K of tiles 0 and 1 and V of tile 0, then B_0 once all three
+  // have landed.  Tiles on the fast path need no table cache and are issued
+  // before the barrier that completes it.
+  const bool f0 = fast_tile(0), f1 = nt > 1u && fast_tile(1);
+  const uint32_t pg0 = f0 ? wave_page(0) : 0u;
+  uint32_t pg_v = f1 ? wave_page(1) : 0u;  // V of tile 1 (interval 0)
+  if (f0) {
+    issue(false, 0u, pg0);
+    issue(true, 0u, pg0);
+  }
+  if (f1) issue(false, 1u, pg_v);
+  block_sync_lds();  // table cache ready
+  if (!f0) {
+    issue(false, 0u, 0u);
+    issue(true, 0u, 0u);
+  }
+  if (nt > 1u && !f1) issue(false, 1u, 0u);
+  uint32_t pg_k = nt > 2u && fast_tile(2) ? wave_page(2) : 0u;  // K of tile 2 (interval 0)
+  wait_vm<0>();
+  block_sync_lds();  // B_0
+
+  // interval k: loads of K of tile k + 2 and V of tile k + 1 (their stages
+  // were last read in interval k - 1); returns the number of tiles issued
+  auto loads = [&](uint32_t k) {
+    uint32_t n = 0;
+    if (k + 2u < nt) { issue(false, k + 2u, pg_k); ++n; }
+    if (k + 1u < nt) { issue(true, k + 1u, pg_v); ++n; }
+    pg_v = pg_k;
+    pg_k = k + 3u < nt && fast_tile(k + 3u) ? wave_page(k + 3u) : 0u;
+    return n;
+  };
+  wait_all_but(loads(0u));
+  block_sync_lds();  // B_1
+
+  // interval t + 1: value product of tile t, then the loads
+  constexpr int kAhead = 3;
+  auto vinterval = [&](auto j_c, uint32_t t) {
+    constexpr uint32_t J = decltype(j_c)::value;  // == t mod 6
+    constexpr uint32_t ST = J % kRS, BUF = J % 2u;
+    const unsigned char *vst = lds + ST * kTileB;
+    uint4 vb[kAhead + 1];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) vb[j] = v_read(vst, j);
+    const float alpha = abw[BUF * 64u];
+    const uint4 pa = *reinterpret_cast<const uint4 *>(pbw + BUF * 2048u);
+    const uint4 pb = *reinterpret_cast<const uint4 *>(pbw + BUF * 2048u + 1024u);
+    const uint32_t n_issued = t + 1u < nt ? loads(t + 1u) : 0u;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b) o[b] *= alpha;
+    }
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+      if (j + kAhead < NPV) vb[(j + kAhead) % (kAhead + 1)] = v_read(vst, j + kAhead);
+      o[j % MB] = M::mma(vb[j % (kAhead + 1)], j / MB == 0 ? pa : pb, o[j % MB]);
+    }
+    if (t + 1u < nt) {
+      wait_all_but(n_issued);
+      block_sync_lds();  // B_{t+2}
+    }
+  };
+  uint32_t t = 0;
+  for (; t + 6u <= nt; t += 6u) {
+    vinterval(IC<0>(), t);
+    vinterval(IC<1>(), t + 1u);
+    vinterval(IC<2>(), t + 2u);
+    vinterval(IC<3>(), t + 3u);
+    vinterval(IC<4>(), t + 4u);
+    vinterval(IC<5>(), t + 5u);
+  }
+  if (t < nt) vinterval(IC<0>(), t);
+  if (t + 1u < nt) vinterval(IC<1>(), t + 1u);
+  if (t + 2u < nt) vinterval(IC<2>(), t + 2u);
+  if (t + 3u < nt) vinterval(IC<3>(), t + 3u);
+  if (t + 4u < nt) vinterval(IC<4>(), t + 4u);
+
+  // normalise and write: lane holds O^T[d = 32mb + 8i + 4hf + e][q-row c32]
+  const float inv = *ibw;  // written by the score wave before the last barrier
+  if (!row_ok) return;
+  T *out = static_cast<T *>(a.out) + (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D;
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint2 w;
+      w.x = M::pack2(o[b][4 * i] * inv, o[b][4 * i + 1] * inv);
+      w.y = M::pack2(o[b][4 * i + 2] * inv, o[b][4 * i + 3] * inv);
+      *reinterpret_cast<uint2 *>(out + 32 * b + 8 * i + 4 * hf) = w;
+    }
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -778,8 +1163,13 @@ hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st) {
   auto pick = [&](auto dt_c, auto f8_c, auto win_c) {
     using DTT = decltype(dt_c);
     constexpr bool F8 = decltype(f8_c)::value, WIN = decltype(win_c)::value;
-    if (d64) launch_k((prefill_kernel<DTT, 64, F8, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
-    else launch_k((prefill_kernel<DTT, 128, F8, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
+    if constexpr (F8) {
+      if (d64) launch_k((prefill_kernel<DTT, 64, true, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
+      else launch_k((prefill_kernel<DTT, 128, true, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
+    } else {
+      if (d64) launch_k((prefill_rs_kernel<DTT, 64, WIN>), grid, dim3(512), 0, st, a, n_sub, ng);
+      else launch_k((prefill_rs_kernel<DTT, 128, WIN>), grid, dim3(512), 0, st, a, n_sub, ng);
+    }
   };
   auto pick_win = [&](auto dt_c, auto f8_c) {
     if (win) pick(dt_c, f8_c, std::true_type());
