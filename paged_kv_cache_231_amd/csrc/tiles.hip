@@ -11,34 +11,32 @@
 // Two kernels share the tiling and the operand layouts below: for 16-bit
 // caches the role-split kernel (prefill_rs_kernel, eight waves per block:
 // four compute the scores and the softmax, four the value product and the
-// ring loads), for FP8 caches prefill_kernel (four waves, each doing all of
-// it), described first.
+// ring loads, which go HBM -> LDS directly), for FP8 caches
+// prefill_f8_kernel (four waves, each doing all of it, the ring filled
+// through registers).
 //
 // A block owns 128 q-rows (a q-row is one (query, q head) pair; with G q
 // heads per KV head that is 128/G queries x G heads) of one tile and one KV
-// head; each of its four waves owns 32 q-rows, the N side of 32x32x16 MFMAs.
-// Keys are walked in tiles of 32 rows.  K and V rows travel HBM -> LDS
-// directly (gfx950 global_load_lds, no registers on the way) into a ring of
-// four stages, three tiles ahead of the tile being computed.  Each wave
-// computes S^T = K . Q^T (keys on the M side, so a lane holds 16 keys of one
-// q-row), applies the absolute-position mask and an online softmax in base
-// 2, and accumulates O^T += V^T . P^T with V^T from transposed LDS reads.
-// The M rows of the score product are a fixed permutation of the tile's key
-// rows, chosen so that a lane's 16 probabilities are, in order, its own
-// K-slots of the value product: P never moves between lanes.  Rows are
-// stored unpadded with their 16-byte chunks XOR-swizzled by row, which
-// keeps the score reads and the transposed value reads free of bank
-// conflicts.  The block table of the sequence is cached in LDS.  Blocks that
-// share a (tile, KV head) are numbered so they land on one XCD and share its
-// L2.
+// head, 32 q-rows per wave, the N side of 32x32x16 MFMAs.  Keys are walked
+// in tiles of 32 rows held in an LDS ring.  A wave computes S^T = K . Q^T
+// (keys on the M side, so a lane holds 16 keys of one q-row), applies the
+// absolute-position mask and an online softmax in base 2, and O^T += V^T .
+// P^T takes V^T from transposed LDS reads.  The M rows of the score product
+// are a fixed permutation of the tile's key rows, chosen so that a lane's 16
+// probabilities are, in order, its own K-slots of the value product: P never
+// moves between lanes.  Rows are stored unpadded with their 16-byte chunks
+// XOR-swizzled by row, which keeps the score reads and the transposed value
+// reads free of bank conflicts.  The block table of the sequence is cached
+// in LDS.  Blocks that share a (tile, KV head) are numbered so they land on
+// one XCD and share its L2.
 //
 // FP8 caches (E4M3 codes, one byte per element, with a key and a value scale)
 // cannot go HBM -> LDS directly: the MFMAs take 16-bit operands.  Each thread
 // loads its share of a tile's codes into registers two steps ahead, widens
 // them exactly to the query type (E4M3 values are all representable in bf16
-// and f16) and writes them into the ring stage in the same swizzled layout,
-// one step before the stage is read.  The key scale is folded into the score
-// scale and the value scale into the normalisation.
+// and f16) and writes them into a ring of four stages in the same swizzled
+// layout, one step before the stage is read.  The key scale is folded into
+// the score scale and the value scale into the normalisation.
 
 #include <type_traits>
 
@@ -221,15 +219,6 @@ __device__ __forceinline__ uint4 widen8(uint32_t lo, uint32_t hi) {
 }
 
 // Element type of the cache: the query type, or E4M3 codes.
-template <class T, bool F8>
-struct CacheElem {
-  using type = T;
-};
-template <class T>
-struct CacheElem<T, true> {
-  using type = uint8_t;
-};
-
 template <int N>
 struct IC {
   static constexpr int value = N;
@@ -237,16 +226,15 @@ struct IC {
 
 // WIN: a sliding window is in force (without one the block starts at key 0
 // and the masks are one-sided).
-template <class DT, int D, bool F8, bool WIN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
+template <class DT, int D, bool WIN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_f8_kernel(
     TileArgs a, uint32_t n_sub, uint32_t n_groups) {
   using M = Mfma32<DT>;
   using L = PLds<D>;
   using T = typename DT::T;
-  using CT = typename CacheElem<T, F8>::type;
+  using CT = uint8_t;         // E4M3 codes
   constexpr int KS = D / 16;  // k-steps of the score product (8 values per lane half)
   constexpr int MB = D / 32;  // 32-row blocks of value dims
-  constexpr int kLoadsPerTile = 2 * L::NI;  // per thread: K and V
   __shared__ __align__(1024) unsigned char lds[L::kBytes];
   __shared__ uint32_t tcache[kTableCache];
 
@@ -342,100 +330,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const CT *vbase = static_cast<const CT *>(a.v) + uint64_t(kvh) * D;
   __syncthreads();  // table cache ready (Q loads may still be in flight: fine)
 
-  // Per-lane parts of the DMA addresses: load n of a wave covers rows
-  // r0(n) .. r0(n)+RPW-1, lane -> row r0(n) + lane / CPR and slot lane % CPR,
-  // which holds chunk slot ^ swz(row) of the cache row.  For a power-of-two
-  // page size the token's slot in its page is (kt*kTT mod ps) + (row mod ps),
-  // so its element offset splits into a per-tile uniform part and the
-  // per-lane part kept here.
   const uint32_t tok_elems = uint32_t(a.k_tok);
-  uint32_t lane_off[L::NI];
-#pragma unroll
-  for (int n = 0; n < L::NI; ++n) {
-    const uint32_t rr = L::RPW * (L::NI * wv + n) + lane / L::CPR;
-    const uint32_t chunk = (lane % L::CPR) ^ L::swz(rr);
-    lane_off[n] = (pow2 ? (rr & (ps - 1u)) * tok_elems : 0u) + 8u * chunk;
-  }
-  // DMA of key tile kt into its ring stage, in two parts: `lookup` finds
-  // the element offset of each lane's cache row (block-table entries from
-  // the LDS cache), `issue` starts the loads.  Rows past the end read the
-  // sequence's token 0 (any row inside the pool would do): their scores
-  // are masked out and their value rows are zeroed in LDS before use, so
-  // nothing of them reaches the output.
-  auto lookup = [&](uint32_t kt, uint64_t (&off)[L::NI]) {
-    const uint32_t tok0 = kt * kTT;
-    const uint32_t tile_off = pow2 ? (tok0 & (ps - 1u)) * tok_elems : 0u;
-#pragma unroll
-    for (int n = 0; n < L::NI; ++n) {
-      const uint32_t rr = L::RPW * (L::NI * wv + n) + lane / L::CPR;
-      const uint32_t tok = tok0 + rr;
-      const bool ok = tok < k_end;
-      if (pow2) {
-        const uint32_t lp = ok ? tok >> ps_shift : 0u;  // entry 0 exists whenever a tile does
-        const uint64_t pbase = page_of(lp < uint32_t(kTableCache) ? tcache[lp] : table_word(table + lp));
-        off[n] = ok ? pbase + tile_off + lane_off[n] : pbase + lane_off[n] - (rr & (ps - 1u)) * tok_elems;
-      } else {
-        const uint32_t lp = ok ? tok / ps : 0u;
-        const uint32_t slot = ok ? tok - lp * ps : 0u;
-        const uint64_t pbase = page_of(lp < uint32_t(kTableCache) ? tcache[lp] : table_word(table + lp));
-        off[n] = pbase + slot * tok_elems + lane_off[n];
-      }
-    }
-  };
-  // Fast path (power-of-two pages of at least 8 tokens, tiles wholly before
-  // the end): the 8 rows a wave loads of a tile are consecutive tokens of
-  // one page, so their address is one uniform base (a scalar table read,
-  // issued one pipeline step before the loads) plus a per-lane offset fixed
-  // for the whole kernel.
-  const bool fast_dma = pow2 && ps >= 8u;
-  constexpr uint32_t kWaveRows = uint32_t(L::RPW * L::NI);  // rows per wave per tile
-  uint32_t vo[L::NI];
-#pragma unroll
-  for (int n = 0; n < L::NI; ++n) {
-    const uint32_t rr = L::RPW * (L::NI * wv + n) + lane / L::CPR;
-    const uint32_t chunk = (lane % L::CPR) ^ L::swz(rr);
-    vo[n] = ((rr - kWaveRows * wv) * tok_elems + 8u * chunk) * uint32_t(sizeof(CT));
-  }
-  // (the plan words do not change while a kernel runs: read through the
-  // constant address space, the entry is a scalar load)
-  const __attribute__((address_space(4))) uint32_t *ctable =
-      (const __attribute__((address_space(4))) uint32_t *)table;
-  // the page of the wave's rows in tile kt (a raw table word), and the
-  // element offset of its first row
-  auto wave_page = [&](uint32_t kt) -> uint32_t {
-    const uint32_t tw = __builtin_amdgcn_readfirstlane(kt * kTT + kWaveRows * wv);
-    return ctable[tw >> ps_shift];
-  };
-  auto wave_base_of = [&](uint32_t kt, uint32_t pg) -> uint64_t {
-    const uint32_t tw = kt * kTT + kWaveRows * wv;
-    return page_of(pg) + (tw & (ps - 1u)) * tok_elems;
-  };
-  auto wave_base = [&](uint32_t kt) { return wave_base_of(kt, wave_page(kt)); };
-  auto issue_fast = [&](uint32_t kt, uint64_t wb) {
-    unsigned char *stage = lds + ((kt - kt0) % kStages) * L::kStage;
-    const CT *kb = kbase + wb, *vb = vbase + wb;
-#pragma unroll
-    for (int n = 0; n < L::NI; ++n) {
-      const uint32_t r0 = L::RPW * (L::NI * wv + n);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + r0 * L::kRowB));
-      dma16s(vo[n], kb, dst);
-      dma16s(vo[n], vb, dst + uint32_t(L::kTile));
-    }
-  };
-  auto fast_tile = [&](uint32_t kt) { return fast_dma && (kt + 1) * kTT <= k_end; };
 
-  auto issue = [&](uint32_t kt, const uint64_t (&off)[L::NI]) {
-    unsigned char *stage = lds + ((kt - kt0) % kStages) * L::kStage;
-#pragma unroll
-    for (int n = 0; n < L::NI; ++n) {
-      const uint32_t r0 = L::RPW * (L::NI * wv + n);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + r0 * L::kRowB));
-      dma16(kbase + off[n], dst);
-      dma16(vbase + off[n], dst + uint32_t(L::kTile));
-    }
-  };
-
-  // FP8: thread tid carries codes EPT (tid % 8) .. + EPT - 1 of row tid / 8
+  // Thread tid carries codes EPT (tid % 8) .. + EPT - 1 of row tid / 8
   // of each key tile, K and V, staged in one of two register sets.  The
   // loads are unconditional (a branch around them would make the compiler
   // wait for them at its end): tiles past the last read the last tile again,
@@ -509,55 +406,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(qb[ks]);
-  uint32_t rpg = 0u;  // page of the next refill (fast path)
-  if constexpr (F8) {
-    // tiles 0 and 1 into their stages, 2 and 3 into the register sets
-    if (kt0 < n_tiles) {
-      f8_load(kt0, f8k[0], f8v[0]);
-      f8_load(kt0 + 1u, f8k[1], f8v[1]);
-      f8_store(0u, kt0, f8k[0], f8v[0]);
-      f8_store(1u, kt0 + 1u, f8k[1], f8v[1]);
-      f8_load(kt0 + 2u, f8k[0], f8v[0]);
-      f8_load(kt0 + 3u, f8k[1], f8v[1]);
-    }
-  } else {
-    for (uint32_t kt = kt0; kt < n_tiles && kt < kt0 + uint32_t(kStages - 1); ++kt) {
-      if (fast_tile(kt)) {
-        issue_fast(kt, wave_base(kt));
-      } else {
-        uint64_t off[L::NI];
-        lookup(kt, off);
-        issue(kt, off);
-      }
-    }
-    rpg = fast_tile(kt0 + kStages - 1) ? wave_page(kt0 + kStages - 1) : 0u;
+  // tiles 0 and 1 into their stages, 2 and 3 into the register sets
+  if (kt0 < n_tiles) {
+    f8_load(kt0, f8k[0], f8v[0]);
+    f8_load(kt0 + 1u, f8k[1], f8v[1]);
+    f8_store(0u, kt0, f8k[0], f8v[0]);
+    f8_store(1u, kt0 + 1u, f8k[1], f8v[1]);
+    f8_load(kt0 + 2u, f8k[0], f8v[0]);
+    f8_load(kt0 + 3u, f8k[1], f8v[1]);
   }
-  // Value rows that no query of the block sees are zeroed in LDS once their
-  // tile has landed (after the barrier that makes it ready), and read only
-  // after one more barrier: the rows past the end of the last tile (if it is
-  // partial) and, under a window, the rows of the first tile before the
-  // first query's window.  (Rows some query of the block sees keep their
-  // values; for the others their probability is 0.)
-  const uint32_t tail_r0 = k_end % kTT;         // first row past the end, 0 if none
-  const uint32_t head_r1 = lo_min - kt0 * kTT;  // rows before the first window
-  auto zero_rows = [&](uint32_t j, uint32_t r0, uint32_t r1) {
-    unsigned char *vt = lds + (j % kStages) * L::kStage + L::kTile;
-    for (uint32_t e = tid; e < (r1 - r0) * uint32_t(L::CPR); e += 256)
-      *reinterpret_cast<uint4 *>(vt + (r0 + e / L::CPR) * L::kRowB + 16u * (e % L::CPR)) =
-          make_uint4(0, 0, 0, 0);
-  };
-
-  // Tile kt's ring stage is complete and visible to every wave once each
-  // thread has seen its own loads of kt land and the block has passed a
-  // barrier (which also means every wave finished reading the stage the next
-  // refill overwrites).  `later` = tiles issued after kt that may still be
-  // in flight.
-  auto ready = [&](uint32_t later) {
-    if (later >= 2) wait_vm<2 * kLoadsPerTile>();
-    else if (later == 1) wait_vm<kLoadsPerTile>();
-    else wait_vm<0>();
-    block_sync_lds();
-  };
 
   // Operand reads.  Score product, k-step ks of the tile in `stage`; value
   // product j = MB t + b (step t, value block b) of the tile in `stage`.
@@ -611,22 +468,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const unsigned char *st1_lds = lds + ST1 * L::kStage;
     const uint32_t kt = kt0 + j;
     const uint32_t t0 = kt * kTT;
-    // issued so far: tiles up to kt+2; tile kt+1 ready (after the last tile
-    // the scores below read a stage whose contents are not used; in bounds,
-    // no load in flight to it)
-    // (FP8: stage of tile kt+1 written by the step before)
-    if constexpr (F8) {
-      if (j + 1 < nt) block_sync_lds();
-    } else if (j + 1 < nt) {
-      ready(j + 2 < nt ? 1u : 0u);
-      if (tail_r0 != 0u && j + 2 == nt) zero_rows(j + 1, tail_r0, kTT);
-    } else if (tail_r0 != 0u && nt > 1) {
-      block_sync_lds();  // the zeroed rows of the last tile are visible
-    }
-    const bool refill = !F8 && kt + kStages - 1 < n_tiles;
-    const bool rfast = refill && fast_tile(kt + kStages - 1);
-    uint64_t roff[L::NI];
-    if (refill && !rfast) lookup(kt + kStages - 1, roff);
+    // the stage of tile kt+1 was written by the step before (after the last
+    // tile the scores below read a stage whose contents are not used)
+    if (j + 1 < nt) block_sync_lds();
 
     uint4 kb[kAhead + 1], vb[kAhead + 1];
 #pragma unroll
@@ -697,35 +541,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       o[b] = M::mma(vb[j % (kAhead + 1)], make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]), o[b]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (F8) {
-      // tile kt+2 from its register set into the stage of tile kt-2 (every
-      // wave passed this step's barrier, so none still reads it), then tile
-      // kt+4 into that register set
-      constexpr int RS = ST % 2;
-      if (j + 2 < nt) f8_store((ST + 2) % kStages, kt + 2u, f8k[RS], f8v[RS]);
-      f8_load(kt + 4u, f8k[RS], f8v[RS]);
-    } else {
-      // refill the stage of tile kt-1 (every wave passed this step's
-      // barrier, so none still reads it)
-      if (rfast) issue_fast(kt + kStages - 1, wave_base_of(kt + kStages - 1, rpg));
-      else if (refill) issue(kt + kStages - 1, roff);
-      // page of the next step's refill: its scalar read completes by that
-      // step's barrier
-      rpg = fast_tile(kt + kStages) ? wave_page(kt + kStages) : 0u;
-    }
+    // tile kt+2 from its register set into the stage of tile kt-2 (every
+    // wave passed this step's barrier, so none still reads it), then tile
+    // kt+4 into that register set
+    constexpr int RS = ST % 2;
+    if (j + 2 < nt) f8_store((ST + 2) % kStages, kt + 2u, f8k[RS], f8v[RS]);
+    f8_load(kt + 4u, f8k[RS], f8v[RS]);
   };
 
   f32x16_t sa, sb;
   if (nt) {
-    if constexpr (F8) {
-      block_sync_lds();
-    } else {
-      ready(nt - 1 < 2u ? nt - 1 : 2u);
-      const bool tail0 = tail_r0 != 0u && nt == 1;
-      if (head_r1 != 0u) zero_rows(0, 0u, head_r1);
-      if (tail0) zero_rows(0, tail_r0, kTT);
-      if (head_r1 != 0u || tail0) block_sync_lds();
-    }
+    block_sync_lds();  // tiles 0 and 1 are in their stages
     sa = scores(lds);
   }
   // whole groups of four tiles (ring stages 0..3 in order), then the rest
@@ -739,13 +565,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (n4 < nt) step(IC<0>(), n4, sa, sb);
   if (n4 + 1 < nt) step(IC<1>(), n4 + 1, sb, sa);
   if (n4 + 2 < nt) step(IC<2>(), n4 + 2, sa, sb);
-  if constexpr (F8) wait_vm<0>();  // the register loads past the last tile
+  wait_vm<0>();  // the register loads past the last tile
 
   // normalise and write: lane holds O^T[d = 32mb + 8i + 4hf + e][q-row c32]
   const float l_tot = halves_sum(lsum);
   if (!row_ok) return;
   T *out = static_cast<T *>(a.out) + (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D;
-  const float inv = l_tot > 0.f ? (F8 ? a.v_scale : 1.f) / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
 #pragma unroll
   for (int b = 0; b < MB; ++b)
 #pragma unroll
@@ -1164,8 +990,8 @@ hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st) {
     using DTT = decltype(dt_c);
     constexpr bool F8 = decltype(f8_c)::value, WIN = decltype(win_c)::value;
     if constexpr (F8) {
-      if (d64) launch_k((prefill_kernel<DTT, 64, true, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
-      else launch_k((prefill_kernel<DTT, 128, true, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
+      if (d64) launch_k((prefill_f8_kernel<DTT, 64, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
+      else launch_k((prefill_f8_kernel<DTT, 128, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
     } else {
       if (d64) launch_k((prefill_rs_kernel<DTT, 64, WIN>), grid, dim3(512), 0, st, a, n_sub, ng);
       else launch_k((prefill_rs_kernel<DTT, 128, WIN>), grid, dim3(512), 0, st, a, n_sub, ng);
