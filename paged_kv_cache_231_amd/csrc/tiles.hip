@@ -8,35 +8,23 @@
 // key rows 0..p_last, and every (query, q head) of one KV head forms a dense
 // contraction with those rows.
 //
-// Two kernels share the tiling and the operand layouts below: for 16-bit
-// caches the role-split kernel (prefill_rs_kernel, eight waves per block:
-// four compute the scores and the softmax, four the value product and the
-// ring loads, which go HBM -> LDS directly), for FP8 caches
-// prefill_f8_kernel (four waves, each doing all of it, the ring filled
-// through registers).
-//
 // A block owns 128 q-rows (a q-row is one (query, q head) pair; with G q
 // heads per KV head that is 128/G queries x G heads) of one tile and one KV
 // head, 32 q-rows per wave, the N side of 32x32x16 MFMAs.  Keys are walked
-// in tiles of 32 rows held in an LDS ring.  A wave computes S^T = K . Q^T
-// (keys on the M side, so a lane holds 16 keys of one q-row), applies the
-// absolute-position mask and an online softmax in base 2, and O^T += V^T .
-// P^T takes V^T from transposed LDS reads.  The M rows of the score product
-// are a fixed permutation of the tile's key rows, chosen so that a lane's 16
-// probabilities are, in order, its own K-slots of the value product: P never
-// moves between lanes.  Rows are stored unpadded with their 16-byte chunks
-// XOR-swizzled by row, which keeps the score reads and the transposed value
-// reads free of bank conflicts.  The block table of the sequence is cached
-// in LDS.  Blocks that share a (tile, KV head) are numbered so they land on
-// one XCD and share its L2.
-//
-// FP8 caches (E4M3 codes, one byte per element, with a key and a value scale)
-// cannot go HBM -> LDS directly: the MFMAs take 16-bit operands.  Each thread
-// loads its share of a tile's codes into registers two steps ahead, widens
-// them exactly to the query type (E4M3 values are all representable in bf16
-// and f16) and writes them into a ring of four stages in the same swizzled
-// layout, one step before the stage is read.  The key scale is folded into
-// the score scale and the value scale into the normalisation.
+// in tiles of 32 rows held in LDS rings.  S^T = K . Q^T puts keys on the M
+// side, so a lane holds 16 keys of one q-row; the absolute-position mask
+// and an online softmax in base 2 follow, and O^T += V^T . P^T takes V^T
+// from transposed LDS reads.  The M rows of the score product are a fixed
+// permutation of the tile's key rows, chosen so that a lane's 16
+// probabilities are, in order, its own K-slots of the value product: P
+// moves between waves only as whole lanes.  Rows are stored unpadded with
+// their 16-byte chunks XOR-swizzled by row, which keeps the score reads and
+// the transposed value reads free of bank conflicts.  The block table of the
+// sequence is cached in LDS.  Blocks that share a (tile, KV head) are
+// numbered so they land on one XCD and share its L2.  How the work of a
+// block is split between its waves, and how the rings are filled (16-bit
+// caches HBM -> LDS directly, FP8 caches widened through registers), is
+// described at the kernel.
 
 #include <type_traits>
 
@@ -46,10 +34,9 @@ namespace pkv {
 
 namespace {
 
-constexpr int kPW = 4;             // waves per block
+constexpr int kPW = 4;             // waves per role in a block (each issues a quarter of the ring loads)
 constexpr int kRowsPerBlock = 128; // q-rows per block (32 per wave)
 constexpr int kTT = 32;            // key rows per tile
-constexpr int kStages = 4;         // LDS ring stages (3 tiles in flight)
 constexpr int kTableCache = 1024;  // block-table entries cached in LDS
 // A lane whose 16 probabilities of a tile sum above this (each is then at
 // most this) makes the wave move its softmax references to the row maxima.
@@ -98,8 +85,6 @@ struct PLds {
   static constexpr int kRowB = D * 2;              // bytes per row (unpadded)
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int kTile = kTT * kRowB;        // one K or V tile
-  static constexpr int kStage = 2 * kTile;         // K then V
-  static constexpr int kBytes = kStages * kStage;
   static constexpr int RPW = 1024 / kRowB;         // rows per wave load (64 lanes x 16 B)
   static constexpr int NI = kTT / (RPW * kPW);     // loads per wave per tensor per tile
   // chunk c of row r sits in slot c ^ swz(r)
@@ -177,12 +162,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
       (__attribute__((address_space(3))) const char *)(p)));
 }
 
-// Makes the compiler finish the loads of x here (it cannot see the DMA
-// loads, so a wait it placed later for x would drain them too).
-__device__ __forceinline__ void settle(const uint4 &x) {
-  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
-}
-
 // A block-table entry beyond the LDS copy: one load, waited for in the same
 // instruction block.  The wait covers every earlier load too (the ring can
 // afford it on this path, taken only past kTableCache pages), and the
@@ -218,373 +197,13 @@ __device__ __forceinline__ uint4 widen8(uint32_t lo, uint32_t hi) {
   return make_uint4(widen2<DT>(lo, false), widen2<DT>(lo, true), widen2<DT>(hi, false), widen2<DT>(hi, true));
 }
 
-// Element type of the cache: the query type, or E4M3 codes.
 template <int N>
 struct IC {
   static constexpr int value = N;
 };
 
-// WIN: a sliding window is in force (without one the block starts at key 0
-// and the masks are one-sided).
-template <class DT, int D, bool WIN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_f8_kernel(
-    TileArgs a, uint32_t n_sub, uint32_t n_groups) {
-  using M = Mfma32<DT>;
-  using L = PLds<D>;
-  using T = typename DT::T;
-  using CT = uint8_t;         // E4M3 codes
-  constexpr int KS = D / 16;  // k-steps of the score product (8 values per lane half)
-  constexpr int MB = D / 32;  // 32-row blocks of value dims
-  __shared__ __align__(1024) unsigned char lds[L::kBytes];
-  __shared__ uint32_t tcache[kTableCache];
-
-  // Blocks are dispatched round-robin over the eight XCDs (blockIdx.x % 8).
-  // The (tile, KV head) groups are dealt to the XCDs in turn, group g to XCD
-  // g % 8, and the n_sub blocks of a group run back to back on its XCD, so
-  // they share the group's K/V rows in that XCD's L2.  Dealing groups (not
-  // contiguous ranges) spreads every tile's work over all XCDs: tiles of
-  // one chunk have similar key counts while chunks differ widely.
-  const uint32_t k = blockIdx.x / 8u;
-  const uint32_t group = (k / n_sub) * 8u + blockIdx.x % 8u;
-  if (group >= n_groups) return;
-  const uint32_t sub = k % n_sub;
-  const uint32_t kvh = group % a.hkv;
-  const uint32_t tile = group / a.hkv;
-
-  const uint32_t tid = threadIdx.x, lane = tid & 63u;
-  const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t c32 = lane & 31u, hf = lane >> 5;
-  const PlanView &pv = a.plan;
-  const uint32_t first = a.tiles[2 * tile], count = a.tiles[2 * tile + 1];
-  const uint32_t grp = a.hq / a.hkv;
-  const uint32_t qb_n = kRowsPerBlock / grp;  // queries per block
-  const uint32_t q_lo = sub * qb_n;
-  if (q_lo >= count) return;
-  const uint32_t q_hi = q_lo + qb_n < count ? q_lo + qb_n : count;
-  const uint32_t seq = pv.words[pv.qseq + first];
-  const uint32_t p0 = pv.words[pv.qpos + first];
-  const uint32_t len = pv.words[pv.lens + seq];
-  uint64_t k_end64 = a.causal ? uint64_t(p0) + q_hi : uint64_t(len);
-  const uint64_t reach = uint64_t(pv.W) * pv.ps;
-  if (k_end64 > reach) k_end64 = reach;
-  const uint32_t k_end = uint32_t(k_end64);
-  const uint32_t ps = pv.ps;
-  const bool pow2 = (ps & (ps - 1)) == 0;
-  const uint32_t ps_shift = pow2 ? uint32_t(__builtin_ctz(ps)) : 0u;
-
-  // block table of the sequence, first kTableCache entries, into LDS
-  const uint32_t *table = pv.words + pv.table + uint64_t(seq) * pv.W;
-  // (each entry holds a physical page, ids outside the pool replaced by
-  // page 0; K and V share their strides since head_dim == value_dim)
-  const uint64_t page_elems = a.k_page;
-  // 64-bit element offset of a physical page's first row (a cache tensor may
-  // hold more than 2^32 elements; ids outside the pool read page 0)
-  auto page_of = [&](uint32_t pg) { return uint64_t(pg < pv.N ? pg : 0u) * page_elems; };
-  const uint32_t n_lp = (k_end + ps - 1) / ps;
-  for (uint32_t e = tid; e < n_lp && e < uint32_t(kTableCache); e += 256) {
-    const uint32_t pg = table[e];
-    tcache[e] = pg < pv.N ? pg : 0u;  // never read outside the pool
-  }
-
-  // This lane's q-row (column c32 of the wave's N block) and its half of
-  // the head dims: K-slots of lane half hf at k-step ks are dims
-  // (D/2) hf + 8 ks .. +7, for the query operand and the key rows alike.
-  const uint32_t r = 32u * wv + c32;
-  const uint32_t qq = r / grp, hh = r % grp;
-  const bool row_ok = r < qb_n * grp && q_lo + qq < q_hi;
-  const uint32_t pos = p0 + q_lo + qq;
-  uint4 qb[KS];
-  {
-    const T *qrow = static_cast<const T *>(a.q) +
-                    (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D + (D / 2) * hf;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qb[ks] = row_ok ? *reinterpret_cast<const uint4 *>(qrow + 8 * ks) : make_uint4(0, 0, 0, 0);
-  }
-  // smallest position among the block's queries: key tiles wholly at or
-  // below it need no causal mask
-  const uint32_t pos_min = p0 + q_lo;
-  // last visible key of the q-row: its position (causal) or the last key
-  const uint32_t lim = a.causal && pos < k_end - 1u ? pos : k_end - 1u;
-  // Sliding window: a query with visible keys [0, n) sees [n - window, n).
-  // The block starts at the tile of its first query's first visible key;
-  // key tiles wholly at or above its last query's first key need no lower
-  // mask.
-  auto win_lo = [&](uint32_t n) { return WIN && n > a.window ? n - a.window : 0u; };
-  const uint32_t lo_min = win_lo(a.causal ? pos_min + 1u : k_end);
-  const uint32_t lo_max = win_lo(a.causal ? p0 + q_hi : k_end);
-  const uint32_t lo_row = a.causal ? win_lo(pos + 1u) : lo_min;
-  const uint32_t kt0 = lo_min / kTT;
-  const uint32_t n_tiles = (k_end + kTT - 1) / kTT;  // key tiles kt0 .. n_tiles - 1
-  const uint32_t nt = n_tiles - kt0;                  // tiles this block walks
-
-  f32x16_t o[MB];
-#pragma unroll
-  for (int b = 0; b < MB; ++b)
-#pragma unroll
-    for (int x = 0; x < 16; ++x) o[b][x] = 0.f;
-  float m = kNoMax;  // the row's softmax reference (base 2, scaled)
-  float lsum = 0.f;  // this lane's share of the row's denominator
-  const float sl2 = a.scale_log2;
-  const CT *kbase = static_cast<const CT *>(a.k) + uint64_t(kvh) * D;
-  const CT *vbase = static_cast<const CT *>(a.v) + uint64_t(kvh) * D;
-  __syncthreads();  // table cache ready (Q loads may still be in flight: fine)
-
-  const uint32_t tok_elems = uint32_t(a.k_tok);
-
-  // Thread tid carries codes EPT (tid % 8) .. + EPT - 1 of row tid / 8
-  // of each key tile, K and V, staged in one of two register sets.  The
-  // loads are unconditional (a branch around them would make the compiler
-  // wait for them at its end): tiles past the last read the last tile again,
-  // rows past the end read the sequence's token 0.  Value rows no query of
-  // the block sees (past the end, or before the first query's window) are
-  // written as zeros; their keys' scores are masked.
-  constexpr uint32_t EPT = D / 8;
-  const uint32_t f_row = tid >> 3, f_col = (tid & 7u) * EPT;
-  uint4 f8k[2], f8v[2];
-  auto f8_load = [&](uint32_t kt, uint4 &rk, uint4 &rv) {
-    const uint32_t tok = (kt < n_tiles ? kt : n_tiles - 1u) * kTT + f_row;
-    const uint32_t t = tok < k_end ? tok : 0u;
-    const uint32_t lp = pow2 ? t >> ps_shift : t / ps;
-    const uint32_t slot = t - lp * ps;
-    const uint64_t pbase = page_of(lp < uint32_t(kTableCache) ? tcache[lp] : table_word(table + lp));
-    const uint64_t off = pbase + slot * tok_elems + f_col;
-    if constexpr (EPT == 16) {
-      rk = *reinterpret_cast<const uint4 *>(kbase + off);
-      rv = *reinterpret_cast<const uint4 *>(vbase + off);
-    } else {
-      const uint2 k2 = *reinterpret_cast<const uint2 *>(kbase + off);
-      const uint2 v2 = *reinterpret_cast<const uint2 *>(vbase + off);
-      rk = make_uint4(k2.x, k2.y, 0, 0);
-      rv = make_uint4(v2.x, v2.y, 0, 0);
-    }
-  };
-  // widened codes of key tile kt from a register set into ring stage `st`
-  auto f8_store = [&](uint32_t st, uint32_t kt, const uint4 &rk, const uint4 &rv) {
-    unsigned char *kr = lds + st * L::kStage + f_row * L::kRowB;
-    unsigned char *vr = kr + L::kTile;
-    const uint32_t tok = kt * kTT + f_row;
-    const bool seen = tok < k_end && tok >= lo_min;
-    const uint32_t sw = L::swz(f_row);
-    const uint32_t c0 = EPT == 16 ? 2u * (tid & 7u) : (tid & 7u);  // first 8-element chunk
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4 *>(kr + 16u * (c0 ^ sw)) = widen8<DT>(rk.x, rk.y);
-    *reinterpret_cast<uint4 *>(vr + 16u * (c0 ^ sw)) = seen ? widen8<DT>(rv.x, rv.y) : zero;
-    if constexpr (EPT == 16) {
-      *reinterpret_cast<uint4 *>(kr + 16u * ((c0 + 1u) ^ sw)) = widen8<DT>(rk.z, rk.w);
-      *reinterpret_cast<uint4 *>(vr + 16u * ((c0 + 1u) ^ sw)) = seen ? widen8<DT>(rv.z, rv.w) : zero;
-    }
-  };
-
-  // LDS byte offsets (within a stage) of this lane's operand reads.
-  // Score product, k-step ks: key row key_of_mrow(c32), chunk (CPR/2) hf + ks.
-  uint32_t k_off[KS];
-  {
-    const uint32_t kr = key_of_mrow(c32);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      k_off[ks] = kr * L::kRowB + 16u * ((uint32_t(L::CPR / 2) * hf + ks) ^ L::swz(kr));
-  }
-  // Value product, value block mb, step t, read rr (K-slots 4rr .. 4rr+3):
-  // in each 16-lane group, lane 4e + q addresses key row
-  // key_of_mrow(16t + 8rr + 4hf + e) and value dims 32mb + 16g + 4q .. +3
-  // (g = lane / 16 mod 2); the transposed read hands lane i of the group
-  // value dim 32mb + 16g + i of those four rows.  Step t only adds 16 rows.
-  uint32_t v_off[MB][2];
-  {
-    const uint32_t g = (lane >> 4) & 1u, e = (lane >> 2) & 3u, q4 = lane & 3u;
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const uint32_t kr = key_of_mrow(8u * rr + 4u * hf + e);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const uint32_t dv = 32u * mb + 16u * g + 4u * q4;
-        v_off[mb][rr] = uint32_t(L::kTile) + kr * L::kRowB + 16u * ((dv / 8u) ^ L::swz(kr)) + 2u * (dv % 8u);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) settle(qb[ks]);
-  // tiles 0 and 1 into their stages, 2 and 3 into the register sets
-  if (kt0 < n_tiles) {
-    f8_load(kt0, f8k[0], f8v[0]);
-    f8_load(kt0 + 1u, f8k[1], f8v[1]);
-    f8_store(0u, kt0, f8k[0], f8v[0]);
-    f8_store(1u, kt0 + 1u, f8k[1], f8v[1]);
-    f8_load(kt0 + 2u, f8k[0], f8v[0]);
-    f8_load(kt0 + 3u, f8k[1], f8v[1]);
-  }
-
-  // Operand reads.  Score product, k-step ks of the tile in `stage`; value
-  // product j = MB t + b (step t, value block b) of the tile in `stage`.
-  auto k_read = [&](const unsigned char *stage, int ks) {
-    return *reinterpret_cast<const uint4 *>(stage + k_off[ks]);
-  };
-  auto v_read = [&](const unsigned char *stage, int j) {
-    const unsigned char *p = stage + 16 * (j / MB) * L::kRowB;
-    const uint2 lo = lds_read_tr16(p + v_off[j % MB][0]), hi = lds_read_tr16(p + v_off[j % MB][1]);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-  };
-  // S^T of a key tile alone (the pipeline's first tile): one chain of KS
-  // MFMAs over the stage's K rows.
-  auto scores = [&](const unsigned char *stage) {
-    f32x16_t acc;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) acc[x] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = M::mma(k_read(stage, ks), qb[ks], acc);
-    return acc;
-  };
-
-  // Probabilities of a tile against the current reference, packed as the
-  // value product's B operands (pk[4t .. 4t+3] for step t), and this lane's
-  // sum of them.
-  auto probs = [&](const f32x16_t &x, uint32_t (&pk)[8]) {
-    float ts = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p0v = fast_exp2(__builtin_fmaf(x[2 * j], sl2, -m));
-      const float p1v = fast_exp2(__builtin_fmaf(x[2 * j + 1], sl2, -m));
-      pk[j] = M::pack2(p0v, p1v);
-      ts = M::add_pair(pk[j], ts);
-    }
-    return ts;
-  };
-
-  // One step of the software pipeline for tile kt in ring stage ST.  The
-  // score MFMAs of tile kt + 1 (into s_next) are interleaved with the
-  // softmax arithmetic of tile kt (its scores s_cur came from the step
-  // before): the matrix core runs the independent products while the VALU
-  // works, in the same wave.  Then the value product of tile kt.  Each
-  // MFMA's LDS operand read is issued kAhead MFMAs ahead.
-  constexpr int NPV = 2 * MB;       // value-product MFMAs per tile
-  constexpr int kAhead = 2;
-  constexpr int PPS = 8 / KS;       // probability pairs per score MFMA
-  auto step = [&](auto st_c, uint32_t j, f32x16_t &s_cur, f32x16_t &s_next) {
-    constexpr int ST = decltype(st_c)::value;  // == j % kStages
-    constexpr int ST1 = (ST + 1) % kStages;
-    const unsigned char *st_lds = lds + ST * L::kStage;
-    const unsigned char *st1_lds = lds + ST1 * L::kStage;
-    const uint32_t kt = kt0 + j;
-    const uint32_t t0 = kt * kTT;
-    // the stage of tile kt+1 was written by the step before (after the last
-    // tile the scores below read a stage whose contents are not used)
-    if (j + 1 < nt) block_sync_lds();
-
-    uint4 kb[kAhead + 1], vb[kAhead + 1];
-#pragma unroll
-    for (int j = 0; j < kAhead; ++j) kb[j] = k_read(st1_lds, j);
-
-    f32x16_t &x = s_cur;
-    const bool full = (a.causal ? (t0 + kTT - 1 <= pos_min && t0 + kTT <= k_end)
-                                : (t0 + kTT <= k_end)) && (!WIN || t0 >= lo_max);
-    if (!full) {
-      // result element 4i + e of this lane is key key_of_elem(i, e) + 2 hf
-      // of the tile: visible iff that lies in [lo_row - t0, lim - t0]
-      const int dl = int(lim) - int(t0) - 2 * int(hf);
-      const int dlo = int(lo_row) - int(t0) - 2 * int(hf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          x[4 * i + e] = key_of_elem(i, e) <= dl && (!WIN || key_of_elem(i, e) >= dlo) ? x[4 * i + e] : -INFINITY;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // scores of tile kt + 1 beside the probabilities of tile kt, packed as
-    // the value product's B operands (pk[4t .. 4t+3] for step t), and this
-    // lane's sum of them
-    uint32_t pk[8];
-    float ts = 0.f;
-#pragma unroll
-    for (int z = 0; z < 16; ++z) s_next[z] = 0.f;
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      if (j + kAhead < KS) kb[(j + kAhead) % (kAhead + 1)] = k_read(st1_lds, j + kAhead);
-      if (j >= KS - kAhead) vb[j - (KS - kAhead)] = v_read(st_lds, j - (KS - kAhead));
-      s_next = M::mma(kb[j % (kAhead + 1)], qb[j], s_next);
-#pragma unroll
-      for (int u = 0; u < PPS; ++u) {
-        const int pr = PPS * j + u;
-        const float p0v = fast_exp2(__builtin_fmaf(x[2 * pr], sl2, -m));
-        const float p1v = fast_exp2(__builtin_fmaf(x[2 * pr + 1], sl2, -m));
-        pk[pr] = M::pack2(p0v, p1v);
-        ts = M::add_pair(pk[pr], ts);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Lazy rescaling: the reference moves only when some lane's tile sum
-    // passes kSumLimit (so no probability exceeds it); numerator and
-    // denominator share the reference, so the result is the same softmax.
-    if (__any(ts > kSumLimit)) {
-      float lmax = vmax3(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], x[5]), vmax3(x[6], x[7], x[8]));
-      lmax = vmax3(lmax, vmax3(x[9], x[10], x[11]), vmax3(x[12], x[13], x[14]));
-      lmax = vmax(lmax, x[15]);
-      lmax = halves_max(lmax);  // both halves of the q-row
-      const float m_new = vmax(m, lmax * sl2);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-#pragma unroll
-      for (int b = 0; b < MB; ++b) o[b] *= alpha;
-      lsum *= alpha;
-      ts = probs(x, pk);
-    }
-    lsum += ts;
-    __builtin_amdgcn_sched_barrier(0);
-
-    // value product of tile kt
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-      if (j + kAhead < NPV) vb[(j + kAhead) % (kAhead + 1)] = v_read(st_lds, j + kAhead);
-      const int t = j / MB, b = j % MB;
-      o[b] = M::mma(vb[j % (kAhead + 1)], make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]), o[b]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // tile kt+2 from its register set into the stage of tile kt-2 (every
-    // wave passed this step's barrier, so none still reads it), then tile
-    // kt+4 into that register set
-    constexpr int RS = ST % 2;
-    if (j + 2 < nt) f8_store((ST + 2) % kStages, kt + 2u, f8k[RS], f8v[RS]);
-    f8_load(kt + 4u, f8k[RS], f8v[RS]);
-  };
-
-  f32x16_t sa, sb;
-  if (nt) {
-    block_sync_lds();  // tiles 0 and 1 are in their stages
-    sa = scores(lds);
-  }
-  // whole groups of four tiles (ring stages 0..3 in order), then the rest
-  const uint32_t n4 = nt & ~3u;
-  for (uint32_t j = 0; j < n4; j += 4) {
-    step(IC<0>(), j, sa, sb);
-    step(IC<1>(), j + 1, sb, sa);
-    step(IC<2>(), j + 2, sa, sb);
-    step(IC<3>(), j + 3, sb, sa);
-  }
-  if (n4 < nt) step(IC<0>(), n4, sa, sb);
-  if (n4 + 1 < nt) step(IC<1>(), n4 + 1, sb, sa);
-  if (n4 + 2 < nt) step(IC<2>(), n4 + 2, sa, sb);
-  wait_vm<0>();  // the register loads past the last tile
-
-  // normalise and write: lane holds O^T[d = 32mb + 8i + 4hf + e][q-row c32]
-  const float l_tot = halves_sum(lsum);
-  if (!row_ok) return;
-  T *out = static_cast<T *>(a.out) + (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D;
-  const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
-#pragma unroll
-  for (int b = 0; b < MB; ++b)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint2 w;
-      w.x = M::pack2(o[b][4 * i] * inv, o[b][4 * i + 1] * inv);
-      w.y = M::pack2(o[b][4 * i + 2] * inv, o[b][4 * i + 3] * inv);
-      *reinterpret_cast<uint2 *>(out + 32 * b + 8 * i + 4 * hf) = w;
-    }
-}
-
-// Role-split form of the kernel above for 16-bit caches.  A block runs
-// eight waves for the same 128 q-rows: waves 0-3 (score waves) compute
+// The kernel.  A block runs eight waves for the same 128 q-rows: waves 0-3
+// (score waves) compute
 // S^T = K . Q^T of their 32 q-rows, mask it, run the online softmax and
 // hand the packed probabilities and the rescale factor to LDS; waves 4-7
 // (value waves, wave w + 4 beside score wave w on one SIMD) accumulate
@@ -599,12 +218,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // the end) are loaded from the first row the block sees, so the ring never
 // holds values the probabilities do not zero exactly.  Two blocks fit a CU
 // (71 KB of LDS each for D = 128, at most 128 VGPRs per wave).
-template <class DT, int D, bool WIN>
+//
+// FP8 caches (E4M3 codes, one byte per element, with a key and a value
+// scale) cannot go HBM -> LDS directly: the MFMAs take 16-bit operands.  The
+// value waves load each tile's codes into registers two intervals ahead,
+// widen them exactly to the query type (every E4M3 value is a bf16 and an
+// f16) and store them into the same rings in the same swizzled layout.  The
+// key scale is folded into the score scale, the value scale into the
+// normalisation.
+//
+// WIN: a sliding window is in force (without one the block starts at key 0
+// and the masks are one-sided).
+template <class DT, int D, bool F8, bool WIN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void prefill_rs_kernel(
     TileArgs a, uint32_t n_sub, uint32_t n_groups) {
   using M = Mfma32<DT>;
   using L = PLds<D>;
   using T = typename DT::T;
+  using CT = std::conditional_t<F8, uint8_t, T>;  // cache element: the query type or E4M3 codes
   constexpr int KS = D / 16;  // k-steps of the score product
   constexpr int MB = D / 32;  // 32-row blocks of value dims
   constexpr int NPV = 2 * MB; // value-product MFMAs per tile
@@ -777,8 +408,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
   // ---------------- value waves ----------------
   const uint32_t tok_elems = uint32_t(a.k_tok);
-  const T *kbase = static_cast<const T *>(a.k) + uint64_t(kvh) * D;
-  const T *vbase = static_cast<const T *>(a.v) + uint64_t(kvh) * D;
+  const CT *kbase = static_cast<const CT *>(a.k) + uint64_t(kvh) * D;
+  const CT *vbase = static_cast<const CT *>(a.v) + uint64_t(kvh) * D;
   // Load n of this wave covers rows RPW (NI wq + n) .. + RPW - 1 of a tile;
   // lane -> row + lane / CPR, LDS slot lane % CPR holding chunk
   // slot ^ swz(row) of the cache row.
@@ -789,7 +420,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const uint32_t rr = L::RPW * (L::NI * wq + n) + lane / L::CPR;
     const uint32_t chunk = (lane % L::CPR) ^ L::swz(rr);
     chunk_el[n] = 8u * chunk;
-    vo[n] = ((rr - kWaveRows * wq) * tok_elems + 8u * chunk) * uint32_t(sizeof(T));
+    vo[n] = ((rr - kWaveRows * wq) * tok_elems + 8u * chunk) * uint32_t(sizeof(CT));
   }
   const uint32_t vis_lo = lo_min, vis_hi = k_end;
   // element offset of the cache row of token tok (rows no query of the
@@ -818,10 +449,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // pg: the wave's page of that tile when fast_tile(j)
   auto issue = [&](bool is_v, uint32_t j, uint32_t pg) {
     const uint32_t st_off = (is_v ? kVRing : 0u) + (j % kRS) * kTileB;
-    const T *base = is_v ? vbase : kbase;
+    const CT *base = is_v ? vbase : kbase;
     if (fast_tile(j)) {
       const uint32_t tw = (kt0 + j) * kTT + kWaveRows * wq;
-      const T *wb = base + (page_of(pg) + uint64_t(tw & (ps - 1u)) * tok_elems);
+      const CT *wb = base + (page_of(pg) + uint64_t(tw & (ps - 1u)) * tok_elems);
 #pragma unroll
       for (int n = 0; n < L::NI; ++n) {
         const uint32_t r0 = L::RPW * (L::NI * wq + n);
@@ -871,29 +502,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
     for (int x = 0; x < 16; ++x) o[b][x] = 0.f;
 
-  // Prologue: K of tiles 0 and 1 and V of tile 0, then B_0 once all three
-  // have landed.  Tiles on the fast path need no table cache and are issued
-  // before the barrier that completes it.
-  const bool f0 = fast_tile(0), f1 = nt > 1u && fast_tile(1);
-  const uint32_t pg0 = f0 ? wave_page(0) : 0u;
-  uint32_t pg_v = f1 ? wave_page(1) : 0u;  // V of tile 1 (interval 0)
-  if (f0) {
-    issue(false, 0u, pg0);
-    issue(true, 0u, pg0);
-  }
-  if (f1) issue(false, 1u, pg_v);
-  block_sync_lds();  // table cache ready
-  if (!f0) {
-    issue(false, 0u, 0u);
-    issue(true, 0u, 0u);
-  }
-  if (nt > 1u && !f1) issue(false, 1u, 0u);
-  uint32_t pg_k = nt > 2u && fast_tile(2) ? wave_page(2) : 0u;  // K of tile 2 (interval 0)
-  wait_vm<0>();
-  block_sync_lds();  // B_0
+  // FP8 caches: value-wave thread tv carries codes EPT (tv % 8) .. + EPT - 1
+  // of row tv / 8 of a tile, K and V, in one of two register sets; tile j's
+  // codes are loaded two intervals before they are widened (exactly: every
+  // E4M3 value is a bf16 and an f16) into the tile's K and V stages.  The
+  // loads are unconditional (past the last tile they read it again), so the
+  // compiler waits only for the set it stores.
+  constexpr uint32_t EPT = D / 8;
+  const uint32_t tv = tid - 256u;
+  const uint32_t f_row = tv >> 3, f_col = (tv & 7u) * EPT;
+  uint4 f8k[2], f8v[2];
+  auto f8_load = [&](uint32_t j, uint4 &rk, uint4 &rv) {
+    const uint32_t jj = j < nt ? j : nt - 1u;
+    const uint64_t off = row_off((kt0 + jj) * kTT + f_row) + f_col;
+    if constexpr (EPT == 16) {
+      rk = *reinterpret_cast<const uint4 *>(kbase + off);
+      rv = *reinterpret_cast<const uint4 *>(vbase + off);
+    } else {
+      const uint2 k2 = *reinterpret_cast<const uint2 *>(kbase + off);
+      const uint2 v2 = *reinterpret_cast<const uint2 *>(vbase + off);
+      rk = make_uint4(k2.x, k2.y, 0, 0);
+      rv = make_uint4(v2.x, v2.y, 0, 0);
+    }
+  };
+  auto f8_store = [&](uint32_t j, const uint4 &rk, const uint4 &rv) {
+    unsigned char *kr = lds + (j % kRS) * kTileB + f_row * L::kRowB;
+    unsigned char *vr = lds + kVRing + (j % kRS) * kTileB + f_row * L::kRowB;
+    const uint32_t sw = L::swz(f_row);
+    const uint32_t c0 = EPT == 16 ? 2u * (tv & 7u) : (tv & 7u);  // first 8-element chunk
+    *reinterpret_cast<uint4 *>(kr + 16u * (c0 ^ sw)) = widen8<DT>(rk.x, rk.y);
+    *reinterpret_cast<uint4 *>(vr + 16u * (c0 ^ sw)) = widen8<DT>(rv.x, rv.y);
+    if constexpr (EPT == 16) {
+      *reinterpret_cast<uint4 *>(kr + 16u * ((c0 + 1u) ^ sw)) = widen8<DT>(rk.z, rk.w);
+      *reinterpret_cast<uint4 *>(vr + 16u * ((c0 + 1u) ^ sw)) = widen8<DT>(rv.z, rv.w);
+    }
+  };
 
-  // interval k: loads of K of tile k + 2 and V of tile k + 1 (their stages
-  // were last read in interval k - 1); returns the number of tiles issued
+  uint32_t pg_v = 0u, pg_k = 0u;  // pages of the next interval's loads (DMA, fast path)
+  // DMA, interval k: loads of K of tile k + 2 and V of tile k + 1 (their
+  // stages were last read in interval k - 1); returns the number of tiles
+  // issued
   auto loads = [&](uint32_t k) {
     uint32_t n = 0;
     if (k + 2u < nt) { issue(false, k + 2u, pg_k); ++n; }
@@ -902,8 +550,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     pg_k = k + 3u < nt && fast_tile(k + 3u) ? wave_page(k + 3u) : 0u;
     return n;
   };
-  wait_all_but(loads(0u));
-  block_sync_lds();  // B_1
+  if constexpr (F8) {
+    // Prologue: tile 0 into its stages, tiles 1 and 2 into the register
+    // sets; interval 0: tile 1 into its stages, tile 3 into its set.
+    block_sync_lds();  // table cache ready
+    f8_load(0u, f8k[0], f8v[0]);
+    f8_load(1u, f8k[1], f8v[1]);
+    f8_store(0u, f8k[0], f8v[0]);
+    f8_load(2u, f8k[0], f8v[0]);
+    block_sync_lds();  // B_0
+    if (nt > 1u) f8_store(1u, f8k[1], f8v[1]);
+    f8_load(3u, f8k[1], f8v[1]);
+    block_sync_lds();  // B_1
+  } else {
+    // Prologue: K of tiles 0 and 1 and V of tile 0, then B_0 once all three
+    // have landed.  Tiles on the fast path need no table cache and are issued
+    // before the barrier that completes it.
+    const bool f0 = fast_tile(0), f1 = nt > 1u && fast_tile(1);
+    const uint32_t pg0 = f0 ? wave_page(0) : 0u;
+    pg_v = f1 ? wave_page(1) : 0u;  // V of tile 1 (interval 0)
+    if (f0) {
+      issue(false, 0u, pg0);
+      issue(true, 0u, pg0);
+    }
+    if (f1) issue(false, 1u, pg_v);
+    block_sync_lds();  // table cache ready
+    if (!f0) {
+      issue(false, 0u, 0u);
+      issue(true, 0u, 0u);
+    }
+    if (nt > 1u && !f1) issue(false, 1u, 0u);
+    pg_k = nt > 2u && fast_tile(2) ? wave_page(2) : 0u;  // K of tile 2 (interval 0)
+    wait_vm<0>();
+    block_sync_lds();  // B_0
+    wait_all_but(loads(0u));
+    block_sync_lds();  // B_1
+  }
 
   // interval t + 1: value product of tile t, then the loads
   constexpr int kAhead = 3;
@@ -917,7 +599,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const float alpha = abw[BUF * 64u];
     const uint4 pa = *reinterpret_cast<const uint4 *>(pbw + BUF * 2048u);
     const uint4 pb = *reinterpret_cast<const uint4 *>(pbw + BUF * 2048u + 1024u);
-    const uint32_t n_issued = t + 1u < nt ? loads(t + 1u) : 0u;
+    uint32_t n_issued = 0u;
+    if constexpr (F8) {
+      // interval t + 1: tile t + 2 from its set into its stages, tile t + 4
+      // into that set
+      if (t + 2u < nt) f8_store(t + 2u, f8k[J % 2u], f8v[J % 2u]);
+      if (t + 1u < nt) f8_load(t + 4u, f8k[J % 2u], f8v[J % 2u]);
+    } else {
+      n_issued = t + 1u < nt ? loads(t + 1u) : 0u;
+    }
     if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int b = 0; b < MB; ++b) o[b] *= alpha;
@@ -928,7 +618,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       o[j % MB] = M::mma(vb[j % (kAhead + 1)], j / MB == 0 ? pa : pb, o[j % MB]);
     }
     if (t + 1u < nt) {
-      wait_all_but(n_issued);
+      if constexpr (!F8) wait_all_but(n_issued);
       block_sync_lds();  // B_{t+2}
     }
   };
@@ -947,8 +637,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (t + 3u < nt) vinterval(IC<3>(), t + 3u);
   if (t + 4u < nt) vinterval(IC<4>(), t + 4u);
 
+  if constexpr (F8) wait_vm<0>();  // the register loads past the last tile
   // normalise and write: lane holds O^T[d = 32mb + 8i + 4hf + e][q-row c32]
-  const float inv = *ibw;  // written by the score wave before the last barrier
+  // (1 / denominator written by the score wave before the last barrier;
+  // FP8: times the value scale)
+  const float inv = F8 ? *ibw * a.v_scale : *ibw;
   if (!row_ok) return;
   T *out = static_cast<T *>(a.out) + (uint64_t(first + q_lo + qq) * a.hq + kvh * grp + hh) * D;
 #pragma unroll
@@ -989,13 +682,8 @@ hipError_t launch_tiles(const TileArgs &a, pkv_dtype dt, hipStream_t st) {
   auto pick = [&](auto dt_c, auto f8_c, auto win_c) {
     using DTT = decltype(dt_c);
     constexpr bool F8 = decltype(f8_c)::value, WIN = decltype(win_c)::value;
-    if constexpr (F8) {
-      if (d64) launch_k((prefill_f8_kernel<DTT, 64, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
-      else launch_k((prefill_f8_kernel<DTT, 128, WIN>), grid, dim3(256), 0, st, a, n_sub, ng);
-    } else {
-      if (d64) launch_k((prefill_rs_kernel<DTT, 64, WIN>), grid, dim3(512), 0, st, a, n_sub, ng);
-      else launch_k((prefill_rs_kernel<DTT, 128, WIN>), grid, dim3(512), 0, st, a, n_sub, ng);
-    }
+    if (d64) launch_k((prefill_rs_kernel<DTT, 64, F8, WIN>), grid, dim3(512), 0, st, a, n_sub, ng);
+    else launch_k((prefill_rs_kernel<DTT, 128, F8, WIN>), grid, dim3(512), 0, st, a, n_sub, ng);
   };
   auto pick_win = [&](auto dt_c, auto f8_c) {
     if (win) pick(dt_c, f8_c, std::true_type());
