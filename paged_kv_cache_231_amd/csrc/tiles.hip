@@ -203,9 +203,9 @@ struct IC {
 };
 
 // The kernel.  A block runs eight waves for the same 128 q-rows: waves 0-3
-// (score waves) compute
-// S^T = K . Q^T of their 32 q-rows, mask it, run the online softmax and
-// hand the packed probabilities and the rescale factor to LDS; waves 4-7
+// (score waves) compute S^T = K . Q^T of their 32 q-rows, mask it, run the
+// online softmax and hand the packed probabilities and the rescale factor
+// to LDS; waves 4-7
 // (value waves, wave w + 4 beside score wave w on one SIMD) accumulate
 // O^T += V^T . P^T one tile behind and issue every ring load.  A wave's own
 // VALU work does not run beside its own MFMAs, but it does beside another
@@ -249,7 +249,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __shared__ __align__(1024) unsigned char lds[kBytes];
   __shared__ uint32_t tcache[kTableCache];
 
-  // block -> (tile, KV head, sub-block): as in the kernel above
+  // Blocks are dispatched round-robin over the eight XCDs (blockIdx.x % 8).
+  // The (tile, KV head) groups are dealt to the XCDs in turn, group g to XCD
+  // g % 8, and the n_sub blocks of a group run back to back on its XCD, so
+  // they share the group's K/V rows in that XCD's L2.  Dealing groups (not
+  // contiguous ranges) spreads every tile's work over all XCDs: tiles of
+  // one chunk have similar key counts while chunks differ widely.
   const uint32_t kb = blockIdx.x / 8u;
   const uint32_t group = (kb / n_sub) * 8u + blockIdx.x % 8u;
   if (group >= n_groups) return;
@@ -308,6 +313,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
   if (!vrole) {
     // ---------------- score waves ----------------
+    // This lane's q-row (column c32 of the wave's N block) and its half of
+    // the head dims: K-slots of lane half hf at k-step ks are dims
+    // (D/2) hf + 8 ks .. +7, for the query operand and the key rows alike.
     uint4 qb[KS];
     {
       const T *qrow = static_cast<const T *>(a.q) +
@@ -317,6 +325,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         qb[ks] = row_ok ? *reinterpret_cast<const uint4 *>(qrow + 8 * ks) : make_uint4(0, 0, 0, 0);
     }
     block_sync_lds();  // table cache ready (the query loads may still be in flight)
+    // LDS byte offsets (within a stage) of this lane's score operand reads:
+    // k-step ks reads key row key_of_mrow(c32), chunk (CPR/2) hf + ks.
     uint32_t k_off[KS];
     {
       const uint32_t kr = key_of_mrow(c32);
@@ -365,8 +375,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         }
       };
       probs();
-      // lazy rescaling, as in the kernel above; the factor goes to the value
-      // wave, which scales O before it adds this tile
+      // Lazy rescaling: the reference moves to the row maxima only when some
+      // lane's tile sum passes kSumLimit (so no probability exceeds it);
+      // numerator and denominator share the reference, so the result is the
+      // same softmax.  The factor goes to the value wave, which scales O
+      // before it adds this tile.
       float alpha = 1.f;
       if (__any(ts > kSumLimit)) {
         float lmax = vmax3(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], x[5]), vmax3(x[6], x[7], x[8]));
@@ -475,8 +488,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     else wait_vm<0>();
   };
 
-  // Value product, block mb, step t, read rr: as in the kernel above, the V
-  // ring's stage added per tile.
+  // Value product, value block mb, step t, read rr (K-slots 4rr .. 4rr+3):
+  // in each 16-lane group, lane 4e + q addresses key row
+  // key_of_mrow(16t + 8rr + 4hf + e) and value dims 32mb + 16g + 4q .. +3
+  // (g = lane / 16 mod 2); the transposed read hands lane i of the group
+  // value dim 32mb + 16g + i of those four rows.  Step t only adds 16 rows,
+  // the stage is added per tile.
   uint32_t v_off[MB][2];
   {
     const uint32_t g = (lane >> 4) & 1u, e = (lane >> 2) & 3u, q4 = lane & 3u;
