@@ -299,6 +299,16 @@ def test_prefill_tiles_gqa(dtype, g, d):
     assert_close(run(wl), expected(wl), dtype, f"prefill g={g} d={d}")
 
 
+@pytest.mark.parametrize("g", [32, 48, 128])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_tiles_wide_groups(g, d):
+    """Groups of 32 to 128 q heads per KV head: a block's 128 q-rows are 4,
+    2 (48 heads: 96 rows, the rest of the block idle) or 1 query, so a
+    150-query tile spreads over up to 128 blocks."""
+    wl = _prefill_wl(torch.bfloat16, g, 1, d, 16, [(77, 150), (0, 20)], [33, 300], seed=1900 + g + d)
+    assert_close(run(wl), expected(wl), torch.bfloat16, f"prefill g={g} d={d}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("ps", [1, 5, 64])
 def test_prefill_tiles_page_sizes(causal, ps):
