@@ -145,6 +145,16 @@ def test_fp8_chunk_queries_window_on_tiles(g, d, ps, causal):
                      torch.bfloat16, f"fp8 chunk window {w} g={g} d={d} ps={ps} causal={causal}")
 
 
+@pytest.mark.parametrize("g,d", [(48, 128), (128, 64)])
+def test_fp8_chunk_queries_wide_groups(g, d):
+    """FP8 chunk queries with 48 and 128 q heads per KV head on the tile
+    kernel (two queries, or one, per block)."""
+    wl = _chunk_workload(torch.bfloat16, g, d, 16, True, seed=4270 + g + d, chunks=((77, 150), (0, 20)),
+                         dec=(33,))
+    k8, v8 = fp8_caches(wl, KS, VS)
+    assert_close(_run_on_tiles(wl, k8, v8, 1), _want(wl, k8, v8), torch.bfloat16, f"fp8 chunks g={g} d={d}")
+
+
 def test_fp8_chunk_behind_long_table():
     """A chunk whose keys span more block-table entries than the kernel keeps
     in LDS (16600 prior tokens, 16-token pages)."""
