@@ -258,7 +258,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const uint32_t kb = blockIdx.x / 8u;
   const uint32_t group = (kb / n_sub) * 8u + blockIdx.x % 8u;
   if (group >= n_groups) return;
-  const uint32_t sub = kb % n_sub;
+  // the group's sub-blocks longest first (the last queries see the most keys)
+  const uint32_t sub = n_sub - 1u - kb % n_sub;
   const uint32_t kvh = group % a.hkv;
   const uint32_t tile = group / a.hkv;
 
