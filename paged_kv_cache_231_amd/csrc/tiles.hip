@@ -530,9 +530,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const uint32_t tv = tid - 256u;
   const uint32_t f_row = tv >> 3, f_col = (tv & 7u) * EPT;
   uint4 f8k[2], f8v[2];
-  auto f8_load = [&](uint32_t j, uint4 &rk, uint4 &rv) {
+  // (pg: the wave's page of the tile when it is on the fast path, where a
+  // wave's 8 rows are consecutive tokens of one page, as for the DMA)
+  auto f8_load = [&](uint32_t j, uint32_t pg, uint4 &rk, uint4 &rv) {
     const uint32_t jj = j < nt ? j : nt - 1u;
-    const uint64_t off = row_off((kt0 + jj) * kTT + f_row) + f_col;
+    const uint32_t tok = (kt0 + jj) * kTT + f_row;
+    const uint64_t off =
+        (fast_tile(jj) ? page_of(pg) + uint64_t(tok & (ps - 1u)) * tok_elems : row_off(tok)) + f_col;
     if constexpr (EPT == 16) {
       rk = *reinterpret_cast<const uint4 *>(kbase + off);
       rv = *reinterpret_cast<const uint4 *>(vbase + off);
@@ -568,17 +572,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     pg_k = k + 3u < nt && fast_tile(k + 3u) ? wave_page(k + 3u) : 0u;
     return n;
   };
+  // the page f8_load needs for tile j (clamped as it clamps); pgf: that of
+  // the tile the next interval loads, read one interval ahead
+  auto page_f8 = [&](uint32_t j) {
+    const uint32_t jj = j < nt ? j : nt - 1u;
+    return fast_tile(jj) ? wave_page(jj) : 0u;
+  };
+  uint32_t pgf = 0u;
   if constexpr (F8) {
     // Prologue: tile 0 into its stages, tiles 1 and 2 into the register
     // sets; interval 0: tile 1 into its stages, tile 3 into its set.
     block_sync_lds();  // table cache ready
-    f8_load(0u, f8k[0], f8v[0]);
-    f8_load(1u, f8k[1], f8v[1]);
+    f8_load(0u, page_f8(0u), f8k[0], f8v[0]);
+    f8_load(1u, page_f8(1u), f8k[1], f8v[1]);
     f8_store(0u, f8k[0], f8v[0]);
-    f8_load(2u, f8k[0], f8v[0]);
+    f8_load(2u, page_f8(2u), f8k[0], f8v[0]);
     block_sync_lds();  // B_0
     if (nt > 1u) f8_store(1u, f8k[1], f8v[1]);
-    f8_load(3u, f8k[1], f8v[1]);
+    f8_load(3u, page_f8(3u), f8k[1], f8v[1]);
+    pgf = page_f8(4u);
     block_sync_lds();  // B_1
   } else {
     // Prologue: K of tiles 0 and 1 and V of tile 0, then B_0 once all three
@@ -622,7 +634,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       // interval t + 1: tile t + 2 from its set into its stages, tile t + 4
       // into that set
       if (t + 2u < nt) f8_store(t + 2u, f8k[J % 2u], f8v[J % 2u]);
-      if (t + 1u < nt) f8_load(t + 4u, f8k[J % 2u], f8v[J % 2u]);
+      if (t + 1u < nt) {
+        f8_load(t + 4u, pgf, f8k[J % 2u], f8v[J % 2u]);
+        pgf = page_f8(t + 5u);
+      }
     } else {
       n_issued = t + 1u < nt ? loads(t + 1u) : 0u;
     }
