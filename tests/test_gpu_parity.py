@@ -309,6 +309,20 @@ def test_prefill_tiles_wide_groups(g, d):
     assert_close(run(wl), expected(wl), torch.bfloat16, f"prefill g={g} d={d}")
 
 
+def test_prefill_groups_past_the_tile_limit_run_as_rows():
+    """More than 128 q heads per KV head do not fit one block's q-rows: such
+    chunk queries run on the per-query kernels, with the same results."""
+    wl = _prefill_wl(torch.bfloat16, 192, 1, 64, 16, [(40, 24)], [9], seed=1990)
+    dev = to_dev(wl)
+    plan = make_plan(wl)
+    assert plan.n_tiles > 0
+    plan.timing(True)
+    got = run(wl, plan=plan, dev=dev)
+    assert plan.timing_read("tiles")[0] == 0 and plan.timing_read("rows")[0] == 1
+    plan.timing(False)
+    assert_close(got, expected(wl), torch.bfloat16, "prefill g=192 as rows")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("ps", [1, 5, 64])
 def test_prefill_tiles_page_sizes(causal, ps):
