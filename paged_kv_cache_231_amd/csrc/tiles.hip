@@ -453,8 +453,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const uint32_t t0 = (kt0 + j) * kTT;
     return fast_dma && t0 >= vis_lo && t0 + kTT <= vis_hi;
   };
+  // (the plan words do not change while a kernel runs: read through the
+  // constant address space, a table entry is a scalar load)
   const __attribute__((address_space(4))) uint32_t *ctable =
       (const __attribute__((address_space(4))) uint32_t *)table;
+  // the wave's page of tile j (its 8 rows are consecutive tokens of one page)
   auto wave_page = [&](uint32_t j) -> uint32_t {
     const uint32_t tw = __builtin_amdgcn_readfirstlane((kt0 + j) * kTT + kWaveRows * wq);
     return ctable[tw >> ps_shift];
