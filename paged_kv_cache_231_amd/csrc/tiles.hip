@@ -217,7 +217,8 @@ struct IC {
 // Rows no query of the block sees (before the first query's window, past
 // the end) are loaded from the first row the block sees, so the ring never
 // holds values the probabilities do not zero exactly.  Two blocks fit a CU
-// (71 KB of LDS each for D = 128, at most 128 VGPRs per wave).
+// at D = 128 (71 KB of LDS each, at most 128 VGPRs per wave), three at
+// D = 64 (47 KB, at most 85 VGPRs).
 //
 // FP8 caches (E4M3 codes, one byte per element, with a key and a value
 // scale) cannot go HBM -> LDS directly: the MFMAs take 16-bit operands.  The
@@ -230,7 +231,7 @@ struct IC {
 // WIN: a sliding window is in force (without one the block starts at key 0
 // and the masks are one-sided).
 template <class DT, int D, bool F8, bool WIN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void prefill_rs_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, D == 64 ? 6 : 4))) void prefill_rs_kernel(
     TileArgs a, uint32_t n_sub, uint32_t n_groups) {
   using M = Mfma32<DT>;
   using L = PLds<D>;
